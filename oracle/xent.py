@@ -1,0 +1,98 @@
+"""Vocabulary-parallel logits + cross-entropy, float64.
+
+Test infrastructure only (see the package header).
+
+Passages: "Megatron-LM: Training ... Model Parallelism" (paper digest), §3.4 "Output
+Embedding Parallelism and the Fused Cross-Entropy Optimization" (logits Y_i = X E_i^T on the
+rank's vocabulary rows; per-rank max, global max, per-rank sums of shifted exponentials,
+global sum, loss from log s and the correct logit; weight tying; padding the vocabulary so
+each rank's share is a multiple of 128) and "Megatron-LM, annotated", §3.4 The embedding
+and the loss (51,200 = ceil(50,257 / 1,024) * 1,024; 943 padding rows; b*s numbers are
+exchanged, not b*s*v).
+
+Readings where the pages are silent or garbled:
+* the max is per token (a row max over the rank's vocabulary);
+* the printed loss "log(s) minus the correct logit" drops the max shift; with s taken
+  relative to the global max M the loss is M + log s - y_target;
+* the one-round merge (each rank keeps its own max; sums are rescaled when merged) equals
+  the pages' two-round scheme in exact arithmetic; both are coded;
+* padding columns are ordinary logits unless ``mask_padding`` (then they are -inf);
+* rank r owns global columns [r*V_t, (r+1)*V_t); a rank that does not own the target
+  reports 0 for it; argmax ties go to the lowest global index.
+
+Pins: the padding arithmetic of "Megatron-LM, annotated" §3.4 (tests/golden); PyTorch CPU
+float64 cross_entropy for the unsplit loss; one-round == two-round == unsplit; argmax and max
+against numpy on the full logits.
+"""
+import numpy as np
+
+
+def pad_vocab(v, t, multiple=128):
+    """Smallest multiple of multiple*t that is >= v."""
+    q = multiple * t
+    return -(-v // q) * q
+
+
+def vocab_shard(E, t, r):
+    """Rank r's rows of the tied embedding: [r*V/t, (r+1)*V/t)."""
+    V = E.shape[0]
+    assert V % t == 0
+    w = V // t
+    return E[r * w:(r + 1) * w]
+
+
+def _masked_logits(X, E_rows, col0, Vreal, mask_padding):
+    y = X @ E_rows.T
+    if mask_padding:
+        cols = col0 + np.arange(E_rows.shape[0])
+        y = np.where(cols[None, :] < Vreal, y, -np.inf)
+    return y
+
+
+def xent_full(X, E, targets, Vreal, mask_padding=False):
+    """Unsplit: loss_n = logsumexp_v(y_n) - y_n[target_n], y = X E^T."""
+    y = _masked_logits(X, E, 0, Vreal, mask_padding)
+    m = y.max(axis=1)
+    lse = m + np.log(np.exp(y - m[:, None]).sum(axis=1))
+    n = np.arange(X.shape[0])
+    return {"loss": lse - y[n, targets], "max": m, "argmax": y.argmax(axis=1), "logits": y}
+
+
+def xent_shard_stats(X, E_r, targets, t, r, Vreal, mask_padding=False):
+    """One rank's per-token statistics: own max, sum of exp relative to it, the target's
+    logit if this rank owns it (else 0), and the argmax as a global column index."""
+    Vt = E_r.shape[0]
+    col0 = r * Vt
+    y = _masked_logits(X, E_r, col0, Vreal, mask_padding)
+    m = y.max(axis=1)
+    with np.errstate(invalid="ignore"):
+        s = np.where(np.isfinite(m), np.exp(y - m[:, None]).sum(axis=1), 0.0)
+    local = targets.astype(np.int64) - col0
+    owned = (local >= 0) & (local < Vt)
+    n = np.arange(X.shape[0])
+    tgt = np.where(owned, y[n, np.clip(local, 0, Vt - 1)], 0.0)
+    return {"max": m, "sumexp": s, "tgt": tgt, "argmax": y.argmax(axis=1) + col0}
+
+
+def xent_combine(maxes, sumexps, tgts):
+    """One-round merge of t ranks' statistics into per-token losses."""
+    Mx = np.max(np.stack(maxes), axis=0)
+    S = sum(s * np.exp(m - Mx) for m, s in zip(maxes, sumexps))
+    return Mx + np.log(S) - sum(tgts)
+
+
+def xent_two_round(X, E, targets, t, Vreal, mask_padding=False):
+    """The pages' scheme: round 1 all-reduces the per-rank maxima to M; round 2 all-reduces
+    each rank's sum of exp(y - M) and the owned target logits; loss = M + log s - y_target."""
+    shards = [vocab_shard(E, t, r) for r in range(t)]
+    Vt = shards[0].shape[0]
+    ys = [_masked_logits(X, Er, r * Vt, Vreal, mask_padding) for r, Er in enumerate(shards)]
+    Mx = np.max(np.stack([y.max(axis=1) for y in ys]), axis=0)
+    s = sum(np.exp(y - Mx[:, None]).sum(axis=1) for y in ys)
+    n = np.arange(X.shape[0])
+    tgt = np.zeros(X.shape[0])
+    for r, y in enumerate(ys):
+        local = targets.astype(np.int64) - r * Vt
+        owned = (local >= 0) & (local < Vt)
+        tgt += np.where(owned, y[n, np.clip(local, 0, Vt - 1)], 0.0)
+    return Mx + np.log(s) - tgt
