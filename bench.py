@@ -1,0 +1,214 @@
+"""Throughput of one GPU's share of the 8.3B-shape tensor-parallel layer (t = 8, rank 0) on MI355X.
+
+One step = the whole hot path of rank 0 over one batch of 8 x 1024 synthetic tokens:
+  * the pre-LN layer shard, forward + backward (h=3072, 32 heads of 96 -> 4 per rank,
+    ffn=12288 -> 1536 columns per rank): LN1, QKV GEMM, causal attention, output projection,
+    residual, LN2, MLP GEMM1 + bias + GeLU, GEMM2, residual; the backward with dgrad/wgrad GEMMs,
+    the attention backward, both LN backwards and the bias column sums;
+  * the vocabulary-parallel fused logits GEMM + cross-entropy statistics of the same model
+    (vocabulary 50,257 padded to 51,200 -> 6,400 rows per rank) and the loss merge.
+The all-reduce results rank 0 would receive (g forward, f backward, the loss statistics of the
+other ranks) are computed once before timing by running all 8 ranks, then handed to rank 0's
+step: no collective runs inside the timed region.
+
+value = algorithmic FLOP of the step / measured step time (TFLOP/s), FLOPs counted 2 per
+multiply-add, backward = 2x forward, causal attention over the visible pairs only.
+Prints ONE JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+B, S, H, HEADS, FFN, TP = 8, 1024, 3072, 32, 12288, 8
+VOCAB, VOCAB_PAD = 50257, 51200
+PEAK_BF16 = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12         # bytes/s
+
+
+def layer_flops(b, s, h, heads, ffn, t):
+    T = b * s
+    d = h // heads
+    mm = 2 * T * h * (3 * h) + 2 * T * h * h + 2 * 2 * T * h * ffn          # QKV, out-proj, MLP (unsplit)
+    attn = 4 * d * (s * (s + 1) // 2) * b * heads                          # QK^T and PV, visible pairs
+    return 3 * (mm + attn) / t
+
+
+def xent_flops(N, h, Vt):
+    return 2.0 * N * Vt * h
+
+
+def stage_inputs():
+    import tp_synth
+    w = tp_synth.WORKLOADS["layer_8p3b_t8"]
+    p = tp_synth.layer_inputs(w.seed, B, S, H, FFN, "bf16")
+    wx = tp_synth.WORKLOADS["xent_8p3b_t8"]
+    Vt = VOCAB_PAD // TP
+    xe = {"X": tp_synth.normal(wx.seed, 0, (B * S, H), 1.0, "bf16"),
+          "E0": tp_synth.normal(wx.seed, 14, (Vt, H), 0.02, "bf16"),
+          "targets": tp_synth.targets(wx.seed, 15, B * S, VOCAB)}
+    return p, xe
+
+
+def cpu_baseline(p, xe, seqs=8):
+    """The float64 oracle on rank 0's work for `seqs` sequences (the same step, fewer tokens)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    T = seqs * S
+    ht, Ft, Vt = H // TP, FFN // TP, VOCAB_PAD // TP
+    x, G = p["x"][:T], p["G"][:T]
+    Wqkv_r = oracle.qkv_shard(p["Wqkv"], HEADS, TP, 0)
+    bq = oracle.qkv_shard(p["bqkv"], HEADS, TP, 0)
+    Wo_r = oracle.wo_shard(p["Wo"], HEADS, TP, 0)
+    A_r, b1_r, B_r = p["A"][:, :Ft], p["b1"][:Ft], p["B"][:Ft]
+    t0 = time.perf_counter()
+    l1 = oracle.layernorm_fwd(x, p["ln1_g"], p["ln1_b"])
+    fa = oracle.attn_shard_fwd(l1["y"], Wqkv_r, bq, Wo_r, seqs, S, HEADS // TP)
+    x1 = x + fa["Z"] + p["bo"]                 # rank 0's partial stands in for the all-reduced sum
+    l2 = oracle.layernorm_fwd(x1, p["ln2_g"], p["ln2_b"])
+    fm = oracle.mlp_shard_fwd(l2["y"], A_r, b1_r, B_r)
+    gm = oracle.mlp_shard_bwd(l2["y"], A_r, B_r, fm["U"], fm["Y"], G)
+    b2 = oracle.layernorm_bwd(x1, p["ln2_g"], l2["mean"], l2["rstd"], gm["dX"])
+    dx1 = G + b2["dx"]
+    ga = oracle.attn_shard_bwd(l1["y"], Wqkv_r, Wo_r, fa, dx1, seqs, S, HEADS // TP)
+    oracle.layernorm_bwd(x, p["ln1_g"], l1["mean"], l1["rstd"], ga["dXn"])
+    oracle.xent_shard_stats(xe["X"][:T], xe["E0"], xe["targets"][:T], TP, 0, VOCAB)
+    dt = time.perf_counter() - t0
+    flops = layer_flops(seqs, S, H, HEADS, FFN, TP) + xent_flops(T, H, Vt)
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"rank 0 step (layer fwd+bwd + vocab-shard statistics) on {seqs} of {B} sequences "
+                      f"({T} tokens), float64 NumPy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
+              "(the multi-GPU all-reduces are not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tensor_transformer_layer_amd as tp
+    from tensor_transformer_layer_amd.layer import LayerShard, rank_params
+
+    dev = "cuda:0"
+    T = B * S
+    Vt = VOCAB_PAD // TP
+    p, xe = stage_inputs()
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(dev)
+
+    x, G = d(p["x"]), d(p["G"])
+    # verification run over all ranks: the sums rank 0 would receive
+    shards = [LayerShard(B, S, H, HEADS, FFN, TP, r, rank_params(p, HEADS, TP, r, dev), dev) for r in range(TP)]
+    attn_sum = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    mlp_sum, dxn2_sum, dxn1_sum = (torch.empty_like(attn_sum) for _ in range(3))
+    shards[0].combine([sh.attn_fwd(x) for sh in shards], None, None, attn_sum)
+    x1 = torch.empty_like(attn_sum)
+    shards[0].combine([attn_sum], shards[0].p["bo"], x, x1)
+    shards[0].combine([sh.mlp_fwd(x1) for sh in shards], None, None, mlp_sum)
+    shards[0].combine([sh.mlp_bwd(G) for sh in shards], None, None, dxn2_sum)
+    dx1 = shards[0].ln2_bwd(dxn2_sum, G)
+    shards[0].combine([sh.attn_bwd(dx1) for sh in shards], None, None, dxn1_sum)
+    torch.cuda.synchronize()
+    rank0 = shards[0]
+    del shards
+    torch.cuda.empty_cache()
+
+    # rank 0's vocabulary shard; the other ranks' loss statistics are pre-staged (their values only
+    # feed the merge, which reads t per-token triples)
+    Xv, E0 = d(xe["X"]), d(xe["E0"])
+    tg = torch.from_numpy(xe["targets"]).to(dev)
+    mx, se, tv = (torch.empty(T, dtype=torch.float32, device=dev) for _ in range(3))
+    am = torch.empty(T, dtype=torch.int32, device=dev)
+    xws_bytes = tp.tp_vocab_xent_shard_fwd_workspace(T, H, VOCAB_PAD, TP, tp.TP_BF16)
+    xws = torch.empty(xws_bytes, dtype=torch.uint8, device=dev)
+    peers = [(mx, se, tv)] + [tuple(torch.empty(T, dtype=torch.float32, device=dev) for _ in range(3))
+                              for _ in range(TP - 1)]
+    tp.tp_vocab_xent_shard_fwd(T, H, VOCAB_PAD, VOCAB, TP, 0, tp.TP_BF16, 0, Xv, E0, tg, mx, se, tv, am, xws, xws_bytes)
+    for q in peers[1:]:
+        for a, b_ in zip(q, (mx, se, tv)):
+            a.copy_(b_)
+    loss = torch.empty(T, dtype=torch.float32, device=dev)
+    mean = torch.empty(1, dtype=torch.float32, device=dev)
+
+    stream = torch.cuda.current_stream()
+    xev = []
+
+    def step(record):
+        rank0.step(x, G, attn_sum, mlp_sum, dxn2_sum, dxn1_sum)
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        tp.tp_vocab_xent_shard_fwd(T, H, VOCAB_PAD, VOCAB, TP, 0, tp.TP_BF16, 0, Xv, E0, tg, mx, se, tv, am, xws,
+                                   xws_bytes)
+        if record:
+            e1.record(stream)
+            xev.append((e0, e1))
+        tp.tp_vocab_xent_combine(T, TP, [q[0] for q in peers], [q[1] for q in peers], [q[2] for q in peers], loss, mean)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    fl_layer = layer_flops(B, S, H, HEADS, FFN, TP)
+    fl_xent = xent_flops(T, H, Vt)
+    value = (fl_layer + fl_xent) / (ms * 1e-3) / 1e12
+    xent_ms = float(np.mean([a.elapsed_time(b_) for a, b_ in xev]))
+    xent_achieved = fl_xent / (xent_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": "layer-shard TFLOP/s fwd+bwd (% bf16 MFMA peak), 8.3B shape t=8, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, uniform targets)",
+        "config": {"workload": "8.3B-shape layer shard t=8 rank 0 fwd+bwd + vocab-parallel xent shard",
+                   "batch": B, "seq_len": S, "hidden": H, "heads": HEADS, "ffn": FFN, "tp": TP,
+                   "vocab_padded": VOCAB_PAD, "parallelism": "one rank of tp8 (sums pre-staged)"},
+        "pct_bf16_peak": round(100 * value * 1e12 / PEAK_BF16, 2),
+        "breakdown": {"layer_gflop": round(fl_layer / 1e9, 2), "xent_gflop": round(fl_xent / 1e9, 2),
+                      "xent_ms": round(xent_ms, 4),
+                      "layer_ms": round(ms - xent_ms, 4),
+                      "layer_tflops": round(fl_layer / ((ms - xent_ms) * 1e-3) / 1e12, 2)},
+        "roofline": {"bound": "mfma", "kernel": "fused vocab logits GEMM + CE statistics (gemm_bf16_kernel "
+                     "with EpiXent, plus its per-token tile merge)",
+                     "achieved": round(xent_achieved, 2), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                     "frac": round(xent_achieved * 1e12 / PEAK_BF16, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p, xe)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * tp_shard.h — C ABI of one GPU's share of a Megatron-style tensor-parallel transformer layer,
+ * built for AMD MI355X (gfx950).
+ *
+ * The operations are those of "Megatron-LM: Training Multi-Billion Parameter Language Models
+ * Using Model Parallelism" (paper digest), §3.4 Detailed, Sentence-Based Technical Breakdown,
+ * and of "Tensor and pipeline parallelism, and choosing a layout" (ML Systems, lesson 9), §3,
+ * Proposition (Megatron MLP split). Each call computes ONE rank's share from the replicated
+ * input and that rank's own weight shard, and returns a sharded output or a full-size partial.
+ * Summing partials across ranks (the paper's g in the forward pass and f in the backward pass)
+ * is the caller's job; tp_sum_partials does it on one device.
+ *
+ * Conventions shared by every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library never allocates,
+ *    frees or synchronises; it launches only on the stream it is given (0 = null stream).
+ *  - Row-major, contiguous, 16-byte aligned. Tokens are rows: token = batch*s + position.
+ *  - dt selects the element type of activations, weights, saved tensors and partials
+ *    (TP_BF16: bfloat16 in, fp32 accumulate, bfloat16 out; TP_F32: fp32 throughout).
+ *    Statistics (LayerNorm mean/rstd, attention lse, cross-entropy max/sumexp/target) are fp32.
+ *  - Feature sizes (h, ffn/t, 3h/t, h/t, V/t) must be multiples of 8. Token counts are free.
+ *  - Errors: arguments are checked on the host before any launch. On failure the call returns
+ *    a non-zero tp_status, launches nothing, writes nothing and sets tp_last_error(). A launch
+ *    failure reported by the HIP runtime returns TP_ERR_HIP. Calls with zero tokens return
+ *    TP_OK and launch nothing. Nothing aborts or throws across this boundary.
+ *  - Determinism: fixed reduction orders, no floating-point atomics; repeated calls on the
+ *    same inputs give identical bits.
+ *  - Workspace: calls that need scratch memory take (ws, ws_bytes); the matching *_workspace
+ *    function returns the minimum size for the same shape arguments. The library does not keep
+ *    anything in the workspace between calls.
+ */
+#ifndef TP_SHARD_H
+#define TP_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h> /* hipStream_t only */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TP_ABI_VERSION 1
+
+typedef enum tp_status {
+    TP_OK = 0,
+    TP_ERR_ARG = 1,         /* null pointer, t < 1, r outside [0, t), bad flag */
+    TP_ERR_SHAPE = 2,       /* a size is negative, not divisible as required, or not a multiple of 8 */
+    TP_ERR_DTYPE = 3,       /* unknown dtype */
+    TP_ERR_WORKSPACE = 4,   /* ws_bytes smaller than the *_workspace query returns */
+    TP_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
+    TP_ERR_UNSUPPORTED = 6  /* valid request this build does not implement (e.g. fp32 attention) */
+} tp_status;
+
+typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* Version of this header's ABI (TP_ABI_VERSION). */
+int tp_abi_version(void);
+
+/* Text of the last error on the calling thread; "" if the last call succeeded. The pointer is
+ * valid until the next tp_* call on the same thread. */
+const char* tp_last_error(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * MLP block, column-parallel first GEMM + row-parallel second GEMM.
+ * Passage: "Megatron-LM ..." digest §3.4, "Column-Parallel GEMM for the First MLP Layer"
+ * (A cut by columns, GeLU applied locally) and "Row-Parallel GEMM for the Second MLP Layer"
+ * (B cut by rows, each rank's product is a full-size partial summed by g). GeLU is the erf form
+ * ("Megatron-LM, annotated", §2.2).
+ *
+ * Rank r of t, F_t = ffn/t:
+ *   X    [T, h]    replicated input (f is the identity forward)
+ *   A_r  [h, F_t]  columns r*F_t .. (r+1)*F_t of A [h, ffn]
+ *   b1_r [F_t]     the same slice of the first bias (may be NULL: no bias)
+ *   B_r  [F_t, h]  rows r*F_t .. (r+1)*F_t of B [ffn, h]
+ * Outputs (saved for backward):
+ *   U_r  [T, F_t]  X A_r + b1_r          (pre-activation)
+ *   Y_r  [T, F_t]  GeLU(U_r)
+ *   Z_r  [T, h]    Y_r B_r, the rank's partial WITHOUT the second bias (added once after the sum)
+ * ------------------------------------------------------------------------------------------- */
+tp_status tp_mlp_shard_fwd(int T, int h, int ffn, int t, int r, tp_dtype dt,
+                           const void* X, const void* A_r, const void* b1_r, const void* B_r,
+                           void* U_r, void* Y_r, void* Z_r, hipStream_t stream);
+
+/* Backward of the MLP shard. Passage: "Tensor and pipeline parallelism ..." §3, Proposition
+ * (Megatron MLP split), proof steps 4-5:
+ *   dU_r = (G B_r^T) * GeLU'(U_r)   (kept in the workspace)
+ *   dB_r = Y_r^T G     [F_t, h]      dA_r = X^T dU_r  [h, F_t]    db1_r = column sums of dU_r [F_t]
+ *   dX_r = dU_r A_r^T  [T, h]        the rank's partial of dL/dX; f sums the ranks' partials.
+ * G [T, h] = dL/dZ is replicated (g is the identity backward). db1_r may be NULL.
+ * accumulate = 0 overwrites dA_r, db1_r, dB_r; 1 adds into them (dX_r is always overwritten). */
+size_t tp_mlp_shard_bwd_workspace(int T, int h, int ffn, int t, tp_dtype dt);
+tp_status tp_mlp_shard_bwd(int T, int h, int ffn, int t, int r, tp_dtype dt,
+                           const void* X, const void* A_r, const void* B_r, const void* U_r,
+                           const void* Y_r, const void* G, void* dX_r, void* dA_r, void* db1_r,
+                           void* dB_r, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Self-attention block, head-sharded. Passage: "Megatron-LM ..." digest §3.4, "Attention Head
+ * Parallelism in the Self-Attention Block" (Q, K, V cut by columns along whole heads; softmax
+ * of query key^T / sqrt(d_k) times value per head, locally; output projection cut by rows,
+ * partials summed by g). Causal masking: a GPT-2 decoder attends left to right
+ * ("Megatron-LM, annotated", §2.2). Only dt = TP_BF16 is implemented (fp32 softmax inside).
+ *
+ * Rank r of t owns heads r*heads/t .. (r+1)*heads/t - 1; d = h/heads; h_t = h/t:
+ *   Xn     [b*s, h]     replicated (normalised) input
+ *   Wqkv_r [h, 3h_t]    [Wq[:, H_r] | Wk[:, H_r] | Wv[:, H_r]] with H_r the rank's head columns
+ *   bqkv_r [3h_t]       the matching bias slices (may be NULL)
+ *   Wo_r   [h_t, h]     rows H_r of the output projection
+ * Outputs (saved for backward):
+ *   QKV_r  [b*s, 3h_t]  Xn Wqkv_r + bqkv_r, packed [Q | K | V], local head j at columns j*d
+ *   O_r    [b*s, h_t]   attention output of the rank's heads
+ *   lse_r  [b, heads/t, s] fp32, natural log of each query's softmax denominator
+ *   Z_r    [b*s, h]     O_r Wo_r, partial WITHOUT the output bias
+ * causal = 1: query i sees keys j <= i of its own sequence; 0: all keys of the sequence. */
+tp_status tp_attn_shard_fwd(int b, int s, int h, int heads, int t, int r, tp_dtype dt, int causal,
+                            const void* Xn, const void* Wqkv_r, const void* bqkv_r, const void* Wo_r,
+                            void* QKV_r, void* O_r, float* lse_r, void* Z_r, hipStream_t stream);
+
+/* Backward of the attention shard for G [b*s, h] = dL/dZ (replicated). The attention chain is the
+ * textbook one (not on the pages): dO = G Wo_r^T; D = rowsum(dO * O); P recomputed from lse;
+ * dV = P^T dO; dS = P * (dO V^T - D); dQ = dS K / sqrt(d); dK = dS^T Q / sqrt(d).
+ * Outputs: dXn_r [b*s, h] partial (f sums them); dWqkv_r [h, 3h_t]; dbqkv_r [3h_t] (may be NULL);
+ * dWo_r [h_t, h]. accumulate as in tp_mlp_shard_bwd (dXn_r always overwritten). */
+size_t tp_attn_shard_bwd_workspace(int b, int s, int h, int heads, int t, tp_dtype dt);
+tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dtype dt, int causal,
+                            const void* Xn, const void* Wqkv_r, const void* Wo_r, const void* QKV_r,
+                            const void* O_r, const float* lse_r, const void* G, void* dXn_r,
+                            void* dWqkv_r, void* dbqkv_r, void* dWo_r, int accumulate,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Vocabulary-parallel fused logits GEMM + cross-entropy statistics. Passage: "Megatron-LM ..."
+ * digest §3.4, "Output Embedding Parallelism and the Fused Cross-Entropy Optimization" (logits
+ * X E_r^T on the rank's vocabulary rows; per-rank maximum; sums of exponentials; the correct
+ * token's logit; padding so each rank's share is a multiple of 128; weight tying).
+ * The logits never reach memory. Rank r owns global columns [r*V_t, (r+1)*V_t), V_t = Vpad/t.
+ *   X [N, h]; E_r [V_t, h] rows of the tied embedding; targets int32 [N] in [0, Vreal)
+ *   (targets are not range-checked: that would need a device sync; out-of-range ids give 0).
+ * Outputs per token (fp32 / int32, [N] each):
+ *   max_r     maximum logit over the rank's columns
+ *   sumexp_r  sum of exp(logit - max_r) over the rank's columns
+ *   tgt_r     the target's logit if this rank owns it, else 0
+ *   argmax_r  global column index of max_r, lowest index on ties (may be NULL)
+ * mask_padding = 1 treats columns >= Vreal as -inf; 0 scores them like any other column.
+ * dt = TP_BF16 only. */
+size_t tp_vocab_xent_shard_fwd_workspace(int N, int h, int Vpad, int t, tp_dtype dt);
+tp_status tp_vocab_xent_shard_fwd(int N, int h, int Vpad, int Vreal, int t, int r, tp_dtype dt,
+                                  int mask_padding, const void* X, const void* E_r,
+                                  const int32_t* targets, float* max_r, float* sumexp_r, float* tgt_r,
+                                  int32_t* argmax_r, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The rank's fp32 logits [N, V_t], computed by the same GEMM kernel as tp_vocab_xent_shard_fwd
+ * (same tiles, same accumulation order, hence the same bits). For verification of the fused
+ * statistics; not on the hot path. */
+tp_status tp_vocab_logits_shard(int N, int h, int Vpad, int t, int r, tp_dtype dt, const void* X,
+                                const void* E_r, float* logits, hipStream_t stream);
+
+/* Merge of t ranks' statistics into per-token losses, standing in for the cross-entropy's
+ * all-reduces on one device: M = max_r max_r; S = sum_r sumexp_r exp(max_r - M);
+ * loss = M + log S - sum_r tgt_r. max_r/sumexp_r/tgt_r are HOST arrays of t device pointers.
+ * loss [N] fp32; mean_loss (1 float, may be NULL) gets the mean over N. */
+tp_status tp_vocab_xent_combine(int N, int t, const float* const* max_r, const float* const* sumexp_r,
+                                const float* const* tgt_r, float* loss, float* mean_loss,
+                                hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Helpers for the replicated parts of the layer ("Megatron-LM ..." digest §3.4, "Duplicate
+ * Computation vs. Communication": norm, dropout and residual are computed by every rank).
+ * ------------------------------------------------------------------------------------------- */
+
+/* out = sum_{r=0}^{t-1} parts[r] + bias (broadcast over rows) + residual, summed in fp32 in rank
+ * order. parts is a HOST array of t device pointers to [rows, cols] tensors of in_dt; bias
+ * [cols] and residual [rows, cols] are in out_dt and may be NULL. Stands in for g (forward) and
+ * f (backward) on one device. */
+tp_status tp_sum_partials(int rows, int cols, int t, tp_dtype in_dt, const void* const* parts,
+                          const void* bias, const void* residual, void* out, tp_dtype out_dt,
+                          hipStream_t stream);
+
+/* LayerNorm over the last dimension: y = (x - mean) / sqrt(var + eps) * gamma + beta with the
+ * biased variance. x, y [T, h] and gamma, beta [h] in dt; mean, rstd [T] fp32 (may be NULL). */
+tp_status tp_layernorm_fwd(int T, int h, tp_dtype dt, float eps, const void* x, const void* gamma,
+                           const void* beta, void* y, float* mean, float* rstd, hipStream_t stream);
+
+/* LayerNorm backward: dx = dres + d(LN)/dx^T dy; dgamma = sum_rows dy * xhat; dbeta = sum_rows dy.
+ * dres [T, h] (the residual branch's gradient) may be NULL. dgamma/dbeta [h] in dt may be NULL;
+ * accumulate as above. */
+size_t tp_layernorm_bwd_workspace(int T, int h, tp_dtype dt);
+tp_status tp_layernorm_bwd(int T, int h, tp_dtype dt, const void* x, const void* gamma,
+                           const float* mean, const float* rstd, const void* dy, const void* dres,
+                           void* dx, void* dgamma, void* dbeta, int accumulate,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Column sums of G [T, n] into out [n] (the replicated bias gradients of the row-parallel
+ * layers), in a fixed order. */
+size_t tp_colsum_workspace(int T, int n, tp_dtype dt);
+tp_status tp_colsum(int T, int n, tp_dtype dt, const void* G, void* out, int accumulate,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TP_SHARD_H */

@@ -1,0 +1,193 @@
+"""Python binding of libtpshard.so, one GPU's share of a tensor-parallel transformer layer on
+MI355X (gfx950).
+
+Argument marshalling only: each function below has the name, argument order and meaning of the
+C entry point in ``include/tp_shard.h``. Tensor arguments may be torch tensors (their
+``data_ptr()`` is passed), raw integer device addresses, or None (NULL). ``stream`` defaults to
+torch's current HIP stream. A non-zero status raises ``TPError`` with ``tp_last_error()``.
+Every computation happens in the library's HIP kernels; there is no fallback path. Importing
+this package fails if the library has not been built
+(``python -m tensor_transformer_layer_amd.build``).
+"""
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtpshard.so")
+
+TP_OK, TP_ERR_ARG, TP_ERR_SHAPE, TP_ERR_DTYPE, TP_ERR_WORKSPACE, TP_ERR_HIP, TP_ERR_UNSUPPORTED = range(7)
+TP_F32, TP_BF16 = 0, 1
+STATUS_NAMES = {0: "TP_OK", 1: "TP_ERR_ARG", 2: "TP_ERR_SHAPE", 3: "TP_ERR_DTYPE", 4: "TP_ERR_WORKSPACE",
+                5: "TP_ERR_HIP", 6: "TP_ERR_UNSUPPORTED"}
+
+
+class TPError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with 'python -m tensor_transformer_layer_amd.build'")
+lib = C.CDLL(LIB_PATH)
+
+_i, _z, _p, _f = C.c_int, C.c_size_t, C.c_void_p, C.c_float
+_pp = C.POINTER(C.c_void_p)
+
+# name -> (restype, argtypes), in header order
+SIGNATURES = {
+    "tp_abi_version": (_i, []),
+    "tp_last_error": (C.c_char_p, []),
+    "tp_mlp_shard_fwd": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "tp_mlp_shard_bwd_workspace": (_z, [_i, _i, _i, _i, _i]),
+    "tp_mlp_shard_bwd": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
+    "tp_attn_shard_fwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "tp_attn_shard_bwd_workspace": (_z, [_i, _i, _i, _i, _i, _i]),
+    "tp_attn_shard_bwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i,
+                               _p, _z, _p]),
+    "tp_vocab_xent_shard_fwd_workspace": (_z, [_i, _i, _i, _i, _i]),
+    "tp_vocab_xent_shard_fwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _z, _p]),
+    "tp_vocab_logits_shard": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p]),
+    "tp_vocab_xent_combine": (_i, [_i, _i, _pp, _pp, _pp, _p, _p, _p]),
+    "tp_sum_partials": (_i, [_i, _i, _i, _i, _pp, _p, _p, _p, _i, _p]),
+    "tp_layernorm_fwd": (_i, [_i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p]),
+    "tp_layernorm_bwd_workspace": (_z, [_i, _i, _i]),
+    "tp_layernorm_bwd": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
+    "tp_colsum_workspace": (_z, [_i, _i, _i]),
+    "tp_colsum": (_i, [_i, _i, _i, _p, _p, _i, _p, _z, _p]),
+}
+for _name, (_rt, _at) in SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _rt
+    _fn.argtypes = _at
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _ptr_array(xs):
+    arr = (C.c_void_p * len(xs))(*[_ptr(x) for x in xs])
+    return C.cast(arr, _pp), arr
+
+
+def _dt(dt):
+    if isinstance(dt, int):
+        return dt
+    import torch
+    if dt == torch.bfloat16:
+        return TP_BF16
+    if dt == torch.float32:
+        return TP_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status):
+    if status != TP_OK:
+        raise TPError(status, lib.tp_last_error().decode())
+
+
+def tp_abi_version():
+    return lib.tp_abi_version()
+
+
+def tp_last_error():
+    return lib.tp_last_error().decode()
+
+
+def tp_mlp_shard_fwd(T, h, ffn, t, r, dt, X, A_r, b1_r, B_r, U_r, Y_r, Z_r, stream=None):
+    _check(lib.tp_mlp_shard_fwd(T, h, ffn, t, r, _dt(dt), _ptr(X), _ptr(A_r), _ptr(b1_r), _ptr(B_r), _ptr(U_r),
+                                _ptr(Y_r), _ptr(Z_r), _stream(stream)))
+
+
+def tp_mlp_shard_bwd_workspace(T, h, ffn, t, dt):
+    return lib.tp_mlp_shard_bwd_workspace(T, h, ffn, t, _dt(dt))
+
+
+def tp_mlp_shard_bwd(T, h, ffn, t, r, dt, X, A_r, B_r, U_r, Y_r, G, dX_r, dA_r, db1_r, dB_r, accumulate, ws,
+                     ws_bytes, stream=None):
+    _check(lib.tp_mlp_shard_bwd(T, h, ffn, t, r, _dt(dt), _ptr(X), _ptr(A_r), _ptr(B_r), _ptr(U_r), _ptr(Y_r),
+                                _ptr(G), _ptr(dX_r), _ptr(dA_r), _ptr(db1_r), _ptr(dB_r), accumulate, _ptr(ws),
+                                ws_bytes, _stream(stream)))
+
+
+def tp_attn_shard_fwd(b, s, h, heads, t, r, dt, causal, Xn, Wqkv_r, bqkv_r, Wo_r, QKV_r, O_r, lse_r, Z_r,
+                      stream=None):
+    _check(lib.tp_attn_shard_fwd(b, s, h, heads, t, r, _dt(dt), causal, _ptr(Xn), _ptr(Wqkv_r), _ptr(bqkv_r),
+                                 _ptr(Wo_r), _ptr(QKV_r), _ptr(O_r), _ptr(lse_r), _ptr(Z_r), _stream(stream)))
+
+
+def tp_attn_shard_bwd_workspace(b, s, h, heads, t, dt):
+    return lib.tp_attn_shard_bwd_workspace(b, s, h, heads, t, _dt(dt))
+
+
+def tp_attn_shard_bwd(b, s, h, heads, t, r, dt, causal, Xn, Wqkv_r, Wo_r, QKV_r, O_r, lse_r, G, dXn_r, dWqkv_r,
+                      dbqkv_r, dWo_r, accumulate, ws, ws_bytes, stream=None):
+    _check(lib.tp_attn_shard_bwd(b, s, h, heads, t, r, _dt(dt), causal, _ptr(Xn), _ptr(Wqkv_r), _ptr(Wo_r),
+                                 _ptr(QKV_r), _ptr(O_r), _ptr(lse_r), _ptr(G), _ptr(dXn_r), _ptr(dWqkv_r),
+                                 _ptr(dbqkv_r), _ptr(dWo_r), accumulate, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tp_vocab_xent_shard_fwd_workspace(N, h, Vpad, t, dt):
+    return lib.tp_vocab_xent_shard_fwd_workspace(N, h, Vpad, t, _dt(dt))
+
+
+def tp_vocab_xent_shard_fwd(N, h, Vpad, Vreal, t, r, dt, mask_padding, X, E_r, targets, max_r, sumexp_r, tgt_r,
+                            argmax_r, ws, ws_bytes, stream=None):
+    _check(lib.tp_vocab_xent_shard_fwd(N, h, Vpad, Vreal, t, r, _dt(dt), mask_padding, _ptr(X), _ptr(E_r),
+                                       _ptr(targets), _ptr(max_r), _ptr(sumexp_r), _ptr(tgt_r), _ptr(argmax_r),
+                                       _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tp_vocab_logits_shard(N, h, Vpad, t, r, dt, X, E_r, logits, stream=None):
+    _check(lib.tp_vocab_logits_shard(N, h, Vpad, t, r, _dt(dt), _ptr(X), _ptr(E_r), _ptr(logits), _stream(stream)))
+
+
+def tp_vocab_xent_combine(N, t, max_r, sumexp_r, tgt_r, loss, mean_loss=None, stream=None):
+    pm, _a = _ptr_array(max_r)
+    ps, _b = _ptr_array(sumexp_r)
+    pt, _c = _ptr_array(tgt_r)
+    _check(lib.tp_vocab_xent_combine(N, t, pm, ps, pt, _ptr(loss), _ptr(mean_loss), _stream(stream)))
+
+
+def tp_sum_partials(rows, cols, t, in_dt, parts, bias, residual, out, out_dt, stream=None):
+    pp, _keep = _ptr_array(parts)
+    _check(lib.tp_sum_partials(rows, cols, t, _dt(in_dt), pp, _ptr(bias), _ptr(residual), _ptr(out), _dt(out_dt),
+                               _stream(stream)))
+
+
+def tp_layernorm_fwd(T, h, dt, eps, x, gamma, beta, y, mean, rstd, stream=None):
+    _check(lib.tp_layernorm_fwd(T, h, _dt(dt), eps, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean),
+                                _ptr(rstd), _stream(stream)))
+
+
+def tp_layernorm_bwd_workspace(T, h, dt):
+    return lib.tp_layernorm_bwd_workspace(T, h, _dt(dt))
+
+
+def tp_layernorm_bwd(T, h, dt, x, gamma, mean, rstd, dy, dres, dx, dgamma, dbeta, accumulate, ws, ws_bytes,
+                     stream=None):
+    _check(lib.tp_layernorm_bwd(T, h, _dt(dt), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dy), _ptr(dres),
+                                _ptr(dx), _ptr(dgamma), _ptr(dbeta), accumulate, _ptr(ws), ws_bytes,
+                                _stream(stream)))
+
+
+def tp_colsum_workspace(T, n, dt):
+    return lib.tp_colsum_workspace(T, n, _dt(dt))
+
+
+def tp_colsum(T, n, dt, G, out, accumulate, ws, ws_bytes, stream=None):
+    _check(lib.tp_colsum(T, n, _dt(dt), _ptr(G), _ptr(out), accumulate, _ptr(ws), ws_bytes, _stream(stream)))

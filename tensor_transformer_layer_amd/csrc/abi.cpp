@@ -1,0 +1,449 @@
+// C ABI entry points: host-side validation, workspace carving and launch sequencing.
+// Operation definitions and argument conventions are documented in include/tp_shard.h.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "launch.h"
+#include "tp_shard.h"
+
+using namespace tp;
+
+namespace {
+
+thread_local std::string g_err;
+
+tp_status fail(tp_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+tp_status ok() {
+    g_err.clear();
+    return TP_OK;
+}
+
+#define HIP_TRY(expr, what)                                                                          \
+    do {                                                                                             \
+        hipError_t e_ = (expr);                                                                      \
+        if (e_ != hipSuccess) return fail(TP_ERR_HIP, "%s: %s", (what), hipGetErrorString(e_));      \
+    } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// required pointer: non-null and 16-byte aligned
+#define NEED(p)                                                                                      \
+    do {                                                                                             \
+        if (!(p)) return fail(TP_ERR_ARG, "%s: argument '%s' is NULL", fn, #p);                      \
+        if (!aligned16(p)) return fail(TP_ERR_ARG, "%s: argument '%s' is not 16-byte aligned", fn, #p); \
+    } while (0)
+// optional pointer: null, or 16-byte aligned
+#define OPT(p)                                                                                       \
+    do {                                                                                             \
+        if ((p) && !aligned16(p)) return fail(TP_ERR_ARG, "%s: argument '%s' is not 16-byte aligned", fn, #p); \
+    } while (0)
+
+tp_status check_dt(const char* fn, tp_dtype dt) {
+    if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)dt);
+    return TP_OK;
+}
+
+tp_status check_rank(const char* fn, int t, int r) {
+    if (t < 1) return fail(TP_ERR_ARG, "%s: tp degree t=%d must be >= 1", fn, t);
+    if (r < 0 || r >= t) return fail(TP_ERR_ARG, "%s: rank r=%d outside [0, %d)", fn, r, t);
+    return TP_OK;
+}
+
+tp_status check_mult8(const char* fn, const char* what, long v) {
+    if (v <= 0 || v % 8 != 0) return fail(TP_ERR_SHAPE, "%s: %s=%ld must be a positive multiple of 8", fn, what, v);
+    return TP_OK;
+}
+
+size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+size_t esize(tp_dtype dt) { return dt == TP_BF16 ? 2 : 4; }
+
+GemmReq req(int M, int N, int K, const void* A, int lda, int a_mn, const void* B, int ldb, int b_mn, int epi,
+            void* out, int ldc) {
+    GemmReq g;
+    memset(&g, 0, sizeof(g));
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda; g.a_mn = a_mn;
+    g.B = B; g.ldb = ldb; g.b_mn = b_mn;
+    g.epi = epi; g.out = out; g.ldc = ldc;
+    return g;
+}
+
+hipError_t run_gemm(tp_dtype dt, const GemmReq& g, bool allow_split, void* split_ws, hipStream_t st) {
+    if (dt == TP_F32) return gemm_f32(g, st);
+    GemmPlan p = plan_gemm_bf16(g.M, g.N, g.K, allow_split);
+    return gemm_bf16(g, p, split_ws, st);
+}
+
+size_t wgrad_split_ws(tp_dtype dt, int M, int N, int K) {
+    if (dt != TP_BF16) return 0;
+    return split_ws_bytes(plan_gemm_bf16(M, N, K, true), M, N);
+}
+
+size_t colsum_ws(int T, int n) { return (size_t)colsum_row_blocks(T) * n * sizeof(float); }
+
+struct MlpWs {
+    size_t dU, scratch, total;
+};
+MlpWs mlp_ws(int T, int h, int Ft, tp_dtype dt) {
+    MlpWs w;
+    w.dU = al256((size_t)T * Ft * esize(dt));
+    size_t s = std::max(wgrad_split_ws(dt, Ft, h, T), wgrad_split_ws(dt, h, Ft, T));
+    w.scratch = al256(std::max(s, colsum_ws(T, Ft)));
+    w.total = w.dU + w.scratch;
+    return w;
+}
+
+struct AttnWs {
+    size_t dO, D, dQKV, scratch, total;
+};
+AttnWs attn_ws(int b, int s, int h, int heads_t, int h_t) {
+    long T = (long)b * s;
+    AttnWs w;
+    w.dO = al256((size_t)T * h_t * 2);
+    w.D = al256((size_t)b * heads_t * s * sizeof(float));
+    w.dQKV = al256((size_t)T * 3 * h_t * 2);
+    size_t sp = std::max(wgrad_split_ws(TP_BF16, h_t, h, (int)T), wgrad_split_ws(TP_BF16, h, 3 * h_t, (int)T));
+    w.scratch = al256(std::max(sp, colsum_ws((int)T, 3 * h_t)));
+    w.total = w.dO + w.D + w.dQKV + w.scratch;
+    return w;
+}
+
+tp_status check_mlp(const char* fn, int T, int h, int ffn, int t, int r, tp_dtype dt) {
+    tp_status s;
+    if ((s = check_dt(fn, dt)) != TP_OK) return s;
+    if ((s = check_rank(fn, t, r)) != TP_OK) return s;
+    if (T < 0) return fail(TP_ERR_SHAPE, "%s: T=%d is negative", fn, T);
+    if ((s = check_mult8(fn, "h", h)) != TP_OK) return s;
+    if (ffn <= 0 || ffn % t != 0) return fail(TP_ERR_SHAPE, "%s: ffn=%d must be a positive multiple of t=%d", fn, ffn, t);
+    return check_mult8(fn, "ffn/t", ffn / t);
+}
+
+tp_status check_attn(const char* fn, int b, int s, int h, int heads, int t, int r, tp_dtype dt, int causal) {
+    tp_status st;
+    if ((st = check_dt(fn, dt)) != TP_OK) return st;
+    if (dt != TP_BF16) return fail(TP_ERR_UNSUPPORTED, "%s: attention is implemented for bf16 only", fn);
+    if ((st = check_rank(fn, t, r)) != TP_OK) return st;
+    if (causal != 0 && causal != 1) return fail(TP_ERR_ARG, "%s: causal=%d must be 0 or 1", fn, causal);
+    if (b < 0 || s < 0) return fail(TP_ERR_SHAPE, "%s: b=%d, s=%d must be >= 0", fn, b, s);
+    if (b > 65535) return fail(TP_ERR_SHAPE, "%s: b=%d exceeds 65535", fn, b);
+    if ((long)b * s > INT32_MAX / 4) return fail(TP_ERR_SHAPE, "%s: b*s too large", fn);
+    if ((st = check_mult8(fn, "h", h)) != TP_OK) return st;
+    if (heads <= 0 || heads % t != 0) return fail(TP_ERR_SHAPE, "%s: heads=%d must be a positive multiple of t=%d", fn, heads, t);
+    if (h % heads != 0) return fail(TP_ERR_SHAPE, "%s: h=%d is not a multiple of heads=%d", fn, h, heads);
+    int d = h / heads;
+    if (d != 64 && d != 96 && d != 128) return fail(TP_ERR_UNSUPPORTED, "%s: head width %d (supported: 64, 96, 128)", fn, d);
+    return TP_OK;
+}
+
+tp_status check_vocab(const char* fn, int N, int h, int Vpad, int t, int r, tp_dtype dt) {
+    tp_status s;
+    if ((s = check_dt(fn, dt)) != TP_OK) return s;
+    if (dt != TP_BF16) return fail(TP_ERR_UNSUPPORTED, "%s: the vocabulary GEMM is implemented for bf16 only", fn);
+    if ((s = check_rank(fn, t, r)) != TP_OK) return s;
+    if (N < 0) return fail(TP_ERR_SHAPE, "%s: N=%d is negative", fn, N);
+    if ((s = check_mult8(fn, "h", h)) != TP_OK) return s;
+    if (Vpad <= 0 || Vpad % t != 0) return fail(TP_ERR_SHAPE, "%s: Vpad=%d must be a positive multiple of t=%d", fn, Vpad, t);
+    return check_mult8(fn, "Vpad/t", Vpad / t);
+}
+
+size_t xent_ws(int N, int h, int Vt) {
+    GemmPlan p = plan_gemm_bf16(Vt, N, h, false);
+    size_t tiles_m = (size_t)(Vt + p.bm - 1) / p.bm;
+    return al256(tiles_m * (size_t)N * 16);
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_abi_version(void) { return TP_ABI_VERSION; }
+
+const char* tp_last_error(void) { return g_err.c_str(); }
+
+// ------------------------------------------------------------------------------------------------
+tp_status tp_mlp_shard_fwd(int T, int h, int ffn, int t, int r, tp_dtype dt, const void* X, const void* A_r,
+                           const void* b1_r, const void* B_r, void* U_r, void* Y_r, void* Z_r, hipStream_t stream) {
+    const char* fn = "tp_mlp_shard_fwd";
+    tp_status s = check_mlp(fn, T, h, ffn, t, r, dt);
+    if (s != TP_OK) return s;
+    NEED(X); NEED(A_r); NEED(B_r); NEED(U_r); NEED(Y_r); NEED(Z_r); OPT(b1_r);
+    if (T == 0) return ok();
+    const int Ft = ffn / t;
+    GemmReq g1 = req(T, Ft, h, X, h, 0, A_r, Ft, 1, EPI_BIAS_GELU, U_r, Ft);
+    g1.out2 = Y_r;
+    g1.bias = b1_r;
+    HIP_TRY(run_gemm(dt, g1, false, nullptr, stream), "tp_mlp_shard_fwd: column-parallel GEMM");
+    GemmReq g2 = req(T, h, Ft, Y_r, Ft, 0, B_r, h, 1, EPI_STORE, Z_r, h);
+    HIP_TRY(run_gemm(dt, g2, false, nullptr, stream), "tp_mlp_shard_fwd: row-parallel GEMM");
+    return ok();
+}
+
+size_t tp_mlp_shard_bwd_workspace(int T, int h, int ffn, int t, tp_dtype dt) {
+    if (T < 0 || h <= 0 || t < 1 || ffn <= 0 || ffn % t) return 0;
+    return mlp_ws(T, h, ffn / t, dt).total;
+}
+
+tp_status tp_mlp_shard_bwd(int T, int h, int ffn, int t, int r, tp_dtype dt, const void* X, const void* A_r,
+                           const void* B_r, const void* U_r, const void* Y_r, const void* G, void* dX_r, void* dA_r,
+                           void* db1_r, void* dB_r, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "tp_mlp_shard_bwd";
+    tp_status s = check_mlp(fn, T, h, ffn, t, r, dt);
+    if (s != TP_OK) return s;
+    if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_ARG, "%s: accumulate=%d must be 0 or 1", fn, accumulate);
+    NEED(X); NEED(A_r); NEED(B_r); NEED(U_r); NEED(Y_r); NEED(G); NEED(dX_r); NEED(dA_r); NEED(dB_r); OPT(db1_r);
+    const int Ft = ffn / t;
+    MlpWs w = mlp_ws(T, h, Ft, dt);
+    if (ws_bytes < w.total) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, w.total);
+    if (w.total > 0) NEED(ws);
+    char* base = (char*)ws;
+    void* dU = base;
+    void* scratch = base + w.dU;
+    // dU = (G B_r^T) * GeLU'(U_r)
+    GemmReq g = req(T, Ft, h, G, h, 0, B_r, h, 0, EPI_DGELU, dU, Ft);
+    g.aux = U_r;
+    HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_mlp_shard_bwd: dU GEMM");
+    // dB_r = Y_r^T G
+    g = req(Ft, h, T, Y_r, Ft, 1, G, h, 1, EPI_STORE, dB_r, h);
+    g.accumulate = accumulate;
+    HIP_TRY(run_gemm(dt, g, true, scratch, stream), "tp_mlp_shard_bwd: dB GEMM");
+    // dA_r = X^T dU
+    g = req(h, Ft, T, X, h, 1, dU, Ft, 1, EPI_STORE, dA_r, Ft);
+    g.accumulate = accumulate;
+    HIP_TRY(run_gemm(dt, g, true, scratch, stream), "tp_mlp_shard_bwd: dA GEMM");
+    if (db1_r) HIP_TRY(colsum(dt == TP_BF16, T, Ft, dU, db1_r, accumulate, (float*)scratch, stream), "tp_mlp_shard_bwd: db1");
+    // dX_r = dU A_r^T
+    g = req(T, h, Ft, dU, Ft, 0, A_r, Ft, 0, EPI_STORE, dX_r, h);
+    HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_mlp_shard_bwd: dX GEMM");
+    return ok();
+}
+
+// ------------------------------------------------------------------------------------------------
+tp_status tp_attn_shard_fwd(int b, int s, int h, int heads, int t, int r, tp_dtype dt, int causal, const void* Xn,
+                            const void* Wqkv_r, const void* bqkv_r, const void* Wo_r, void* QKV_r, void* O_r,
+                            float* lse_r, void* Z_r, hipStream_t stream) {
+    const char* fn = "tp_attn_shard_fwd";
+    tp_status st = check_attn(fn, b, s, h, heads, t, r, dt, causal);
+    if (st != TP_OK) return st;
+    NEED(Xn); NEED(Wqkv_r); NEED(Wo_r); NEED(QKV_r); NEED(O_r); NEED(lse_r); NEED(Z_r); OPT(bqkv_r);
+    const int T = b * s;
+    if (T == 0) return ok();
+    const int heads_t = heads / t, d = h / heads, h_t = heads_t * d;
+    GemmReq g = req(T, 3 * h_t, h, Xn, h, 0, Wqkv_r, 3 * h_t, 1, EPI_STORE, QKV_r, 3 * h_t);
+    g.bias = bqkv_r;
+    HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_fwd: QKV GEMM");
+    HIP_TRY(attn_fwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, stream), "tp_attn_shard_fwd: attention");
+    g = req(T, h, h_t, O_r, h_t, 0, Wo_r, h, 1, EPI_STORE, Z_r, h);
+    HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_fwd: output projection");
+    return ok();
+}
+
+size_t tp_attn_shard_bwd_workspace(int b, int s, int h, int heads, int t, tp_dtype dt) {
+    (void)dt;
+    if (b < 0 || s < 0 || h <= 0 || heads <= 0 || t < 1 || heads % t || h % heads) return 0;
+    int heads_t = heads / t, h_t = heads_t * (h / heads);
+    return attn_ws(b, s, h, heads_t, h_t).total;
+}
+
+tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dtype dt, int causal, const void* Xn,
+                            const void* Wqkv_r, const void* Wo_r, const void* QKV_r, const void* O_r,
+                            const float* lse_r, const void* G, void* dXn_r, void* dWqkv_r, void* dbqkv_r,
+                            void* dWo_r, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "tp_attn_shard_bwd";
+    tp_status st = check_attn(fn, b, s, h, heads, t, r, dt, causal);
+    if (st != TP_OK) return st;
+    if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_ARG, "%s: accumulate=%d must be 0 or 1", fn, accumulate);
+    NEED(Xn); NEED(Wqkv_r); NEED(Wo_r); NEED(QKV_r); NEED(O_r); NEED(lse_r); NEED(G); NEED(dXn_r); NEED(dWqkv_r);
+    NEED(dWo_r); OPT(dbqkv_r);
+    const int T = b * s;
+    const int heads_t = heads / t, d = h / heads, h_t = heads_t * d;
+    AttnWs w = attn_ws(b, s, h, heads_t, h_t);
+    if (ws_bytes < w.total) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, w.total);
+    if (w.total > 0) NEED(ws);
+    char* base = (char*)ws;
+    void* dO = base;
+    float* Dv = (float*)(base + w.dO);
+    void* dQKV = base + w.dO + w.D;
+    void* scratch = base + w.dO + w.D + w.dQKV;
+    // dO = G Wo_r^T
+    GemmReq g = req(T, h_t, h, G, h, 0, Wo_r, h, 0, EPI_STORE, dO, h_t);
+    HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_bwd: dO GEMM");
+    // dWo_r = O_r^T G
+    g = req(h_t, h, T, O_r, h_t, 1, G, h, 1, EPI_STORE, dWo_r, h);
+    g.accumulate = accumulate;
+    HIP_TRY(run_gemm(dt, g, true, scratch, stream), "tp_attn_shard_bwd: dWo GEMM");
+    if (T > 0)
+        HIP_TRY(attn_bwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, dO, Dv, dQKV, stream),
+                "tp_attn_shard_bwd: attention backward");
+    // dWqkv_r = Xn^T dQKV
+    g = req(h, 3 * h_t, T, Xn, h, 1, dQKV, 3 * h_t, 1, EPI_STORE, dWqkv_r, 3 * h_t);
+    g.accumulate = accumulate;
+    HIP_TRY(run_gemm(dt, g, true, scratch, stream), "tp_attn_shard_bwd: dWqkv GEMM");
+    if (dbqkv_r)
+        HIP_TRY(colsum(1, T, 3 * h_t, dQKV, dbqkv_r, accumulate, (float*)scratch, stream), "tp_attn_shard_bwd: dbqkv");
+    // dXn_r = dQKV Wqkv_r^T
+    g = req(T, h, 3 * h_t, dQKV, 3 * h_t, 0, Wqkv_r, 3 * h_t, 0, EPI_STORE, dXn_r, h);
+    HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_bwd: dXn GEMM");
+    return ok();
+}
+
+// ------------------------------------------------------------------------------------------------
+size_t tp_vocab_xent_shard_fwd_workspace(int N, int h, int Vpad, int t, tp_dtype dt) {
+    (void)dt;
+    if (N < 0 || h <= 0 || t < 1 || Vpad <= 0 || Vpad % t) return 0;
+    return xent_ws(N, h, Vpad / t);
+}
+
+tp_status tp_vocab_xent_shard_fwd(int N, int h, int Vpad, int Vreal, int t, int r, tp_dtype dt, int mask_padding,
+                                  const void* X, const void* E_r, const int32_t* targets, float* max_r,
+                                  float* sumexp_r, float* tgt_r, int32_t* argmax_r, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+    const char* fn = "tp_vocab_xent_shard_fwd";
+    tp_status st = check_vocab(fn, N, h, Vpad, t, r, dt);
+    if (st != TP_OK) return st;
+    if (Vreal <= 0 || Vreal > Vpad) return fail(TP_ERR_SHAPE, "%s: Vreal=%d must be in [1, Vpad=%d]", fn, Vreal, Vpad);
+    if (mask_padding != 0 && mask_padding != 1) return fail(TP_ERR_ARG, "%s: mask_padding=%d must be 0 or 1", fn, mask_padding);
+    NEED(X); NEED(E_r); NEED(targets); NEED(max_r); NEED(sumexp_r); NEED(tgt_r); OPT(argmax_r);
+    const int Vt = Vpad / t;
+    size_t need = xent_ws(N, h, Vt);
+    if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    if (need > 0) NEED(ws);
+    if (N == 0) return ok();
+    GemmPlan p = plan_gemm_bf16(Vt, N, h, false);
+    GemmReq g = req(Vt, N, h, E_r, h, 0, X, h, 0, EPI_XENT, ws, 0);
+    g.targets = targets;
+    g.col0 = r * Vt;
+    g.Vreal = Vreal;
+    g.mask = mask_padding;
+    HIP_TRY(gemm_bf16(g, p, nullptr, stream), "tp_vocab_xent_shard_fwd: fused logits GEMM");
+    HIP_TRY(xent_merge(ws, (Vt + p.bm - 1) / p.bm, N, r * Vt, max_r, sumexp_r, tgt_r, argmax_r, stream),
+            "tp_vocab_xent_shard_fwd: tile merge");
+    return ok();
+}
+
+tp_status tp_vocab_logits_shard(int N, int h, int Vpad, int t, int r, tp_dtype dt, const void* X, const void* E_r,
+                                float* logits, hipStream_t stream) {
+    const char* fn = "tp_vocab_logits_shard";
+    tp_status st = check_vocab(fn, N, h, Vpad, t, r, dt);
+    if (st != TP_OK) return st;
+    NEED(X); NEED(E_r); NEED(logits);
+    if (N == 0) return ok();
+    const int Vt = Vpad / t;
+    GemmPlan p = plan_gemm_bf16(Vt, N, h, false);
+    GemmReq g = req(Vt, N, h, E_r, h, 0, X, h, 0, EPI_STORE_T, logits, Vt);
+    HIP_TRY(gemm_bf16(g, p, nullptr, stream), "tp_vocab_logits_shard: logits GEMM");
+    return ok();
+}
+
+tp_status tp_vocab_xent_combine(int N, int t, const float* const* max_r, const float* const* sumexp_r,
+                                const float* const* tgt_r, float* loss, float* mean_loss, hipStream_t stream) {
+    const char* fn = "tp_vocab_xent_combine";
+    if (t < 1 || t > 64) return fail(TP_ERR_ARG, "%s: t=%d must be in [1, 64]", fn, t);
+    if (N < 0) return fail(TP_ERR_SHAPE, "%s: N=%d is negative", fn, N);
+    if (!max_r || !sumexp_r || !tgt_r) return fail(TP_ERR_ARG, "%s: pointer arrays must not be NULL", fn);
+    for (int i = 0; i < t; ++i)
+        if (!max_r[i] || !sumexp_r[i] || !tgt_r[i]) return fail(TP_ERR_ARG, "%s: rank %d pointer is NULL", fn, i);
+    NEED(loss);
+    if (N == 0) return ok();
+    HIP_TRY(xent_combine(N, t, max_r, sumexp_r, tgt_r, loss, mean_loss, stream), "tp_vocab_xent_combine");
+    return ok();
+}
+
+// ------------------------------------------------------------------------------------------------
+tp_status tp_sum_partials(int rows, int cols, int t, tp_dtype in_dt, const void* const* parts, const void* bias,
+                          const void* residual, void* out, tp_dtype out_dt, hipStream_t stream) {
+    const char* fn = "tp_sum_partials";
+    tp_status s;
+    if ((s = check_dt(fn, in_dt)) != TP_OK || (s = check_dt(fn, out_dt)) != TP_OK) return s;
+    if (t < 1 || t > 64) return fail(TP_ERR_ARG, "%s: t=%d must be in [1, 64]", fn, t);
+    if (rows < 0) return fail(TP_ERR_SHAPE, "%s: rows=%d is negative", fn, rows);
+    if ((s = check_mult8(fn, "cols", cols)) != TP_OK) return s;
+    if (!parts) return fail(TP_ERR_ARG, "%s: parts is NULL", fn);
+    for (int i = 0; i < t; ++i) {
+        if (!parts[i]) return fail(TP_ERR_ARG, "%s: parts[%d] is NULL", fn, i);
+        if (!aligned16(parts[i])) return fail(TP_ERR_ARG, "%s: parts[%d] is not 16-byte aligned", fn, i);
+    }
+    NEED(out); OPT(bias); OPT(residual);
+    HIP_TRY(sum_partials(in_dt == TP_BF16, out_dt == TP_BF16, (size_t)rows, cols, t, parts, bias, residual, out, stream),
+            "tp_sum_partials");
+    return ok();
+}
+
+tp_status tp_layernorm_fwd(int T, int h, tp_dtype dt, float eps, const void* x, const void* gamma, const void* beta,
+                           void* y, float* mean, float* rstd, hipStream_t stream) {
+    const char* fn = "tp_layernorm_fwd";
+    tp_status s;
+    if ((s = check_dt(fn, dt)) != TP_OK) return s;
+    if (T < 0) return fail(TP_ERR_SHAPE, "%s: T=%d is negative", fn, T);
+    if ((s = check_mult8(fn, "h", h)) != TP_OK) return s;
+    if (h > 8192) return fail(TP_ERR_UNSUPPORTED, "%s: h=%d exceeds 8192", fn, h);
+    if (!(eps >= 0.0f)) return fail(TP_ERR_ARG, "%s: eps must be >= 0", fn);
+    NEED(x); NEED(gamma); NEED(beta); NEED(y); OPT(mean); OPT(rstd);
+    HIP_TRY(layernorm_fwd(dt == TP_BF16, T, h, eps, x, gamma, beta, y, mean, rstd, stream), fn);
+    return ok();
+}
+
+size_t tp_layernorm_bwd_workspace(int T, int h, tp_dtype dt) {
+    (void)dt;
+    if (T < 0 || h <= 0) return 0;
+    return al256(2 * (size_t)ln_bwd_blocks(T) * h * sizeof(float));
+}
+
+tp_status tp_layernorm_bwd(int T, int h, tp_dtype dt, const void* x, const void* gamma, const float* mean,
+                           const float* rstd, const void* dy, const void* dres, void* dx, void* dgamma, void* dbeta,
+                           int accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "tp_layernorm_bwd";
+    tp_status s;
+    if ((s = check_dt(fn, dt)) != TP_OK) return s;
+    if (T < 0) return fail(TP_ERR_SHAPE, "%s: T=%d is negative", fn, T);
+    if ((s = check_mult8(fn, "h", h)) != TP_OK) return s;
+    if (h > 8192) return fail(TP_ERR_UNSUPPORTED, "%s: h=%d exceeds 8192", fn, h);
+    if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_ARG, "%s: accumulate=%d must be 0 or 1", fn, accumulate);
+    NEED(x); NEED(gamma); NEED(mean); NEED(rstd); NEED(dy); NEED(dx); OPT(dres); OPT(dgamma); OPT(dbeta);
+    if ((dgamma || dbeta)) {
+        size_t need = tp_layernorm_bwd_workspace(T, h, dt);
+        if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+        if (need > 0) NEED(ws);
+    }
+    HIP_TRY(layernorm_bwd(dt == TP_BF16, T, h, x, gamma, mean, rstd, dy, dres, dx, dgamma, dbeta, accumulate,
+                          (float*)ws, stream), fn);
+    return ok();
+}
+
+size_t tp_colsum_workspace(int T, int n, tp_dtype dt) {
+    (void)dt;
+    if (T < 0 || n <= 0) return 0;
+    return al256(colsum_ws(T, n));
+}
+
+tp_status tp_colsum(int T, int n, tp_dtype dt, const void* G, void* out, int accumulate, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+    const char* fn = "tp_colsum";
+    tp_status s;
+    if ((s = check_dt(fn, dt)) != TP_OK) return s;
+    if (T < 0) return fail(TP_ERR_SHAPE, "%s: T=%d is negative", fn, T);
+    if ((s = check_mult8(fn, "n", n)) != TP_OK) return s;
+    if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_ARG, "%s: accumulate=%d must be 0 or 1", fn, accumulate);
+    NEED(G); NEED(out);
+    size_t need = tp_colsum_workspace(T, n, dt);
+    if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    if (need > 0) NEED(ws);
+    HIP_TRY(colsum(dt == TP_BF16, T, n, G, out, accumulate, (float*)ws, stream), fn);
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Instantiation helper for the bf16 GEMM: plan -> tile configuration -> epilogue -> launch.
+// Included by the per-layout translation units only.
+#pragma once
+#include "gemm.h"
+#include "launch.h"
+#include "xent.h"
+
+namespace tp {
+
+static inline int cdiv_h(long a, long b) { return (int)((a + b - 1) / b); }
+
+template <class C, int LA, int LB, class Epi>
+static hipError_t launch_cfg(const GemmReq& r, int splits, const Epi& e, hipStream_t st) {
+    int tiles = cdiv_h(r.M, C::BM) * cdiv_h(r.N, C::BN);
+    if (tiles == 0) return hipSuccess;
+    int kps = cdiv_h(cdiv_h(r.K, splits), C::BK) * C::BK;
+    hipLaunchKernelGGL((gemm_bf16_kernel<C, LA, LB, Epi>), dim3(tiles, splits), dim3(C::NT), 0, st,
+                       (const bf16*)r.A, r.lda, (const bf16*)r.B, r.ldb, r.M, r.N, r.K, kps, e);
+    return hipGetLastError();
+}
+
+template <int LA, int LB, class Epi>
+static hipError_t launch_plan(const GemmReq& r, const GemmPlan& p, const Epi& e, hipStream_t st) {
+    switch (p.cfg) {
+        case 0: return launch_cfg<Cfg256x256, LA, LB>(r, p.splits, e, st);
+        case 1: return launch_cfg<Cfg256x128, LA, LB>(r, p.splits, e, st);
+        case 2: return launch_cfg<Cfg128x256, LA, LB>(r, p.splits, e, st);
+        case 3: return launch_cfg<Cfg128x128, LA, LB>(r, p.splits, e, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+// kinds: bit mask of the EpiKinds this layout instantiates.
+template <int LA, int LB, int KINDS>
+static hipError_t gemm_run(const GemmReq& r, const GemmPlan& p, void* ws, hipStream_t st) {
+    if (p.splits > 1) {
+        if constexpr ((KINDS & (1 << EPI_STORE)) != 0) {
+            if (r.epi != EPI_STORE || ws == nullptr) return hipErrorInvalidValue;
+            EpiPartial e{(float*)ws, r.N, (size_t)r.M * r.N, 0};
+            hipError_t err = launch_plan<LA, LB>(r, p, e, st);
+            if (err != hipSuccess) return err;
+            EpiStore<bf16> fin{(bf16*)r.out, r.ldc, (const bf16*)r.bias, r.accumulate};
+            size_t n = (size_t)r.M * r.N;
+            hipLaunchKernelGGL((splitk_reduce_kernel<EpiStore<bf16>>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+                               0, st, (const float*)ws, p.splits, n, r.M, r.N, r.N, fin);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
+    switch (r.epi) {
+        case EPI_STORE:
+            if constexpr ((KINDS & (1 << EPI_STORE)) != 0)
+                return launch_plan<LA, LB>(r, p, EpiStore<bf16>{(bf16*)r.out, r.ldc, (const bf16*)r.bias, r.accumulate}, st);
+            break;
+        case EPI_BIAS_GELU:
+            if constexpr ((KINDS & (1 << EPI_BIAS_GELU)) != 0)
+                return launch_plan<LA, LB>(r, p, EpiBiasGelu<bf16>{(bf16*)r.out, (bf16*)r.out2, r.ldc, (const bf16*)r.bias}, st);
+            break;
+        case EPI_DGELU:
+            if constexpr ((KINDS & (1 << EPI_DGELU)) != 0)
+                return launch_plan<LA, LB>(r, p, EpiDGelu<bf16>{(bf16*)r.out, (const bf16*)r.aux, r.ldc}, st);
+            break;
+        case EPI_STORE_T:
+            if constexpr ((KINDS & (1 << EPI_STORE_T)) != 0)
+                return launch_plan<LA, LB>(r, p, EpiStoreT<float>{(float*)r.out, r.ldc}, st);
+            break;
+        case EPI_XENT:
+            if constexpr ((KINDS & (1 << EPI_XENT)) != 0)
+                return launch_plan<LA, LB>(r, p, EpiXent{(XentPartial*)r.out, r.targets, r.col0, r.Vreal, r.mask}, st);
+            break;
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tp

@@ -1,0 +1,47 @@
+// Host-side tile planning for the bf16 MFMA GEMM and layout dispatch.
+#include <hip/hip_runtime.h>
+#include "launch.h"
+
+namespace tp {
+
+static const int kBM[4] = {256, 256, 128, 128};
+static const int kBN[4] = {256, 128, 256, 128};
+// relative MFMA efficiency of a tile shape (operand reuse per LDS byte and per L2 byte)
+static const double kEff[4] = {1.0, 0.9, 0.9, 0.75};
+static const int kCUs = 256;
+
+GemmPlan plan_gemm_bf16(int M, int N, int K, bool allow_split) {
+    const double cu_flops = 2.5e15 / kCUs * 0.8;   // sustained per-CU rate at full efficiency
+    const double round_overhead = 2.0e-6;          // prologue + epilogue per wave of tiles
+    GemmPlan best{3, 1, 128, 128};
+    double best_t = 1e30;
+    static const int splits_opt[] = {1, 2, 3, 4, 6, 8};
+    for (int c = 0; c < 4; ++c) {
+        for (int s : splits_opt) {
+            if (s > 1 && (!allow_split || K / s < 512)) continue;
+            long tiles = (long)((M + kBM[c] - 1) / kBM[c]) * ((N + kBN[c] - 1) / kBN[c]);
+            long units = tiles * s;
+            long rounds = (units + kCUs - 1) / kCUs;
+            long kc = ((K + s - 1) / s + 63) / 64 * 64;
+            double t_tile = 2.0 * kBM[c] * kBN[c] * (double)kc / (cu_flops * kEff[c]);
+            double t = rounds * (t_tile + round_overhead);
+            if (s > 1) t += (s + 1.0) * 4.0 * (double)M * N / 4.0e12 + 3.0e-6;
+            if (t < best_t * 0.999) { best_t = t; best = GemmPlan{c, s, kBM[c], kBN[c]}; }
+        }
+    }
+    return best;
+}
+
+size_t split_ws_bytes(const GemmPlan& p, int M, int N) {
+    return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+}
+
+hipError_t gemm_bf16(const GemmReq& r, const GemmPlan& p, void* ws, hipStream_t st) {
+    if (r.M == 0 || r.N == 0) return hipSuccess;
+    if (!r.a_mn && r.b_mn) return gemm_bf16_nn(r, p, ws, st);
+    if (!r.a_mn && !r.b_mn) return gemm_bf16_nt(r, p, ws, st);
+    if (r.a_mn && r.b_mn) return gemm_bf16_tn(r, p, ws, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tp

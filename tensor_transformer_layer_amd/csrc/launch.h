@@ -1,0 +1,78 @@
+// Host-side interface between the translation units: GEMM requests, tile planning and the
+// kernel launchers. Everything here is plain host C++; no torch types.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tp {
+
+enum EpiKind {
+    EPI_STORE = 0,      // out = acc (+ bias[col]) (+ out if accumulate)
+    EPI_BIAS_GELU = 1,  // out = acc + bias (pre-activation U), out2 = GeLU(U)
+    EPI_DGELU = 2,      // out = acc * GeLU'(aux)
+    EPI_STORE_T = 3,    // fp32 out[col*ldc + row] = acc (transposed store)
+    EPI_XENT = 4,       // cross-entropy tile statistics (xent.h)
+};
+
+// C[M,N] = sum_k A(m,k) B(k,n). a_mn / b_mn: operand is MN-contiguous (element (mn,k) at
+// p[k*ld + mn]) instead of K-contiguous (p[mn*ld + k]).
+struct GemmReq {
+    int M, N, K;
+    const void* A; int lda; int a_mn;
+    const void* B; int ldb; int b_mn;
+    int epi;
+    void* out; void* out2; int ldc;
+    const void* bias; const void* aux; int accumulate;
+    // EPI_XENT
+    const int32_t* targets; int col0, Vreal, mask;
+};
+
+struct GemmPlan {
+    int cfg;      // 0: 256x256, 1: 256x128, 2: 128x256, 3: 128x128
+    int splits;   // K splits (>1 only when the request allows it)
+    int bm, bn;
+};
+
+// Pick a tile configuration and K split count for a bf16 GEMM. allow_split permits split-K
+// with fp32 partials (only plain stores). Pure function of the shape.
+GemmPlan plan_gemm_bf16(int M, int N, int K, bool allow_split);
+size_t split_ws_bytes(const GemmPlan& p, int M, int N);
+
+// Launch one bf16 GEMM (+ split-K reduction if the plan has splits). ws must hold
+// split_ws_bytes(plan) bytes when plan.splits > 1.
+hipError_t gemm_bf16(const GemmReq& r, const GemmPlan& plan, void* ws, hipStream_t st);
+// Launch one fp32 SIMT GEMM.
+hipError_t gemm_f32(const GemmReq& r, hipStream_t st);
+
+// Per-layout instantiations (separate translation units).
+hipError_t gemm_bf16_nn(const GemmReq& r, const GemmPlan& p, void* ws, hipStream_t st);   // A K-contig, B MN-contig
+hipError_t gemm_bf16_nt(const GemmReq& r, const GemmPlan& p, void* ws, hipStream_t st);   // both K-contig
+hipError_t gemm_bf16_tn(const GemmReq& r, const GemmPlan& p, void* ws, hipStream_t st);   // both MN-contig
+
+// Attention (bf16, head width d)
+hipError_t attn_fwd(int b, int s, int h_t, int heads_t, int d, int causal, const void* QKV, void* O, float* lse,
+                    hipStream_t st);
+hipError_t attn_bwd(int b, int s, int h_t, int heads_t, int d, int causal, const void* QKV, const void* O,
+                    const float* lse, const void* dO, float* Dws, void* dQKV, hipStream_t st);
+
+// Cross-entropy merge / combine
+size_t xent_tiles_m(int Vt);
+hipError_t xent_merge(const void* part, int tiles_m, int N, int col0, float* mx, float* se, float* tg,
+                      int32_t* am, hipStream_t st);
+hipError_t xent_combine(int N, int t, const float* const* mx, const float* const* se, const float* const* tg,
+                        float* loss, float* mean, hipStream_t st);
+
+// Norm / elementwise (dt: 0 fp32, 1 bf16)
+int ln_bwd_blocks(int rows);
+hipError_t layernorm_fwd(int dt, int rows, int h, float eps, const void* x, const void* g, const void* b, void* y,
+                         float* mean, float* rstd, hipStream_t st);
+hipError_t layernorm_bwd(int dt, int rows, int h, const void* x, const void* g, const float* mean,
+                         const float* rstd, const void* dy, const void* dres, void* dx, void* dg, void* db,
+                         int accumulate, float* ws, hipStream_t st);
+int colsum_row_blocks(int rows);
+hipError_t colsum(int dt, int rows, int n, const void* G, void* out, int accumulate, float* ws, hipStream_t st);
+hipError_t sum_partials(int in_dt, int out_dt, size_t rows, int cols, int t, const void* const* parts,
+                        const void* bias, const void* residual, void* out, hipStream_t st);
+
+}  // namespace tp

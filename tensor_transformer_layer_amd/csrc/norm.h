@@ -1,0 +1,236 @@
+// Bandwidth-bound kernels of the replicated layer parts: LayerNorm forward/backward, the
+// on-device sum of rank partials (+ bias + residual), and column sums. Every reduction has a
+// fixed order (wave butterflies, then block partials reduced in block order): no atomics.
+#pragma once
+#include "common.h"
+
+namespace tp {
+
+// 8 consecutive elements <-> fp32
+__device__ __forceinline__ void load8(const bf16* p, float (&o)[8]) {
+    bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (float)v[e];
+}
+__device__ __forceinline__ void load8(const float* p, float (&o)[8]) {
+    f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { o[e] = a[e]; o[e + 4] = b[e]; }
+}
+__device__ __forceinline__ void store8(bf16* p, const float (&v)[8]) {
+    *(u32x4*)p = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7])};
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+    *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
+    *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// ---------------------------------------------------------------------------------------------
+// LayerNorm forward: one wave per row, the row held in registers (C chunks of 8 per lane).
+// ---------------------------------------------------------------------------------------------
+template <typename T, int C>
+__global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int h, float eps, const T* __restrict__ x,
+                                                     const T* __restrict__ gamma, const T* __restrict__ beta,
+                                                     T* __restrict__ y, float* __restrict__ mean,
+                                                     float* __restrict__ rstd) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const T* xr = x + (size_t)row * h;
+    float v[C][8];
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+        int c = (lane + 64 * k) * 8;
+        if (c < h) {
+            load8(xr + c, v[k]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += v[k][e];
+        }
+    }
+    const float mu = wave_sum(s) / (float)h;
+    float q = 0.f;
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+        int c = (lane + 64 * k) * 8;
+        if (c < h) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { float d = v[k][e] - mu; q += d * d; }
+        }
+    }
+    const float rs = rsqrtf(wave_sum(q) / (float)h + eps);
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+        int c = (lane + 64 * k) * 8;
+        if (c < h) {
+            float g[8], b[8], o[8];
+            load8(gamma + c, g);
+            load8(beta + c, b);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (v[k][e] - mu) * rs * g[e] + b[e];
+            store8(y + (size_t)row * h + c, o);
+        }
+    }
+    if (lane == 0) {
+        if (mean) mean[row] = mu;
+        if (rstd) rstd[row] = rs;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// LayerNorm backward. Block b handles rows b*4 + w + k*(4*nblocks) (wave w). dx is written per
+// row; dgamma/dbeta partials are accumulated per lane, merged over the block's waves in wave
+// order through LDS, and written as one row per block into part[b][h] (reduced afterwards).
+// ---------------------------------------------------------------------------------------------
+template <typename T, int C>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int h, const T* __restrict__ x,
+                                                     const T* __restrict__ gamma, const float* __restrict__ mean,
+                                                     const float* __restrict__ rstd, const T* __restrict__ dy,
+                                                     const T* __restrict__ dres, T* __restrict__ dx,
+                                                     float* __restrict__ part_g, float* __restrict__ part_b) {
+    extern __shared__ float lds[];   // [2][h]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float pg[C][8], pb[C][8], gm[C][8];
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+        int c = (lane + 64 * k) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { pg[k][e] = 0.f; pb[k][e] = 0.f; gm[k][e] = 0.f; }
+        if (c < h) load8(gamma + c, gm[k]);
+    }
+    const float inv_h = 1.0f / (float)h;
+    for (int row = blockIdx.x * 4 + wave; row < rows; row += 4 * gridDim.x) {
+        const float mu = mean[row], rs = rstd[row];
+        float xh[C][8], g[C][8];
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < C; ++k) {
+            int c = (lane + 64 * k) * 8;
+            if (c < h) {
+                float xv[8], dv[8];
+                load8(x + (size_t)row * h + c, xv);
+                load8(dy + (size_t)row * h + c, dv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    xh[k][e] = (xv[e] - mu) * rs;
+                    g[k][e] = dv[e] * gm[k][e];
+                    s1 += g[k][e];
+                    s2 += g[k][e] * xh[k][e];
+                    pg[k][e] += dv[e] * xh[k][e];
+                    pb[k][e] += dv[e];
+                }
+            }
+        }
+        s1 = wave_sum(s1) * inv_h;
+        s2 = wave_sum(s2) * inv_h;
+#pragma unroll
+        for (int k = 0; k < C; ++k) {
+            int c = (lane + 64 * k) * 8;
+            if (c < h) {
+                float o[8], rr[8];
+                if (dres) load8(dres + (size_t)row * h + c, rr);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    o[e] = rs * (g[k][e] - s1 - xh[k][e] * s2);
+                    if (dres) o[e] += rr[e];
+                }
+                store8(dx + (size_t)row * h + c, o);
+            }
+        }
+    }
+    if (!part_g) return;   // uniform across the block
+    for (int w = 0; w < 4; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int k = 0; k < C; ++k) {
+                int c = (lane + 64 * k) * 8;
+                if (c < h) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if (w == 0) { lds[c + e] = pg[k][e]; lds[h + c + e] = pb[k][e]; }
+                        else { lds[c + e] += pg[k][e]; lds[h + c + e] += pb[k][e]; }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    for (int c = threadIdx.x; c < h; c += 256) {
+        part_g[(size_t)blockIdx.x * h + c] = lds[c];
+        part_b[(size_t)blockIdx.x * h + c] = lds[h + c];
+    }
+}
+
+// out[c] (+)= sum_{b=0}^{nb-1} part[b][c], in block order.
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restrict__ part, int nb, int n,
+                                                          T* __restrict__ out, int accumulate) {
+    int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= n) return;
+    float a = 0.f;
+    for (int b = 0; b < nb; ++b) a += part[(size_t)b * n + c];
+    if (accumulate) a += to_f32(out[c]);
+    out[c] = from_f32<T>(a);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Column sums of G [rows, n]: grid (ceil(n/8/256), RB); thread owns 8 columns and rows
+// y, y + RB, ...; partial row y goes to part[y][n].
+// ---------------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void colsum_partial_kernel(int rows, int n, const T* __restrict__ G,
+                                                             float* __restrict__ part) {
+    int c = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (c >= n) return;
+    float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = blockIdx.y; r < rows; r += gridDim.y) {
+        float v[8];
+        load8(G + (size_t)r * n + c, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] += v[e];
+    }
+    store8(part + (size_t)blockIdx.y * n + c, a);
+}
+
+// ---------------------------------------------------------------------------------------------
+// out = sum_r parts[r] + bias + residual (fp32 sum in rank order), 8 elements per thread.
+// ---------------------------------------------------------------------------------------------
+constexpr int SUM_MAX_T = 64;
+struct PartPtrs { const void* p[SUM_MAX_T]; };
+
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void sum_partials_kernel(size_t n_elems, int cols, int t, PartPtrs parts,
+                                                           const TO* __restrict__ bias,
+                                                           const TO* __restrict__ residual, TO* __restrict__ out) {
+    size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i >= n_elems) return;
+    float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = 0; r < t; ++r) {
+        float v[8];
+        load8((const TI*)parts.p[r] + i, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] += v[e];
+    }
+    if (bias) {
+        float b[8];
+        load8(bias + (i % cols), b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] += b[e];
+    }
+    if (residual) {
+        float rr[8];
+        load8(residual + i, rr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] += rr[e];
+    }
+    store8(out + i, a);
+}
+
+}  // namespace tp

@@ -1,0 +1,104 @@
+// Vocabulary-parallel fused logits GEMM + cross-entropy statistics for gfx950.
+//
+// The GEMM computes the transposed logits C[v][n] = E_r[v] . X[n] (vocab rows on M, tokens on N),
+// so an MFMA accumulator lane holds ONE token and 16 vocabulary rows: the per-token max, argmax,
+// sum of exponentials and target pick-out are in-lane, then one exchange with lane ^ 32, then a
+// merge of the block's wave rows through LDS. Each output tile writes one 16-byte partial per
+// token; logits never reach memory. The merge of a token's tiles (in tile order) and of the ranks
+// into the loss are in xent.hip.
+#pragma once
+#include <climits>
+#include "common.h"
+#include "gemm.h"
+
+namespace tp {
+
+struct XentPartial {
+    float mx;   // max logit over the tile's valid rows (-inf if none)
+    float se;   // sum of exp(logit - mx) over the tile's valid rows
+    float tv;   // target logit if the target row is in the tile, else 0
+    int am;     // local row of mx, lowest on ties (INT_MAX if none)
+};
+
+__device__ __forceinline__ void xent_better(float& mx, int& am, float omx, int oam) {
+    if (omx > mx || (omx == mx && oam < am)) { mx = omx; am = oam; }
+}
+
+// Merge two (max, sumexp) pairs.
+__device__ __forceinline__ void xent_merge_se(float& mx, float& se, float omx, float ose) {
+    if (omx == -INFINITY) return;
+    if (mx == -INFINITY) { mx = omx; se = ose; return; }
+    float m = fmaxf(mx, omx);
+    se = se * expf(mx - m) + ose * expf(omx - m);
+    mx = m;
+}
+
+struct EpiXent {
+    XentPartial* part;        // [tiles_m][N]
+    const int32_t* targets;   // [N] global ids
+    int col0;                 // global id of local row 0 (r * V_t)
+    int Vreal;
+    int mask;                 // 1: rows with col0 + row >= Vreal are -inf
+    __device__ __forceinline__ void set_split(int) {}
+
+    template <class C>
+    __device__ __forceinline__ void apply(f32x16 (&acc)[C::TM][C::TN], int m0, int n0, int mw0, int nw0, int lane,
+                                          int M, int N, char* smem) const {
+        XentPartial* red = (XentPartial*)smem;   // [WGM][BN]; the main loop ended on a barrier
+        const int h = lane >> 5, l32 = lane & 31;
+        const int wm = (mw0 - m0) / C::WM;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const int nloc = (nw0 - n0) + j * 32 + l32;
+            const int n = n0 + nloc;
+            const int trow = (n < N) ? targets[n] - col0 : -1;
+            float mx = -INFINITY, tv = 0.f;
+            int am = INT_MAX;
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    int row = mw0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    bool valid = row < M && (!mask || col0 + row < Vreal);
+                    float x = acc[i][j][v];
+                    if (valid && (x > mx || (x == mx && row < am))) { mx = x; am = row; }
+                    if (row == trow && row < M) tv = x;
+                }
+            xent_better(mx, am, __shfl_xor(mx, 32), __shfl_xor(am, 32));
+            tv += __shfl_xor(tv, 32);
+            float se = 0.f;
+            if (mx != -INFINITY) {
+#pragma unroll
+                for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        int row = mw0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                        bool valid = row < M && (!mask || col0 + row < Vreal);
+                        if (valid) se += expf(acc[i][j][v] - mx);
+                    }
+            }
+            se += __shfl_xor(se, 32);
+            if (h == 0) red[wm * C::BN + nloc] = XentPartial{mx, se, tv, am};
+        }
+        __syncthreads();
+        const int tm = m0 / C::BM;
+        for (int nl = threadIdx.x; nl < C::BN; nl += C::NT) {
+            int n = n0 + nl;
+            if (n >= N) continue;
+            XentPartial p = red[nl];
+#pragma unroll
+            for (int w = 1; w < C::WGM; ++w) {
+                XentPartial q = red[w * C::BN + nl];
+                float mx = p.mx;
+                int am = p.am;
+                xent_better(mx, am, q.mx, q.am);
+                xent_merge_se(p.mx, p.se, q.mx, q.se);
+                p.am = am;
+                p.tv += q.tv;
+            }
+            part[(size_t)tm * N + n] = p;
+        }
+    }
+};
+
+}  // namespace tp

@@ -1,0 +1,94 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments with the documented status before any launch."""
+import os
+import re
+
+import pytest
+
+import tensor_transformer_layer_amd as tp
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tp_shard.h")
+FAKE = 0x10000   # a 16-byte aligned address that is never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(tp.lib, n), n
+        assert n in tp.SIGNATURES, n
+
+
+def test_abi_version_and_error_text():
+    assert tp.tp_abi_version() == 1
+    st = tp.lib.tp_mlp_shard_fwd(8, 64, 256, 0, 0, tp.TP_BF16, *([FAKE] * 7), None)
+    assert st == tp.TP_ERR_ARG
+    assert "t=0" in tp.tp_last_error()
+
+
+def _mlp(**kw):
+    a = dict(T=8, h=64, ffn=256, t=2, r=0, dt=tp.TP_BF16)
+    a.update(kw)
+    ptrs = [FAKE] * 7
+    if "null" in kw:
+        ptrs[kw.pop("null")] = None
+        a.pop("null")
+    return tp.lib.tp_mlp_shard_fwd(a["T"], a["h"], a["ffn"], a["t"], a["r"], a["dt"], *ptrs, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(t=0), tp.TP_ERR_ARG), (dict(r=2), tp.TP_ERR_ARG), (dict(r=-1), tp.TP_ERR_ARG),
+    (dict(T=-1), tp.TP_ERR_SHAPE), (dict(h=60), tp.TP_ERR_SHAPE), (dict(ffn=250), tp.TP_ERR_SHAPE),
+    (dict(ffn=264, t=2), tp.TP_ERR_SHAPE), (dict(dt=7), tp.TP_ERR_DTYPE), (dict(null=0), tp.TP_ERR_ARG),
+])
+def test_mlp_argument_errors(kw, status):
+    assert _mlp(**kw) == status
+
+
+def test_unaligned_pointer_rejected():
+    st = tp.lib.tp_mlp_shard_fwd(8, 64, 256, 2, 0, tp.TP_BF16, FAKE + 2, *([FAKE] * 6), None)
+    assert st == tp.TP_ERR_ARG and "aligned" in tp.tp_last_error()
+
+
+def test_attention_argument_errors():
+    f = tp.lib.tp_attn_shard_fwd
+    p = [FAKE] * 8
+    assert f(2, 64, 384, 4, 2, 0, tp.TP_F32, 1, *p, None) == tp.TP_ERR_UNSUPPORTED   # fp32 attention
+    assert f(2, 64, 384, 4, 3, 0, tp.TP_BF16, 1, *p, None) == tp.TP_ERR_SHAPE        # t does not divide heads
+    assert f(2, 64, 384, 5, 1, 0, tp.TP_BF16, 1, *p, None) == tp.TP_ERR_SHAPE        # heads does not divide h
+    assert f(2, 64, 480, 6, 2, 0, tp.TP_BF16, 1, *p, None) == tp.TP_ERR_UNSUPPORTED  # head width 80
+    assert f(2, 64, 384, 4, 2, 0, tp.TP_BF16, 2, *p, None) == tp.TP_ERR_ARG          # causal flag
+
+
+def test_workspace_too_small():
+    need = tp.tp_mlp_shard_bwd_workspace(512, 256, 1024, 2, tp.TP_BF16)
+    assert need >= 512 * 512 * 2
+    st = tp.lib.tp_mlp_shard_bwd(512, 256, 1024, 2, 0, tp.TP_BF16, *([FAKE] * 10), 0, FAKE, need - 1, None)
+    assert st == tp.TP_ERR_WORKSPACE
+    need_a = tp.tp_attn_shard_bwd_workspace(2, 128, 384, 4, 2, tp.TP_BF16)
+    st = tp.lib.tp_attn_shard_bwd(2, 128, 384, 4, 2, 0, tp.TP_BF16, 1, *([FAKE] * 11), 0, FAKE, need_a - 1, None)
+    assert st == tp.TP_ERR_WORKSPACE
+
+
+def test_vocab_argument_errors():
+    f = tp.lib.tp_vocab_xent_shard_fwd
+    p = [FAKE] * 7
+    assert f(16, 64, 1000, 900, 8, 0, tp.TP_BF16, 0, *p, FAKE, 1 << 30, None) == tp.TP_ERR_SHAPE   # 8 does not divide 1000
+    assert f(16, 64, 1024, 2000, 8, 0, tp.TP_BF16, 0, *p, FAKE, 1 << 30, None) == tp.TP_ERR_SHAPE  # Vreal > Vpad
+    assert f(16, 64, 1024, 1000, 8, 0, tp.TP_BF16, 3, *p, FAKE, 1 << 30, None) == tp.TP_ERR_ARG    # mask flag
+    assert f(16, 64, 1024, 1000, 8, 0, tp.TP_F32, 0, *p, FAKE, 1 << 30, None) == tp.TP_ERR_UNSUPPORTED
+    assert f(16, 64, 1024, 1000, 8, 0, tp.TP_BF16, 0, *p, FAKE, 0, None) == tp.TP_ERR_WORKSPACE
+
+
+def test_sum_partials_argument_errors():
+    arr, _keep = tp._ptr_array([FAKE, None])
+    assert tp.lib.tp_sum_partials(4, 64, 2, tp.TP_BF16, arr, None, None, FAKE, tp.TP_F32, None) == tp.TP_ERR_ARG
+    arr, _keep = tp._ptr_array([FAKE])
+    assert tp.lib.tp_sum_partials(4, 60, 1, tp.TP_BF16, arr, None, None, FAKE, tp.TP_F32, None) == tp.TP_ERR_SHAPE
+    assert tp.lib.tp_sum_partials(4, 64, 0, tp.TP_BF16, arr, None, None, FAKE, tp.TP_F32, None) == tp.TP_ERR_ARG

@@ -1,0 +1,143 @@
+"""GPU parity of the vocabulary-parallel fused logits + cross-entropy statistics, the rank merge,
+LayerNorm forward/backward, the partial sum and the column sums, through the C ABI.
+
+Float tolerances: relative L2 <= 1e-2 for bf16 inputs (fp32 accumulation), <= 1e-5 for fp32.
+Max and argmax are bit-exact against the GPU's own fp32 logits (same kernel, materialised)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tp_synth
+from tests.gpu_util import dev, dev_i32, empty, host, rel_l2, say, ws
+
+pytestmark = pytest.mark.gpu
+tp = pytest.importorskip("tensor_transformer_layer_amd")
+
+
+def run_xent(inp, N, h, Vpad, Vreal, t, ranks, mask):
+    X = dev(inp["X"], "bf16")
+    tg = dev_i32(inp["targets"])
+    Vt = Vpad // t
+    out = {}
+    for r in ranks:
+        E_r = dev(inp["E"][r * Vt:(r + 1) * Vt], "bf16")
+        mx, se, tv = empty((N,), "f32"), empty((N,), "f32"), empty((N,), "f32")
+        am = torch.empty((N,), dtype=torch.int32, device="cuda:0")
+        nb = tp.tp_vocab_xent_shard_fwd_workspace(N, h, Vpad, t, tp.TP_BF16)
+        tp.tp_vocab_xent_shard_fwd(N, h, Vpad, Vreal, t, r, tp.TP_BF16, mask, X, E_r, tg, mx, se, tv, am, ws(nb), nb)
+        logits = empty((N, Vt), "f32")
+        tp.tp_vocab_logits_shard(N, h, Vpad, t, r, tp.TP_BF16, X, E_r, logits)
+        out[r] = dict(max=mx, sumexp=se, tgt=tv, argmax=am, logits=logits)
+    return out
+
+
+def check_bitexact_from_logits(o, r, Vt, Vreal, mask, targets):
+    """max / argmax / target pick-out against the kernel's own fp32 logits, bit for bit."""
+    L = o["logits"].cpu().numpy().astype(np.float32)
+    if mask:
+        cols = r * Vt + np.arange(Vt)
+        L = np.where(cols[None, :] < Vreal, L, -np.inf).astype(np.float32)
+    mx = o["max"].cpu().numpy()
+    am = o["argmax"].cpu().numpy()
+    assert np.array_equal(mx, L.max(axis=1))
+    assert np.array_equal(am, L.argmax(axis=1) + r * Vt)
+    local = targets.astype(np.int64) - r * Vt
+    own = (local >= 0) & (local < Vt)
+    n = np.arange(L.shape[0])
+    want_t = np.where(own, L[n, np.clip(local, 0, Vt - 1)], 0.0).astype(np.float32)
+    assert np.array_equal(o["tgt"].cpu().numpy(), want_t)
+
+
+@pytest.mark.parametrize("mask", [0, 1])
+def test_xent_small_ragged(mask):
+    """N=300 tokens, h=200, Vreal=1000 padded to 1024 for t=4 (V_t=256), all ranks + merge."""
+    N, h, Vreal, t = 300, 200, 1000, 4
+    Vpad = oracle.pad_vocab(Vreal, t, multiple=64)
+    inp = tp_synth.xent_inputs(95, N, h, Vreal, Vpad, "bf16", e_std=0.2)
+    say(f"[xent] small N={N} h={h} Vpad={Vpad} Vreal={Vreal} t={t} mask={mask}")
+    out = run_xent(inp, N, h, Vpad, Vreal, t, range(t), mask)
+    st = [oracle.xent_shard_stats(inp["X"], oracle.vocab_shard(inp["E"], t, r), inp["targets"], t, r, Vreal, bool(mask))
+          for r in range(t)]
+    Vt = Vpad // t
+    for r in range(t):
+        check_bitexact_from_logits(out[r], r, Vt, Vreal, mask, inp["targets"])
+        for k in ("max", "sumexp", "tgt"):
+            e = rel_l2(host(out[r][k]), st[r][k])
+            assert e <= 1e-2, (r, k, e)
+    loss, mean = empty((N,), "f32"), empty((1,), "f32")
+    tp.tp_vocab_xent_combine(N, t, [out[r]["max"] for r in range(t)], [out[r]["sumexp"] for r in range(t)],
+                             [out[r]["tgt"] for r in range(t)], loss, mean)
+    ref = oracle.xent_full(inp["X"], inp["E"], inp["targets"], Vreal, bool(mask))["loss"]
+    e = rel_l2(host(loss), ref)
+    say(f"[xent] small mask={mask}: loss rel-L2 {e:.2e}, mean {host(mean)[0]:.6f} vs {ref.mean():.6f}")
+    assert e <= 1e-2
+    assert abs(host(mean)[0] - ref.mean()) <= 1e-2 * abs(ref.mean())
+
+
+def test_xent_8p3b_workload_sampled():
+    """The 8.3B vocabulary workload: N=8192, h=3072, Vpad=51200 (t=8, V_t=6400), Vreal=50257,
+    all 8 ranks; the oracle takes 64 sampled tokens over the whole padded vocabulary."""
+    w = tp_synth.WORKLOADS["xent_8p3b_t8"]
+    N, h, t = w.T, w.h, w.t
+    inp = tp_synth.xent_inputs(w.seed, N, h, w.vocab, w.vocab_pad, "bf16")
+    say("[xent] 8.3B workload, 8 ranks")
+    out = run_xent(inp, N, h, w.vocab_pad, w.vocab, t, range(t), 0)
+    Vt = w.vocab_pad // t
+    for r in (0, t - 1):
+        check_bitexact_from_logits(out[r], r, Vt, w.vocab, 0, inp["targets"])
+    rows = np.sort(np.random.default_rng([w.seed, 98]).choice(N, 64, replace=False))
+    loss = empty((N,), "f32")
+    tp.tp_vocab_xent_combine(N, t, [out[r]["max"] for r in range(t)], [out[r]["sumexp"] for r in range(t)],
+                             [out[r]["tgt"] for r in range(t)], loss)
+    ref = oracle.xent_full(inp["X"][rows], inp["E"], inp["targets"][rows], w.vocab)
+    e = rel_l2(host(loss)[rows], ref["loss"])
+    st0 = oracle.xent_shard_stats(inp["X"][rows], inp["E"][:Vt], inp["targets"][rows], t, 0, w.vocab)
+    e_se = rel_l2(host(out[0]["sumexp"])[rows], st0["sumexp"])
+    e_mx = rel_l2(host(out[0]["max"])[rows], st0["max"])
+    say(f"[xent] 8.3B: loss rel-L2 {e:.2e}, rank-0 sumexp {e_se:.2e}, max {e_mx:.2e}")
+    assert e <= 1e-2 and e_se <= 1e-2 and e_mx <= 1e-2
+
+
+@pytest.mark.parametrize("dtype,h", [("f32", 136), ("bf16", 3072), ("bf16", 1920), ("f32", 4096)])
+def test_layernorm_fwd_bwd(dtype, h):
+    T = 333
+    g = np.random.default_rng(96)
+    x = tp_synth.round_to_dtype(g.standard_normal((T, h)) * 2 + 0.5, dtype)
+    gam = tp_synth.round_to_dtype(1 + 0.1 * g.standard_normal(h), dtype)
+    bet = tp_synth.round_to_dtype(0.1 * g.standard_normal(h), dtype)
+    dy = tp_synth.round_to_dtype(g.standard_normal((T, h)), dtype)
+    dres = tp_synth.round_to_dtype(g.standard_normal((T, h)), dtype)
+    dt = tp.TP_BF16 if dtype == "bf16" else tp.TP_F32
+    xd, gd, bd = dev(x, dtype), dev(gam, dtype), dev(bet, dtype)
+    y, mean, rstd = empty((T, h), dtype), empty((T,), "f32"), empty((T,), "f32")
+    tp.tp_layernorm_fwd(T, h, dt, 1e-5, xd, gd, bd, y, mean, rstd)
+    dx, dg, db = empty((T, h), dtype), empty((h,), dtype), empty((h,), dtype)
+    nb = tp.tp_layernorm_bwd_workspace(T, h, dt)
+    tp.tp_layernorm_bwd(T, h, dt, xd, gd, mean, rstd, dev(dy, dtype), dev(dres, dtype), dx, dg, db, 0, ws(nb), nb)
+    f = oracle.layernorm_fwd(x, gam, bet)
+    b = oracle.layernorm_bwd(x, gam, f["mean"], f["rstd"], dy)
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    errs = {"y": rel_l2(host(y), f["y"]), "mean": rel_l2(host(mean), f["mean"]), "rstd": rel_l2(host(rstd), f["rstd"]),
+            "dx": rel_l2(host(dx), b["dx"] + dres), "dgamma": rel_l2(host(dg), b["dgamma"]),
+            "dbeta": rel_l2(host(db), b["dbeta"])}
+    say(f"[ln] {dtype} h={h}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
+
+
+def test_sum_partials_and_colsum_exact():
+    """Sum of small integers is exact in fp32: the device sum must equal the integer sum."""
+    g = np.random.default_rng(97)
+    rows, cols, t = 77, 264, 5
+    parts = [g.integers(-8, 8, (rows, cols)).astype(np.float64) for _ in range(t)]
+    bias = g.integers(-4, 4, cols).astype(np.float64)
+    res = g.integers(-4, 4, (rows, cols)).astype(np.float64)
+    out = empty((rows, cols), "f32")
+    tp.tp_sum_partials(rows, cols, t, tp.TP_BF16, [dev(p, "bf16") for p in parts], dev(bias, "f32"), dev(res, "f32"),
+                       out, tp.TP_F32)
+    assert np.array_equal(host(out), sum(parts) + bias + res)
+    cs = empty((cols,), "f32")
+    nb = tp.tp_colsum_workspace(rows, cols, tp.TP_F32)
+    tp.tp_colsum(rows, cols, tp.TP_F32, dev(parts[0], "f32"), cs, 0, ws(nb), nb)
+    assert np.array_equal(host(cs), parts[0].sum(axis=0))
