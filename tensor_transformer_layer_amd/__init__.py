@@ -12,6 +12,10 @@ this package fails if the library has not been built
 import ctypes as C
 import os
 
+# torch first: its HIP runtime must be the one this library binds to (a second copy of the
+# runtime loaded ahead of torch's does not see the device)
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtpshard.so")
 

@@ -48,20 +48,28 @@ __device__ __forceinline__ int lds_off(int row, int kc) {
     return row * 128 + ((kc ^ ((row ^ (row >> 3)) & 7)) << 4);
 }
 
+// Buffer resource over [base, base + bytes): loads at offsets >= bytes return 0, which is how
+// masked chunks (rows past the edge, k past the end of this split) are zero-filled without a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kOOB = 0x7fffffff;
+
 template <int R, int NT, int L> struct TileLoader;
 
 // K-contiguous operand: R rows x 64 k, in 16-byte chunks.
 template <int R, int NT> struct TileLoader<R, NT, KCONTIG> {
     static constexpr int CH = R * 8 / NT;
+    static constexpr int NLOAD = CH, NSTORE = CH;
     static_assert(CH >= 1 && (R * 8) % NT == 0, "tile/threads mismatch");
     u32x4 v[CH];
-    __device__ __forceinline__ void load(const bf16* __restrict__ p, int ld, int mn0, int MN, int k0, int K, int tid) {
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int ld, int mn0, int MN, int k0, int K, int tid) {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             int c = tid + i * NT, row = c >> 3, kc = c & 7;
             int mn = mn0 + row, k = k0 + kc * 8;
-            if (mn < MN && k < K) v[i] = *(const u32x4*)(p + (size_t)mn * ld + k);
-            else v[i] = u32x4{0, 0, 0, 0};
+            int off = (mn < MN && k < K) ? (mn * ld + k) * 2 : kOOB;
+            v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
         }
     }
     __device__ __forceinline__ void store(char* lds, int tid) const {
@@ -79,17 +87,18 @@ template <int R, int NT> struct TileLoader<R, NT, MNCONTIG> {
     static constexpr int EPT = R * 64 / NT;   // elements per thread
     static constexpr int KB = EPT / 8;        // k-rows per thread (8 or 4)
     static constexpr int MC = R / 8;          // 8-wide mn chunks across the tile
+    static constexpr int NLOAD = KB, NSTORE = 8;
     static_assert(KB == 8 || KB == 4, "unsupported tile/threads ratio");
     static_assert(MC * (64 / KB) == NT, "thread mapping must cover the tile exactly");
     u32x4 v[KB];
-    __device__ __forceinline__ void load(const bf16* __restrict__ p, int ld, int mn0, int MN, int k0, int K, int tid) {
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int ld, int mn0, int MN, int k0, int K, int tid) {
         int mc = tid % MC, kg = tid / MC;
         int mn = mn0 + mc * 8;
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
             int k = k0 + kg * KB + j;
-            if (mn < MN && k < K) v[j] = *(const u32x4*)(p + (size_t)k * ld + mn);
-            else v[j] = u32x4{0, 0, 0, 0};
+            int off = (mn < MN && k < K) ? (k * ld + mn) * 2 : kOOB;
+            v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
         }
     }
     __device__ __forceinline__ void store(char* lds, int tid) const {
@@ -224,25 +233,132 @@ struct EpiPartial {
 
 // ----------------------------------------------------------------------------------------------
 // bf16 MFMA kernel. gridDim.x = output tiles; gridDim.y = K splits (each covers k_per_split).
+// LDS: [A stage 0 | A stage 1 | B stage 0 | B stage 1]. Per lane, the fragment addresses of the
+// four 16-deep k-steps are precomputed (the chunk swizzle of row + 32i differs from row's only by
+// XOR 4 on the chunk, i.e. k-step s <-> s ^ 2 for odd i), so every LDS read in the loop is
+// one register + an immediate offset. Fragments of k-step s+1 are read while the MFMAs of
+// k-step s run; the next K tile's global loads are in flight during the whole tile and land in
+// the other stage before its last k-step.
 // ----------------------------------------------------------------------------------------------
+template <class C>
+struct FragAddr {
+    int a[4], b[4];
+    __device__ __forceinline__ void init(int arow, int brow, int khalf) {
+        const int fa = (arow ^ (arow >> 3)) & 7, fb = (brow ^ (brow >> 3)) & 7;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            a[s] = arow * 128 + (((khalf ^ fa) & 1) << 4) + ((s ^ (fa >> 1)) << 5);
+            b[s] = 2 * C::A_BYTES + brow * 128 + (((khalf ^ fb) & 1) << 4) + ((s ^ (fb >> 1)) << 5);
+        }
+    }
+};
+
+template <class C, int ST>
+__device__ __forceinline__ void read_frags(const char* smem, const FragAddr<C>& fa, int s, bf16x8 (&af)[C::TM],
+                                           bf16x8 (&bf)[C::TN]) {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+        af[i] = *(const bf16x8*)(smem + fa.a[s ^ ((i & 1) << 1)] + i * 32 * 128 + ST * C::A_BYTES);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+        bf[j] = *(const bf16x8*)(smem + fa.b[s ^ ((j & 1) << 1)] + j * 32 * 128 + ST * C::B_BYTES);
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[C::TM][C::TN], const bf16x8 (&af)[C::TM],
+                                          const bf16x8 (&bf)[C::TN]) {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+}
+
+template <class C, int LA, int LB>
+struct GemmState {
+    TileLoader<C::BM, C::NT, LA> la;
+    TileLoader<C::BN, C::NT, LB> lb;
+    __amdgpu_buffer_rsrc_t ra, rb;
+    int lda, ldb, m0, n0, M, N, kbeg, kend, tid;
+    FragAddr<C> fa;
+    bf16x8 a0[C::TM], b0[C::TN], a1[C::TM], b1[C::TN];
+};
+
+// Scheduling-group masks (AMDGPU sched_group_barrier): the order inside each k-step is pinned so
+// that the next fragments' LDS reads issue before this k-step's MFMAs and the next tile's LDS
+// writes sit between MFMAs.
+constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
+
+// One K tile held in LDS stage ST (fragments of its k-step 0 already in a0/b0).
+template <class C, int LA, int LB, int ST>
+__device__ __forceinline__ void gemm_tile(GemmState<C, LA, LB>& g, char* smem, f32x16 (&acc)[C::TM][C::TN], int kt,
+                                          int nk) {
+    constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
+    constexpr int NVM = TileLoader<C::BM, C::NT, LA>::NLOAD + TileLoader<C::BN, C::NT, LB>::NLOAD;
+    constexpr int NDW = TileLoader<C::BM, C::NT, LA>::NSTORE + TileLoader<C::BN, C::NT, LB>::NSTORE;
+    const bool more = kt + 1 < nk;
+    if (more) {
+        const int k0 = g.kbeg + (kt + 1) * C::BK;
+        g.la.load(g.ra, g.lda, g.m0, g.M, k0, g.kend, g.tid);
+        g.lb.load(g.rb, g.ldb, g.n0, g.N, k0, g.kend, g.tid);
+    }
+    // k-step 0
+    read_frags<C, ST>(smem, g.fa, 1, g.a1, g.b1);
+    mfma_step<C>(acc, g.a0, g.b0);
+    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, NVM, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // k-step 1
+    read_frags<C, ST>(smem, g.fa, 2, g.a0, g.b0);
+    mfma_step<C>(acc, g.a1, g.b1);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // k-step 2, with the next tile's LDS writes (the other stage was last read in the previous
+    // tile, which ended on a barrier)
+    read_frags<C, ST>(smem, g.fa, 3, g.a1, g.b1);
+    mfma_step<C>(acc, g.a0, g.b0);
+    if (more) {
+        g.la.store(smem + (ST ^ 1) * C::A_BYTES, g.tid);
+        g.lb.store(smem + 2 * C::A_BYTES + (ST ^ 1) * C::B_BYTES, g.tid);
+    }
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM / 2, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, NDW, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM - NM / 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // k-step 3
+    mfma_step<C>(acc, g.a1, g.b1);
+    __syncthreads();
+    if (more) read_frags<C, ST ^ 1>(smem, g.fa, 0, g.a0, g.b0);
+}
+
 template <class C, int LA, int LB, class Epi>
 __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restrict__ A, int lda,
                                                              const bf16* __restrict__ B, int ldb,
-                                                             int M, int N, int K, int k_per_split, Epi epi) {
+                                                             int M, int N, int K, int k_per_split,
+                                                             uint32_t a_bytes, uint32_t b_bytes, Epi epi) {
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WGN, wn = wave % C::WGN;
     const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
     int tm, tn;
     map_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * C::BM, n0 = tn * C::BN;
-    const int kbeg = blockIdx.y * k_per_split;
-    const int kend = min(K, kbeg + k_per_split);
     Epi ep = epi;
     ep.set_split(blockIdx.y);
 
-    TileLoader<C::BM, C::NT, LA> la;
-    TileLoader<C::BN, C::NT, LB> lb;
+    GemmState<C, LA, LB> g;
+    g.ra = make_rsrc(A, a_bytes);
+    g.rb = make_rsrc(B, b_bytes);
+    g.lda = lda; g.ldb = ldb;
+    g.m0 = tm * C::BM; g.n0 = tn * C::BN;
+    g.M = M; g.N = N;
+    g.kbeg = blockIdx.y * k_per_split;
+    g.kend = min(K, g.kbeg + k_per_split);
+    g.tid = tid;
+    g.fa.init(wm * C::WM + (lane & 31), wn * C::WN + (lane & 31), lane >> 5);
+
     f32x16 acc[C::TM][C::TN];
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
@@ -251,47 +367,22 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restr
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    const int nk = (kend - kbeg + C::BK - 1) / C::BK;
+    const int nk = g.kend > g.kbeg ? (g.kend - g.kbeg + C::BK - 1) / C::BK : 0;
     if (nk > 0) {
-        la.load(A, lda, m0, M, kbeg, kend, tid);
-        lb.load(B, ldb, n0, N, kbeg, kend, tid);
-        la.store(smem, tid);
-        lb.store(smem + C::A_BYTES, tid);
+        g.la.load(g.ra, lda, g.m0, M, g.kbeg, g.kend, tid);
+        g.lb.load(g.rb, ldb, g.n0, N, g.kbeg, g.kend, tid);
+        g.la.store(smem, tid);
+        g.lb.store(smem + 2 * C::A_BYTES, tid);
     }
     __syncthreads();
-    const int arow = wm * C::WM + (lane & 31);
-    const int brow = wn * C::WN + (lane & 31);
-    const int khalf = lane >> 5;
-    for (int kt = 0; kt < nk; ++kt) {
-        char* cur = smem + (kt & 1) * C::STAGE;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            int k0 = kbeg + (kt + 1) * C::BK;
-            la.load(A, lda, m0, M, k0, kend, tid);
-            lb.load(B, ldb, n0, N, k0, kend, tid);
-        }
-#pragma unroll
-        for (int s = 0; s < C::BK / 16; ++s) {
-            bf16x8 af[C::TM], bfr[C::TN];
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i) af[i] = *(const bf16x8*)(cur + lds_off(arow + i * 32, 2 * s + khalf));
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j)
-                bfr[j] = *(const bf16x8*)(cur + C::A_BYTES + lds_off(brow + j * 32, 2 * s + khalf));
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-        if (more) {
-            char* nxt = smem + ((kt + 1) & 1) * C::STAGE;
-            la.store(nxt, tid);
-            lb.store(nxt + C::A_BYTES, tid);
-        }
-        __syncthreads();
+    if (nk > 0) read_frags<C, 0>(smem, g.fa, 0, g.a0, g.b0);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        gemm_tile<C, LA, LB, 0>(g, smem, acc, kt, nk);
+        gemm_tile<C, LA, LB, 1>(g, smem, acc, kt + 1, nk);
     }
-    ep.template apply<C>(acc, m0, n0, m0 + wm * C::WM, n0 + wn * C::WN, lane, M, N, smem);
+    if (kt < nk) gemm_tile<C, LA, LB, 0>(g, smem, acc, kt, nk);
+    ep.template apply<C>(acc, g.m0, g.n0, g.m0 + wm * C::WM, g.n0 + wn * C::WN, lane, M, N, smem);
 }
 
 // ----------------------------------------------------------------------------------------------

@@ -14,8 +14,13 @@ static hipError_t launch_cfg(const GemmReq& r, int splits, const Epi& e, hipStre
     int tiles = cdiv_h(r.M, C::BM) * cdiv_h(r.N, C::BN);
     if (tiles == 0) return hipSuccess;
     int kps = cdiv_h(cdiv_h(r.K, splits), C::BK) * C::BK;
+    // bytes addressable through each operand (buffer loads beyond them return 0)
+    size_t a_bytes = (size_t)(LA == KCONTIG ? r.M : r.K) * r.lda * 2;
+    size_t b_bytes = (size_t)(LB == KCONTIG ? r.N : r.K) * r.ldb * 2;
+    if (a_bytes >= 0x7fff0000u || b_bytes >= 0x7fff0000u) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_bf16_kernel<C, LA, LB, Epi>), dim3(tiles, splits), dim3(C::NT), 0, st,
-                       (const bf16*)r.A, r.lda, (const bf16*)r.B, r.ldb, r.M, r.N, r.K, kps, e);
+                       (const bf16*)r.A, r.lda, (const bf16*)r.B, r.ldb, r.M, r.N, r.K, kps, (uint32_t)a_bytes,
+                       (uint32_t)b_bytes, e);
     return hipGetLastError();
 }
 

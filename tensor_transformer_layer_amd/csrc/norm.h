@@ -168,16 +168,26 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int h, const T* _
     }
 }
 
-// out[c] (+)= sum_{b=0}^{nb-1} part[b][c], in block order.
+// out[c] (+)= sum_{b=0}^{nb-1} part[b][c]. Block = 64 columns x 4 row phases: phase p sums rows
+// p, p+4, ... in order, then the four phase sums are added in phase order.
 template <typename T>
 __global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restrict__ part, int nb, int n,
                                                           T* __restrict__ out, int accumulate) {
-    int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= n) return;
+    __shared__ float red[4][64];
+    const int cl = threadIdx.x & 63, ph = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + cl;
     float a = 0.f;
-    for (int b = 0; b < nb; ++b) a += part[(size_t)b * n + c];
-    if (accumulate) a += to_f32(out[c]);
-    out[c] = from_f32<T>(a);
+    if (c < n) {
+#pragma unroll 8
+        for (int b = ph; b < nb; b += 4) a += part[(size_t)b * n + c];
+    }
+    red[ph][cl] = a;
+    __syncthreads();
+    if (ph == 0 && c < n) {
+        a = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
+        if (accumulate) a += to_f32(out[c]);
+        out[c] = from_f32<T>(a);
+    }
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -71,7 +71,7 @@ static hipError_t ln_bwd_t(int rows, int h, const void* x, const void* g, const 
 #undef LNB
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !params) return e;
-    dim3 rg((h + 255) / 256);
+    dim3 rg((h + 63) / 64);
     if (dg) hipLaunchKernelGGL((reduce_rows_kernel<T>), rg, dim3(256), 0, st, (const float*)pg, nb, h, (T*)dg, accumulate);
     if (db) hipLaunchKernelGGL((reduce_rows_kernel<T>), rg, dim3(256), 0, st, (const float*)pb, nb, h, (T*)db, accumulate);
     return hipGetLastError();
@@ -82,7 +82,7 @@ hipError_t layernorm_bwd(int dt, int rows, int h, const void* x, const void* g, 
                          int accumulate, float* ws, hipStream_t st) {
     if (rows == 0) {
         // no rows: parameter gradients are zero (unchanged when accumulating); a zero-block reduction writes them
-        dim3 rg((h + 255) / 256);
+        dim3 rg((h + 63) / 64);
         if (dt == 1) {
             if (dg) hipLaunchKernelGGL((reduce_rows_kernel<bf16>), rg, dim3(256), 0, st, (const float*)ws, 0, h, (bf16*)dg, accumulate);
             if (db) hipLaunchKernelGGL((reduce_rows_kernel<bf16>), rg, dim3(256), 0, st, (const float*)ws, 0, h, (bf16*)db, accumulate);
@@ -96,7 +96,7 @@ hipError_t layernorm_bwd(int dt, int rows, int h, const void* x, const void* g, 
                    : ln_bwd_t<float>(rows, h, x, g, mean, rstd, dy, dres, dx, dg, db, accumulate, ws, st);
 }
 
-int colsum_row_blocks(int rows) { return rows < 256 ? (rows > 0 ? rows : 1) : 256; }
+int colsum_row_blocks(int rows) { return rows < 64 ? (rows > 0 ? rows : 1) : 64; }
 
 hipError_t colsum(int dt, int rows, int n, const void* G, void* out, int accumulate, float* ws, hipStream_t st) {
     int rb = colsum_row_blocks(rows);
@@ -108,7 +108,7 @@ hipError_t colsum(int dt, int rows, int n, const void* G, void* out, int accumul
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     int nb = rows > 0 ? rb : 0;
-    dim3 rg((n + 255) / 256);
+    dim3 rg((n + 63) / 64);
     if (dt == 1) hipLaunchKernelGGL((reduce_rows_kernel<bf16>), rg, dim3(256), 0, st, (const float*)ws, nb, n, (bf16*)out, accumulate);
     else hipLaunchKernelGGL((reduce_rows_kernel<float>), rg, dim3(256), 0, st, (const float*)ws, nb, n, (float*)out, accumulate);
     return hipGetLastError();
