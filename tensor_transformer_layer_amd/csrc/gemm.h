@@ -38,9 +38,10 @@ struct GemmCfg {
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
 };
 
-typedef GemmCfg<256, 256, 2, 2> Cfg256x256;
-typedef GemmCfg<256, 128, 2, 2> Cfg256x128;
-typedef GemmCfg<128, 256, 2, 2> Cfg128x256;
+// 256x256 with 8 waves (2 x 4, 128x64 per wave, two waves per SIMD) and 128x128 with 4 waves
+// (64x64 per wave, two workgroups per CU): both keep two waves per SIMD to hide latency; the
+// larger tile halves LDS and L2 traffic per MFMA.
+typedef GemmCfg<256, 256, 2, 4> Cfg256x256;
 typedef GemmCfg<128, 128, 2, 2> Cfg128x128;
 
 // Byte offset of 16-byte chunk kc (0..7) of tile row `row` (rows are 64 bf16 = 128 bytes).

@@ -4,26 +4,30 @@
 
 namespace tp {
 
-static const int kBM[4] = {256, 256, 128, 128};
-static const int kBN[4] = {256, 128, 256, 128};
-// relative MFMA efficiency of a tile shape (operand reuse per LDS byte and per L2 byte)
-static const double kEff[4] = {1.0, 0.9, 0.9, 0.75};
+static const int kNCfg = 2;
+static const int kBM[kNCfg] = {256, 128};
+static const int kBN[kNCfg] = {256, 128};
+// relative per-tile MFMA efficiency, measured on MI355X at the layer's shapes (K = 1536..3072)
+static const double kEff[kNCfg] = {1.0, 0.93};
+// workgroups of each configuration resident per CU
+static const int kPerCU[kNCfg] = {1, 2};
 static const int kCUs = 256;
 
 GemmPlan plan_gemm_bf16(int M, int N, int K, bool allow_split) {
     const double cu_flops = 2.5e15 / kCUs * 0.8;   // sustained per-CU rate at full efficiency
     const double round_overhead = 2.0e-6;          // prologue + epilogue per wave of tiles
-    GemmPlan best{3, 1, 128, 128};
+    GemmPlan best{1, 1, 128, 128};
     double best_t = 1e30;
     static const int splits_opt[] = {1, 2, 3, 4, 6, 8};
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < kNCfg; ++c) {
         for (int s : splits_opt) {
             if (s > 1 && (!allow_split || K / s < 512)) continue;
             long tiles = (long)((M + kBM[c] - 1) / kBM[c]) * ((N + kBN[c] - 1) / kBN[c]);
             long units = tiles * s;
-            long rounds = (units + kCUs - 1) / kCUs;
+            long slots = (long)kCUs * kPerCU[c];
+            long rounds = (units + slots - 1) / slots;
             long kc = ((K + s - 1) / s + 63) / 64 * 64;
-            double t_tile = 2.0 * kBM[c] * kBN[c] * (double)kc / (cu_flops * kEff[c]);
+            double t_tile = 2.0 * kBM[c] * kBN[c] * (double)kc * kPerCU[c] / (cu_flops * kEff[c]);
             double t = rounds * (t_tile + round_overhead);
             if (s > 1) t += (s + 1.0) * 4.0 * (double)M * N / 4.0e12 + 3.0e-6;
             if (t < best_t * 0.999) { best_t = t; best = GemmPlan{c, s, kBM[c], kBN[c]}; }

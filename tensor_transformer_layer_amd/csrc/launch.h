@@ -29,7 +29,7 @@ struct GemmReq {
 };
 
 struct GemmPlan {
-    int cfg;      // 0: 256x256, 1: 256x128, 2: 128x256, 3: 128x128
+    int cfg;      // 0: 256x256 (8 waves), 1: 128x128 (4 waves)
     int splits;   // K splits (>1 only when the request allows it)
     int bm, bn;
 };

@@ -88,7 +88,23 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int h, float eps,
 // LayerNorm backward. Block b handles rows b*4 + w + k*(4*nblocks) (wave w). dx is written per
 // row; dgamma/dbeta partials are accumulated per lane, merged over the block's waves in wave
 // order through LDS, and written as one row per block into part[b][h] (reduced afterwards).
+// The row's x and dy stay in registers in their storage type (packed bf16) between the two passes.
 // ---------------------------------------------------------------------------------------------
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+    u32x4 v;
+    __device__ __forceinline__ void load(const bf16* p) { v = *(const u32x4*)p; }
+    __device__ __forceinline__ float operator[](int e) const {
+        uint32_t w = v[e >> 1];
+        return __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+template <> struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) { a = *(const f32x4*)p; b = *(const f32x4*)(p + 4); }
+    __device__ __forceinline__ float operator[](int e) const { return e < 4 ? a[e] : b[e - 4]; }
+};
+
 template <typename T, int C>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int h, const T* __restrict__ x,
                                                      const T* __restrict__ gamma, const float* __restrict__ mean,
@@ -97,34 +113,32 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int h, const T* _
                                                      float* __restrict__ part_g, float* __restrict__ part_b) {
     extern __shared__ float lds[];   // [2][h]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float pg[C][8], pb[C][8], gm[C][8];
+    float pg[C][8], pb[C][8];
 #pragma unroll
-    for (int k = 0; k < C; ++k) {
-        int c = (lane + 64 * k) * 8;
+    for (int k = 0; k < C; ++k)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { pg[k][e] = 0.f; pb[k][e] = 0.f; gm[k][e] = 0.f; }
-        if (c < h) load8(gamma + c, gm[k]);
-    }
+        for (int e = 0; e < 8; ++e) { pg[k][e] = 0.f; pb[k][e] = 0.f; }
     const float inv_h = 1.0f / (float)h;
     for (int row = blockIdx.x * 4 + wave; row < rows; row += 4 * gridDim.x) {
         const float mu = mean[row], rs = rstd[row];
-        float xh[C][8], g[C][8];
+        Raw8<T> xr[C], dr[C];
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
         for (int k = 0; k < C; ++k) {
             int c = (lane + 64 * k) * 8;
             if (c < h) {
-                float xv[8], dv[8];
-                load8(x + (size_t)row * h + c, xv);
-                load8(dy + (size_t)row * h + c, dv);
+                xr[k].load(x + (size_t)row * h + c);
+                dr[k].load(dy + (size_t)row * h + c);
+                float gm[8];
+                load8(gamma + c, gm);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    xh[k][e] = (xv[e] - mu) * rs;
-                    g[k][e] = dv[e] * gm[k][e];
-                    s1 += g[k][e];
-                    s2 += g[k][e] * xh[k][e];
-                    pg[k][e] += dv[e] * xh[k][e];
-                    pb[k][e] += dv[e];
+                    float xh = (xr[k][e] - mu) * rs, d = dr[k][e];
+                    float g = d * gm[e];
+                    s1 += g;
+                    s2 += g * xh;
+                    pg[k][e] += d * xh;
+                    pb[k][e] += d;
                 }
             }
         }
@@ -134,11 +148,13 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int h, const T* _
         for (int k = 0; k < C; ++k) {
             int c = (lane + 64 * k) * 8;
             if (c < h) {
-                float o[8], rr[8];
+                float o[8], rr[8], gm[8];
+                load8(gamma + c, gm);
                 if (dres) load8(dres + (size_t)row * h + c, rr);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    o[e] = rs * (g[k][e] - s1 - xh[k][e] * s2);
+                    float xh = (xr[k][e] - mu) * rs;
+                    o[e] = rs * (dr[k][e] * gm[e] - s1 - xh * s2);
                     if (dres) o[e] += rr[e];
                 }
                 store8(dx + (size_t)row * h + c, o);
@@ -191,15 +207,16 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restric
 }
 
 // ---------------------------------------------------------------------------------------------
-// Column sums of G [rows, n]: grid (ceil(n/8/256), RB); thread owns 8 columns and rows
-// y, y + RB, ...; partial row y goes to part[y][n].
+// Column sums of G [rows, n]: grid (ceil(n/8/64), RB), 64 threads; a thread owns 8 columns and
+// rows y, y + RB, ...; partial row y goes to part[y][n].
 // ---------------------------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void colsum_partial_kernel(int rows, int n, const T* __restrict__ G,
-                                                             float* __restrict__ part) {
-    int c = (blockIdx.x * 256 + threadIdx.x) * 8;
+__global__ __launch_bounds__(64) void colsum_partial_kernel(int rows, int n, const T* __restrict__ G,
+                                                            float* __restrict__ part) {
+    int c = (blockIdx.x * 64 + threadIdx.x) * 8;
     if (c >= n) return;
     float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 4
     for (int r = blockIdx.y; r < rows; r += gridDim.y) {
         float v[8];
         load8(G + (size_t)r * n + c, v);

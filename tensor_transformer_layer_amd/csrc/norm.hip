@@ -42,8 +42,8 @@ hipError_t layernorm_fwd(int dt, int rows, int h, float eps, const void* x, cons
 }
 
 int ln_bwd_blocks(int rows) {
-    int nb = (rows + 3) / 4;
-    return nb < 256 ? nb : 256;
+    int nb = (rows + 7) / 8;
+    return nb < 512 ? nb : 512;
 }
 
 template <typename T>
@@ -96,14 +96,14 @@ hipError_t layernorm_bwd(int dt, int rows, int h, const void* x, const void* g, 
                    : ln_bwd_t<float>(rows, h, x, g, mean, rstd, dy, dres, dx, dg, db, accumulate, ws, st);
 }
 
-int colsum_row_blocks(int rows) { return rows < 64 ? (rows > 0 ? rows : 1) : 64; }
+int colsum_row_blocks(int rows) { return rows < 128 ? (rows > 0 ? rows : 1) : 128; }
 
 hipError_t colsum(int dt, int rows, int n, const void* G, void* out, int accumulate, float* ws, hipStream_t st) {
     int rb = colsum_row_blocks(rows);
     if (rows > 0) {
-        dim3 grid((n / 8 + 255) / 256, rb);
-        if (dt == 1) hipLaunchKernelGGL((colsum_partial_kernel<bf16>), grid, dim3(256), 0, st, rows, n, (const bf16*)G, ws);
-        else hipLaunchKernelGGL((colsum_partial_kernel<float>), grid, dim3(256), 0, st, rows, n, (const float*)G, ws);
+        dim3 grid((n / 8 + 63) / 64, rb);
+        if (dt == 1) hipLaunchKernelGGL((colsum_partial_kernel<bf16>), grid, dim3(64), 0, st, rows, n, (const bf16*)G, ws);
+        else hipLaunchKernelGGL((colsum_partial_kernel<float>), grid, dim3(64), 0, st, rows, n, (const float*)G, ws);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
