@@ -16,8 +16,10 @@ multiply-add, backward = 2x forward, causal attention over the visible pairs onl
 Prints ONE JSON line.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,6 +32,31 @@ B, S, H, HEADS, FFN, TP = 8, 1024, 3072, 32, 12288, 8
 VOCAB, VOCAB_PAD = 50257, 51200
 PEAK_BF16 = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12         # bytes/s
+COPY_PROBE_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "vocab_xent_gemm_8p3b.md")
+KERNEL_SOURCES = ["common.h", "gemm.h", "gemm_dispatch.h", "xent.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tensor_transformer_layer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused vocabulary GEMM, from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
 
 
 def layer_flops(b, s, h, heads, ffn, t):
@@ -96,6 +123,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="copy 512 MiB device-to-device once before the steps (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
@@ -150,6 +179,13 @@ def main():
 
     stream = torch.cuda.current_stream()
     xev = []
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(record):
         rank0.step(x, G, attn_sum, mlp_sum, dxn2_sum, dxn1_sum)
@@ -203,7 +239,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "fused vocab logits GEMM + CE statistics (gemm_bf16_kernel "
                      "with EpiXent, plus its per-token tile merge)",
                      "achieved": round(xent_achieved, 2), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                     "frac": round(xent_achieved * 1e12 / PEAK_BF16, 4), "traffic": None},
+                     "frac": round(xent_achieved * 1e12 / PEAK_BF16, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, xe)

@@ -20,8 +20,10 @@
  *  - Feature sizes (h, ffn/t, 3h/t, h/t, V/t) must be multiples of 8. Token counts are free.
  *  - Errors: arguments are checked on the host before any launch. On failure the call returns
  *    a non-zero tp_status, launches nothing, writes nothing and sets tp_last_error(). A launch
- *    failure reported by the HIP runtime returns TP_ERR_HIP. Calls with zero tokens return
- *    TP_OK and launch nothing. Nothing aborts or throws across this boundary.
+ *    failure reported by the HIP runtime returns TP_ERR_HIP. Forward calls with zero tokens
+ *    return TP_OK and launch nothing; backward calls with zero tokens still write their weight
+ *    and bias gradients (zeros, or unchanged when accumulating). Nothing aborts or throws
+ *    across this boundary. Each GEMM operand must be smaller than 2 GiB (TP_ERR_HIP otherwise).
  *  - Determinism: fixed reduction orders, no floating-point atomics; repeated calls on the
  *    same inputs give identical bits.
  *  - Workspace: calls that need scratch memory take (ws, ws_bytes); the matching *_workspace

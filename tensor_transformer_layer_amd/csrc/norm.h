@@ -216,7 +216,7 @@ __global__ __launch_bounds__(64) void colsum_partial_kernel(int rows, int n, con
     int c = (blockIdx.x * 64 + threadIdx.x) * 8;
     if (c >= n) return;
     float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 4
+#pragma unroll 16
     for (int r = blockIdx.y; r < rows; r += gridDim.y) {
         float v[8];
         load8(G + (size_t)r * n + c, v);

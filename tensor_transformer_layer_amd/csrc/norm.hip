@@ -96,7 +96,7 @@ hipError_t layernorm_bwd(int dt, int rows, int h, const void* x, const void* g, 
                    : ln_bwd_t<float>(rows, h, x, g, mean, rstd, dy, dres, dx, dg, db, accumulate, ws, st);
 }
 
-int colsum_row_blocks(int rows) { return rows < 128 ? (rows > 0 ? rows : 1) : 128; }
+int colsum_row_blocks(int rows) { return rows < 512 ? (rows > 0 ? rows : 1) : 512; }
 
 hipError_t colsum(int dt, int rows, int n, const void* G, void* out, int accumulate, float* ws, hipStream_t st) {
     int rb = colsum_row_blocks(rows);
