@@ -2,14 +2,20 @@
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16 on LDS-staged, double-buffered 64-deep K tiles.
 //   * Each operand is either K-contiguous (element (mn,k) at p[mn*ld + k]) or MN-contiguous
-//     (element (mn,k) at p[k*ld + mn]). Both are stored in LDS K-contiguous, in 16-byte chunks
-//     of 8 k-values, so every MFMA fragment is one 128-bit LDS read per lane. MN-contiguous tiles
-//     are transposed in registers (8x8 or 4x8 blocks of bf16) between the global load and the
-//     LDS store; nothing is transposed in HBM.
-//   * LDS chunk index is XOR-swizzled with the row so that the 8 rows a wave reads (MFMA A/B
-//     fragments) and the 8 rows a transposing thread group writes land in distinct banks.
-//   * Global loads of tile k+1 are issued before the MFMAs of tile k and written to the other
-//     LDS buffer after them: one barrier per K tile.
+//     (element (mn,k) at p[k*ld + mn]). Both are held in LDS as [R rows][64 k], 128-byte rows,
+//     16-byte chunk kc stored at kc ^ ((row ^ row/8) & 7), so every MFMA fragment is one
+//     conflict-free 128-bit LDS read per lane:
+//       - K-contiguous tiles go from global memory straight into LDS (buffer_load ... lds, no
+//         staging registers);
+//       - MN-contiguous tiles are fetched into registers (8 k-rows x 8 mn per thread),
+//         transposed there with byte permutes and written to LDS. (Keeping them MN-major in LDS
+//         and reading with the transposing ds_read_b64_tr_b16 was measured slower.)
+//     Nothing is transposed in HBM.
+//   * Out-of-range chunks (rows past the edge, k past the end of this split) are fetched at an
+//     offset past the buffer's end, which the buffer load returns as 0.
+//   * The next K tile is fetched into the other LDS stage at the start of a tile; fragments of
+//     k-step s+1 are read while the MFMAs of k-step s run (order pinned with
+//     sched_group_barrier); one barrier per K tile.
 //   * Tiles are mapped XCD-aware: consecutive workgroups go round-robin to the 8 XCDs, so the
 //     block id is remapped to give each XCD a contiguous, grouped range of output tiles that
 //     share A and B panels in that XCD's L2.
@@ -44,55 +50,74 @@ struct GemmCfg {
 typedef GemmCfg<256, 256, 2, 4> Cfg256x256;
 typedef GemmCfg<128, 128, 2, 2> Cfg128x128;
 
-// Byte offset of 16-byte chunk kc (0..7) of tile row `row` (rows are 64 bf16 = 128 bytes).
-__device__ __forceinline__ int lds_off(int row, int kc) {
-    return row * 128 + ((kc ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
-
 // Buffer resource over [base, base + bytes): loads at offsets >= bytes return 0, which is how
-// masked chunks (rows past the edge, k past the end of this split) are zero-filled without a branch.
+// masked chunks are zero-filled without a branch.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 constexpr int kOOB = 0x7fffffff;
 
-template <int R, int NT, int L> struct TileLoader;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// K-contiguous operand: R rows x 64 k, in 16-byte chunks.
-template <int R, int NT> struct TileLoader<R, NT, KCONTIG> {
-    static constexpr int CH = R * 8 / NT;
-    static constexpr int NLOAD = CH, NSTORE = CH;
-    static_assert(CH >= 1 && (R * 8) % NT == 0, "tile/threads mismatch");
-    u32x4 v[CH];
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int ld, int mn0, int MN, int k0, int K, int tid) {
+// Byte offset of 16-byte chunk kc (0..7) of row `row` in a K-contiguous tile (128-byte rows).
+__device__ __forceinline__ int lds_off(int row, int kc) {
+    return row * 128 + ((kc ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, int off, char* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+
+// One operand tile of R rows (M or N) x 64 k. load(): global -> LDS by 1 KB DMA instructions,
+// lane L of an instruction landing at byte 16*L of its kilobyte. init()/frag(): per-lane
+// fragment addresses (4 registers) and the MFMA operand of 32-row group i at 16-deep k-step s.
+template <int R, int NT, int L> struct Operand;
+
+template <int R, int NT> struct Operand<R, NT, KCONTIG> {
+    static constexpr bool DMA = true;
+    static constexpr int BYTES = R * 128;
+    static constexpr int IPW = BYTES / 1024 / (NT / 64);
+    static_assert(IPW >= 1 && BYTES % (1024 * (NT / 64)) == 0, "tile/threads mismatch");
+    int a[4];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int ld, int mn0, int MN, int k0, int K, int tid,
+                                         char* lds) const {
+        const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            int c = tid + i * NT, row = c >> 3, kc = c & 7;
-            int mn = mn0 + row, k = k0 + kc * 8;
-            int off = (mn < MN && k < K) ? (mn * ld + k) * 2 : kOOB;
-            v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        for (int j = 0; j < IPW; ++j) {
+            const int blk = wave * IPW + j;
+            const int c = blk * 64 + lane, row = c >> 3, p = c & 7;
+            const int kc = p ^ ((row ^ (row >> 3)) & 7);
+            const int mn = mn0 + row, k = k0 + kc * 8;
+            dma16(rs, (mn < MN && k < K) ? (mn * ld + k) * 2 : kOOB, lds + blk * 1024);
         }
     }
-    __device__ __forceinline__ void store(char* lds, int tid) const {
+    // row = first row of the wave's 32-row groups + lane % 32; the swizzle of row + 32i differs
+    // from row's by XOR 4 on the chunk, i.e. k-step s <-> s ^ 2 for odd i.
+    __device__ __forceinline__ void init(int row, int lane) {
+        const int f = (row ^ (row >> 3)) & 7, khalf = lane >> 5;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            int c = tid + i * NT, row = c >> 3, kc = c & 7;
-            *(u32x4*)(lds + lds_off(row, kc)) = v[i];
-        }
+        for (int s = 0; s < 4; ++s) a[s] = row * 128 + (((khalf ^ f) & 1) << 4) + ((s ^ (f >> 1)) << 5);
+    }
+    __device__ __forceinline__ bf16x8 frag(const char* lds, int i, int s) const {
+        return *(const bf16x8*)(lds + a[s ^ ((i & 1) << 1)] + i * 32 * 128);
     }
 };
 
-// MN-contiguous operand: each thread loads KB k-rows x 8 mn (16 bytes per row) and writes them
-// transposed as 8 rows of KB k-values.
-template <int R, int NT> struct TileLoader<R, NT, MNCONTIG> {
+template <int R, int NT> struct Operand<R, NT, MNCONTIG> {
+    // Register-staged: each thread fetches KB k-rows x 8 mn (16 bytes per row) and stores them
+    // transposed into the K-contiguous, swizzled tile layout of Operand<KCONTIG> (8 or 4 k-values
+    // per 16-byte or 8-byte LDS write), whose fragment reads are then used unchanged.
+    static constexpr bool DMA = false;
+    static constexpr int BYTES = R * 128;
     static constexpr int EPT = R * 64 / NT;   // elements per thread
     static constexpr int KB = EPT / 8;        // k-rows per thread (8 or 4)
     static constexpr int MC = R / 8;          // 8-wide mn chunks across the tile
     static constexpr int NLOAD = KB, NSTORE = 8;
     static_assert(KB == 8 || KB == 4, "unsupported tile/threads ratio");
     static_assert(MC * (64 / KB) == NT, "thread mapping must cover the tile exactly");
+    Operand<R, NT, KCONTIG> kc;   // fragment addressing of the K-contiguous layout
     u32x4 v[KB];
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int ld, int mn0, int MN, int k0, int K, int tid) {
+    __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, int ld, int mn0, int MN, int k0, int K, int tid) {
         int mc = tid % MC, kg = tid / MC;
         int mn = mn0 + mc * 8;
 #pragma unroll
@@ -121,6 +146,8 @@ template <int R, int NT> struct TileLoader<R, NT, MNCONTIG> {
             }
         }
     }
+    __device__ __forceinline__ void init(int row, int lane) { kc.init(row, lane); }
+    __device__ __forceinline__ bf16x8 frag(const char* lds, int i, int s) const { return kc.frag(lds, i, s); }
 };
 
 // Block id -> output tile. XCD-aware: block i runs on XCD i % 8; give each XCD a contiguous
@@ -234,35 +261,26 @@ struct EpiPartial {
 
 // ----------------------------------------------------------------------------------------------
 // bf16 MFMA kernel. gridDim.x = output tiles; gridDim.y = K splits (each covers k_per_split).
-// LDS: [A stage 0 | A stage 1 | B stage 0 | B stage 1]. Per lane, the fragment addresses of the
-// four 16-deep k-steps are precomputed (the chunk swizzle of row + 32i differs from row's only by
-// XOR 4 on the chunk, i.e. k-step s <-> s ^ 2 for odd i), so every LDS read in the loop is
-// one register + an immediate offset. Fragments of k-step s+1 are read while the MFMAs of
-// k-step s run; the next K tile's global loads are in flight during the whole tile and land in
-// the other stage before its last k-step.
+// LDS: [A stage 0 | A stage 1 | B stage 0 | B stage 1].
 // ----------------------------------------------------------------------------------------------
-template <class C>
-struct FragAddr {
-    int a[4], b[4];
-    __device__ __forceinline__ void init(int arow, int brow, int khalf) {
-        const int fa = (arow ^ (arow >> 3)) & 7, fb = (brow ^ (brow >> 3)) & 7;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            a[s] = arow * 128 + (((khalf ^ fa) & 1) << 4) + ((s ^ (fa >> 1)) << 5);
-            b[s] = 2 * C::A_BYTES + brow * 128 + (((khalf ^ fb) & 1) << 4) + ((s ^ (fb >> 1)) << 5);
-        }
-    }
+template <class C, int LA, int LB>
+struct GemmState {
+    Operand<C::BM, C::NT, LA> oa;
+    Operand<C::BN, C::NT, LB> ob;
+    __amdgpu_buffer_rsrc_t ra, rb;
+    int lda, ldb, m0, n0, M, N, kbeg, kend, tid;
+    bf16x8 a0[C::TM], b0[C::TN], a1[C::TM], b1[C::TN];
 };
 
-template <class C, int ST>
-__device__ __forceinline__ void read_frags(const char* smem, const FragAddr<C>& fa, int s, bf16x8 (&af)[C::TM],
+template <class C, int LA, int LB, int ST>
+__device__ __forceinline__ void read_frags(const GemmState<C, LA, LB>& g, const char* smem, int s, bf16x8 (&af)[C::TM],
                                            bf16x8 (&bf)[C::TN]) {
+    const char* As = smem + ST * C::A_BYTES;
+    const char* Bs = smem + 2 * C::A_BYTES + ST * C::B_BYTES;
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-        af[i] = *(const bf16x8*)(smem + fa.a[s ^ ((i & 1) << 1)] + i * 32 * 128 + ST * C::A_BYTES);
+    for (int i = 0; i < C::TM; ++i) af[i] = g.oa.frag(As, i, s);
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-        bf[j] = *(const bf16x8*)(smem + fa.b[s ^ ((j & 1) << 1)] + j * 32 * 128 + ST * C::B_BYTES);
+    for (int j = 0; j < C::TN; ++j) bf[j] = g.ob.frag(Bs, j, s);
 }
 
 template <class C>
@@ -275,64 +293,67 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[C::TM][C::TN], const bf1
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
 }
 
+// Scheduling-group masks (AMDGPU sched_group_barrier): inside each k-step the next fragments'
+// LDS reads issue before this k-step's MFMAs.
+constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
+
+// Issue the loads of the K tile at k0: DMA operands go straight into LDS stage `stage`,
+// register-staged operands into their registers (written to LDS by store_stage()).
 template <class C, int LA, int LB>
-struct GemmState {
-    TileLoader<C::BM, C::NT, LA> la;
-    TileLoader<C::BN, C::NT, LB> lb;
-    __amdgpu_buffer_rsrc_t ra, rb;
-    int lda, ldb, m0, n0, M, N, kbeg, kend, tid;
-    FragAddr<C> fa;
-    bf16x8 a0[C::TM], b0[C::TN], a1[C::TM], b1[C::TN];
-};
+__device__ __forceinline__ void load_stage(GemmState<C, LA, LB>& g, char* smem, int stage, int k0) {
+    if constexpr (decltype(g.oa)::DMA) g.oa.load(g.ra, g.lda, g.m0, g.M, k0, g.kend, g.tid, smem + stage * C::A_BYTES);
+    else g.oa.fetch(g.ra, g.lda, g.m0, g.M, k0, g.kend, g.tid);
+    if constexpr (decltype(g.ob)::DMA)
+        g.ob.load(g.rb, g.ldb, g.n0, g.N, k0, g.kend, g.tid, smem + 2 * C::A_BYTES + stage * C::B_BYTES);
+    else g.ob.fetch(g.rb, g.ldb, g.n0, g.N, k0, g.kend, g.tid);
+}
+template <class C, int LA, int LB>
+__device__ __forceinline__ void store_stage(const GemmState<C, LA, LB>& g, char* smem, int stage) {
+    if constexpr (!decltype(g.oa)::DMA) g.oa.store(smem + stage * C::A_BYTES, g.tid);
+    if constexpr (!decltype(g.ob)::DMA) g.ob.store(smem + 2 * C::A_BYTES + stage * C::B_BYTES, g.tid);
+}
 
-// Scheduling-group masks (AMDGPU sched_group_barrier): the order inside each k-step is pinned so
-// that the next fragments' LDS reads issue before this k-step's MFMAs and the next tile's LDS
-// writes sit between MFMAs.
-constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
+constexpr int SG_DS_WRITE = 0x200;
 
-// One K tile held in LDS stage ST (fragments of its k-step 0 already in a0/b0).
+// One K tile held in LDS stage ST (fragments of its k-step 0 already in a0/b0). The next tile
+// goes into the other stage, which was last read before the previous barrier: DMA operands at
+// the start of this tile, register-staged ones after its third k-step.
 template <class C, int LA, int LB, int ST>
 __device__ __forceinline__ void gemm_tile(GemmState<C, LA, LB>& g, char* smem, f32x16 (&acc)[C::TM][C::TN], int kt,
                                           int nk) {
     constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
-    constexpr int NVM = TileLoader<C::BM, C::NT, LA>::NLOAD + TileLoader<C::BN, C::NT, LB>::NLOAD;
-    constexpr int NDW = TileLoader<C::BM, C::NT, LA>::NSTORE + TileLoader<C::BN, C::NT, LB>::NSTORE;
+    constexpr bool REG = !decltype(g.oa)::DMA || !decltype(g.ob)::DMA;
+    constexpr int NDW = (decltype(g.oa)::DMA ? 0 : 8) + (decltype(g.ob)::DMA ? 0 : 8);
     const bool more = kt + 1 < nk;
-    if (more) {
-        const int k0 = g.kbeg + (kt + 1) * C::BK;
-        g.la.load(g.ra, g.lda, g.m0, g.M, k0, g.kend, g.tid);
-        g.lb.load(g.rb, g.ldb, g.n0, g.N, k0, g.kend, g.tid);
-    }
-    // k-step 0
-    read_frags<C, ST>(smem, g.fa, 1, g.a1, g.b1);
+    if (more) load_stage(g, smem, ST ^ 1, g.kbeg + (kt + 1) * C::BK);
+    read_frags<C, LA, LB, ST>(g, smem, 1, g.a1, g.b1);
     mfma_step<C>(acc, g.a0, g.b0);
-    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, NVM, 0);
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // k-step 1
-    read_frags<C, ST>(smem, g.fa, 2, g.a0, g.b0);
+    read_frags<C, LA, LB, ST>(g, smem, 2, g.a0, g.b0);
     mfma_step<C>(acc, g.a1, g.b1);
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // k-step 2, with the next tile's LDS writes (the other stage was last read in the previous
-    // tile, which ended on a barrier)
-    read_frags<C, ST>(smem, g.fa, 3, g.a1, g.b1);
+    read_frags<C, LA, LB, ST>(g, smem, 3, g.a1, g.b1);
     mfma_step<C>(acc, g.a0, g.b0);
-    if (more) {
-        g.la.store(smem + (ST ^ 1) * C::A_BYTES, g.tid);
-        g.lb.store(smem + 2 * C::A_BYTES + (ST ^ 1) * C::B_BYTES, g.tid);
+    if constexpr (REG) {
+        if (more) store_stage(g, smem, ST ^ 1);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM / 2, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, NDW, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM - NM / 2, 0);
+    } else {
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM / 2, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, NDW, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM - NM / 2, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // k-step 3
     mfma_step<C>(acc, g.a1, g.b1);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA into the next stage has landed
     __syncthreads();
-    if (more) read_frags<C, ST ^ 1>(smem, g.fa, 0, g.a0, g.b0);
+    if (more) read_frags<C, LA, LB, ST ^ 1>(g, smem, 0, g.a0, g.b0);
 }
 
 template <class C, int LA, int LB, class Epi>
@@ -340,7 +361,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restr
                                                              const bf16* __restrict__ B, int ldb,
                                                              int M, int N, int K, int k_per_split,
                                                              uint32_t a_bytes, uint32_t b_bytes, Epi epi) {
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WGN, wn = wave % C::WGN;
     const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
@@ -358,7 +379,8 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restr
     g.kbeg = blockIdx.y * k_per_split;
     g.kend = min(K, g.kbeg + k_per_split);
     g.tid = tid;
-    g.fa.init(wm * C::WM + (lane & 31), wn * C::WN + (lane & 31), lane >> 5);
+    g.oa.init(wm * C::WM + (lane & 31), lane);
+    g.ob.init(wn * C::WN + (lane & 31), lane);
 
     f32x16 acc[C::TM][C::TN];
 #pragma unroll
@@ -370,13 +392,12 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restr
 
     const int nk = g.kend > g.kbeg ? (g.kend - g.kbeg + C::BK - 1) / C::BK : 0;
     if (nk > 0) {
-        g.la.load(g.ra, lda, g.m0, M, g.kbeg, g.kend, tid);
-        g.lb.load(g.rb, ldb, g.n0, N, g.kbeg, g.kend, tid);
-        g.la.store(smem, tid);
-        g.lb.store(smem + 2 * C::A_BYTES, tid);
+        load_stage(g, smem, 0, g.kbeg);
+        store_stage(g, smem, 0);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (nk > 0) read_frags<C, 0>(smem, g.fa, 0, g.a0, g.b0);
+    if (nk > 0) read_frags<C, LA, LB, 0>(g, smem, 0, g.a0, g.b0);
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
         gemm_tile<C, LA, LB, 0>(g, smem, acc, kt, nk);
