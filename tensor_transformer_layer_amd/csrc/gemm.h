@@ -44,10 +44,11 @@ struct GemmCfg {
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
 };
 
-// 256x256 with 8 waves (2 x 4, 128x64 per wave, two waves per SIMD) and 128x128 with 4 waves
-// (64x64 per wave, two workgroups per CU): both keep two waves per SIMD to hide latency; the
-// larger tile halves LDS and L2 traffic per MFMA.
+// 256x256 and 256x192 with 8 waves (128x64 / 64x96 per wave, two waves per SIMD) and 128x128
+// with 4 waves (64x64 per wave, two workgroups per CU): all keep two waves per SIMD to hide
+// latency; the larger tiles cut LDS and L2 traffic per MFMA.
 typedef GemmCfg<256, 256, 2, 4> Cfg256x256;
+typedef GemmCfg<256, 192, 4, 2> Cfg256x192;   // 8 waves, 64x96 per wave: N = 1536 / 3072 / 1152 in whole tiles
 typedef GemmCfg<128, 128, 2, 2> Cfg128x128;
 
 // Buffer resource over [base, base + bytes): loads at offsets >= bytes return 0, which is how
@@ -109,12 +110,11 @@ template <int R, int NT> struct Operand<R, NT, MNCONTIG> {
     // per 16-byte or 8-byte LDS write), whose fragment reads are then used unchanged.
     static constexpr bool DMA = false;
     static constexpr int BYTES = R * 128;
-    static constexpr int EPT = R * 64 / NT;   // elements per thread
-    static constexpr int KB = EPT / 8;        // k-rows per thread (8 or 4)
     static constexpr int MC = R / 8;          // 8-wide mn chunks across the tile
+    static constexpr int KB = (MC * 8 >= NT) ? 8 : 4;   // k-rows per thread
+    static constexpr int USED = MC * (64 / KB);        // threads that carry a block
     static constexpr int NLOAD = KB, NSTORE = 8;
-    static_assert(KB == 8 || KB == 4, "unsupported tile/threads ratio");
-    static_assert(MC * (64 / KB) == NT, "thread mapping must cover the tile exactly");
+    static_assert(USED <= NT && (MC * 8 == NT || MC * 16 <= NT), "thread mapping must cover the tile exactly");
     Operand<R, NT, KCONTIG> kc;   // fragment addressing of the K-contiguous layout
     u32x4 v[KB];
     __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, int ld, int mn0, int MN, int k0, int K, int tid) {
@@ -123,11 +123,12 @@ template <int R, int NT> struct Operand<R, NT, MNCONTIG> {
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
             int k = k0 + kg * KB + j;
-            int off = (mn < MN && k < K) ? (k * ld + mn) * 2 : kOOB;
+            int off = (tid < USED && mn < MN && k < K) ? (k * ld + mn) * 2 : kOOB;
             v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
         }
     }
     __device__ __forceinline__ void store(char* lds, int tid) const {
+        if (USED < NT && tid >= USED) return;
         int mc = tid % MC, kg = tid / MC;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {

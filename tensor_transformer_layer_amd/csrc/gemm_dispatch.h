@@ -29,6 +29,7 @@ static hipError_t launch_plan(const GemmReq& r, const GemmPlan& p, const Epi& e,
     switch (p.cfg) {
         case 0: return launch_cfg<Cfg256x256, LA, LB>(r, p.splits, e, st);
         case 1: return launch_cfg<Cfg128x128, LA, LB>(r, p.splits, e, st);
+        case 2: return launch_cfg<Cfg256x192, LA, LB>(r, p.splits, e, st);
     }
     return hipErrorInvalidValue;
 }

@@ -4,16 +4,37 @@
 
 namespace tp {
 
-static const int kNCfg = 2;
-static const int kBM[kNCfg] = {256, 128};
-static const int kBN[kNCfg] = {256, 128};
+static const int kNCfg = 3;
+static const int kBM[kNCfg] = {256, 128, 256};
+static const int kBN[kNCfg] = {256, 128, 192};
 // relative per-tile MFMA efficiency, measured on MI355X at the layer's shapes (K = 1536..3072)
-static const double kEff[kNCfg] = {1.0, 0.93};
+static const double kEff[kNCfg] = {1.0, 0.93, 0.95};
 // workgroups of each configuration resident per CU
-static const int kPerCU[kNCfg] = {1, 2};
+static const int kPerCU[kNCfg] = {1, 2, 1};
 static const int kCUs = 256;
 
+// Plans measured on MI355X for the GEMMs of the 8.3B-shape layer shard (t = 8) and its
+// vocabulary shard: the fastest of the three tile shapes and split counts 1..6 per shape
+// (layout-independent here). Other shapes use the time model below.
+struct TunedPlan { int M, N, K, split_ok, cfg, splits; };
+static const TunedPlan kTuned[] = {
+    {8192, 1536, 3072, 0, 2, 1},   // MLP GEMM1 fwd, dU
+    {8192, 3072, 1536, 0, 2, 1},   // MLP GEMM2 fwd, dX
+    {8192, 1152, 3072, 0, 2, 1},   // QKV fwd
+    {8192, 3072, 384, 0, 2, 1},    // output projection fwd
+    {8192, 384, 3072, 0, 1, 1},    // dO
+    {8192, 3072, 1152, 0, 2, 1},   // dXn
+    {6400, 8192, 3072, 0, 1, 1},   // vocabulary logits
+    {1536, 3072, 8192, 1, 0, 3},   // dB
+    {3072, 1536, 8192, 1, 0, 3},   // dA
+    {384, 3072, 8192, 1, 1, 6},    // dWo
+    {3072, 1152, 8192, 1, 2, 3},   // dWqkv
+};
+
 GemmPlan plan_gemm_bf16(int M, int N, int K, bool allow_split) {
+    for (const TunedPlan& t : kTuned)
+        if (t.M == M && t.N == N && t.K == K && (t.splits == 1 || (allow_split && t.split_ok)))
+            return GemmPlan{t.cfg, t.splits, kBM[t.cfg], kBN[t.cfg]};
     const double cu_flops = 2.5e15 / kCUs * 0.8;   // sustained per-CU rate at full efficiency
     const double round_overhead = 2.0e-6;          // prologue + epilogue per wave of tiles
     GemmPlan best{1, 1, 128, 128};

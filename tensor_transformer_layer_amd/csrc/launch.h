@@ -29,7 +29,7 @@ struct GemmReq {
 };
 
 struct GemmPlan {
-    int cfg;      // 0: 256x256 (8 waves), 1: 128x128 (4 waves)
+    int cfg;      // 0: 256x256 (8 waves), 1: 128x128 (4 waves), 2: 256x192 (8 waves)
     int splits;   // K splits (>1 only when the request allows it)
     int bm, bn;
 };
