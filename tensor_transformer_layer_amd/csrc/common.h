@@ -27,6 +27,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// 8 consecutive elements <-> fp32
+__device__ __forceinline__ void load8(const bf16* p, float (&o)[8]) {
+    bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (float)v[e];
+}
+__device__ __forceinline__ void load8(const float* p, float (&o)[8]) {
+    f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { o[e] = a[e]; o[e + 4] = b[e]; }
+}
+__device__ __forceinline__ void store8(bf16* p, const float (&v)[8]) {
+    *(u32x4*)p = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7])};
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+    *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
+    *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
 // GeLU, erf form: x * Phi(x). Derivative: Phi(x) + x * phi(x).
 __device__ __forceinline__ float gelu_f(float x) {
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));

@@ -166,8 +166,49 @@ __device__ __forceinline__ void map_tile(int bid, int nblocks, int tiles_m, int 
 }
 
 // ----------------------------------------------------------------------------------------------
-// Epilogues. Elementwise ones expose op(row, col, value); the MFMA kernel calls apply().
+// Epilogues. Each exposes op8(row, col, v[8]) for 8 consecutive columns of one row (col % 8 == 0,
+// N and ld multiples of 8, checked at launch) and is applied through apply_staged(): a wave's
+// accumulators go to LDS one 32-row strip at a time and come back row-major, so every auxiliary
+// load and output store is a 16-byte vector access and a wave's store covers whole row segments.
+// (In the MFMA layout a lane holds one column of four rows, which would mean 2-byte accesses.)
 // ----------------------------------------------------------------------------------------------
+template <class C> struct Staging {
+    static constexpr int LD = C::WN + 8;    // floats per slab row: rows r and r + 4 fall in opposite bank halves
+    static constexpr int SLAB = 32 * LD;    // floats per wave
+    static constexpr int CPR = C::WN / 8;   // 8-column chunks per row
+    static constexpr int CHUNKS = 32 * CPR;
+    static_assert(SLAB * 4 * C::NW <= C::LDS, "epilogue staging exceeds the tile buffers");
+    static_assert(CHUNKS % 64 == 0, "chunks must divide evenly over the wave");
+};
+
+template <class C, class Op>
+__device__ __forceinline__ void apply_staged(const Op& op, f32x16 (&acc)[C::TM][C::TN], int mw0, int nw0, int lane,
+                                             int wave, int M, int N, char* smem) {
+    typedef Staging<C> S;
+    float* slab = (float*)smem + wave * S::SLAB;
+    const int h = lane >> 5, l32 = lane & 31;
+    __syncthreads();   // every wave has read its last fragments out of the tile buffers
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) slab[(8 * (v >> 2) + 4 * h + (v & 3)) * S::LD + j * 32 + l32] = acc[i][j][v];
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < S::CHUNKS / 64; ++q) {
+            const int c = q * 64 + lane, r = c / S::CPR, cc = c - r * S::CPR;
+            const float* p = slab + r * S::LD + cc * 8;
+            f32x4 lo = *(const f32x4*)p, hi = *(const f32x4*)(p + 4);
+            float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const int row = mw0 + i * 32 + r, col = nw0 + cc * 8;
+            if (row < M && col < N) op.op8(row, col, v);
+        }
+        __syncthreads();   // the strip is consumed before the next one overwrites it
+    }
+}
+
+// Elementwise form, straight from the MFMA layout (used by the transposed store).
 template <class C, class Op>
 __device__ __forceinline__ void apply_elementwise(const Op& op, f32x16 (&acc)[C::TM][C::TN], int mw0, int nw0,
                                                   int lane, int M, int N) {
@@ -189,8 +230,16 @@ __device__ __forceinline__ void apply_elementwise(const Op& op, f32x16 (&acc)[C:
     }
 }
 
+#define TP_STAGED_APPLY                                                                                         \
+    template <class C>                                                                                          \
+    __device__ __forceinline__ void apply(f32x16 (&acc)[C::TM][C::TN], int, int, int mw0, int nw0, int lane,    \
+                                          int M, int N, char* smem) const {                                     \
+        apply_staged<C>(*this, acc, mw0, nw0, lane, (int)(threadIdx.x >> 6), M, N, smem);                      \
+    }
+
 // out[r*ld + c] = v (+ bias[c]) (+ out[r*ld + c] if accumulate)
 template <typename T> struct EpiStore {
+    static constexpr bool kVec8 = true;
     __device__ __forceinline__ void set_split(int) {}
     T* out; int ld; const T* bias; int accumulate;
     __device__ __forceinline__ void operator()(int r, int c, float v) const {
@@ -199,14 +248,28 @@ template <typename T> struct EpiStore {
         if (accumulate) v += to_f32(*p);
         *p = from_f32<T>(v);
     }
-    template <class C> __device__ __forceinline__ void apply(f32x16 (&acc)[C::TM][C::TN], int, int, int mw0, int nw0,
-                                                            int lane, int M, int N, char*) const {
-        apply_elementwise<C>(*this, acc, mw0, nw0, lane, M, N);
+    __device__ __forceinline__ void op8(int r, int c, float (&v)[8]) const {
+        T* p = out + (size_t)r * ld + c;
+        if (bias) {
+            float b[8];
+            load8(bias + c, b);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += b[e];
+        }
+        if (accumulate) {
+            float o[8];
+            load8(p, o);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += o[e];
+        }
+        store8(p, v);
     }
+    TP_STAGED_APPLY
 };
 
 // out[c*ld + r] = v  (transposed store; fp32 logits of the vocab shard)
 template <typename T> struct EpiStoreT {
+    static constexpr bool kVec8 = false;
     __device__ __forceinline__ void set_split(int) {}
     T* out; int ld;
     __device__ __forceinline__ void operator()(int r, int c, float v) const { out[(size_t)c * ld + r] = from_f32<T>(v); }
@@ -218,6 +281,7 @@ template <typename T> struct EpiStoreT {
 
 // U = v + bias; Y = GeLU(U)
 template <typename T> struct EpiBiasGelu {
+    static constexpr bool kVec8 = true;
     __device__ __forceinline__ void set_split(int) {}
     T* U; T* Y; int ld; const T* bias;
     __device__ __forceinline__ void operator()(int r, int c, float v) const {
@@ -226,38 +290,53 @@ template <typename T> struct EpiBiasGelu {
         U[o] = from_f32<T>(v);
         Y[o] = from_f32<T>(gelu_f(v));
     }
-    template <class C> __device__ __forceinline__ void apply(f32x16 (&acc)[C::TM][C::TN], int, int, int mw0, int nw0,
-                                                            int lane, int M, int N, char*) const {
-        apply_elementwise<C>(*this, acc, mw0, nw0, lane, M, N);
+    __device__ __forceinline__ void op8(int r, int c, float (&v)[8]) const {
+        if (bias) {
+            float b[8];
+            load8(bias + c, b);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += b[e];
+        }
+        const size_t o = (size_t)r * ld + c;
+        store8(U + o, v);
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = gelu_f(v[e]);
+        store8(Y + o, y);
     }
+    TP_STAGED_APPLY
 };
 
 // dU = v * GeLU'(U)
 template <typename T> struct EpiDGelu {
+    static constexpr bool kVec8 = true;
     __device__ __forceinline__ void set_split(int) {}
     T* dU; const T* U; int ld;
     __device__ __forceinline__ void operator()(int r, int c, float v) const {
         size_t o = (size_t)r * ld + c;
         dU[o] = from_f32<T>(v * gelu_grad_f(to_f32(U[o])));
     }
-    template <class C> __device__ __forceinline__ void apply(f32x16 (&acc)[C::TM][C::TN], int, int, int mw0, int nw0,
-                                                            int lane, int M, int N, char*) const {
-        apply_elementwise<C>(*this, acc, mw0, nw0, lane, M, N);
+    __device__ __forceinline__ void op8(int r, int c, float (&v)[8]) const {
+        const size_t o = (size_t)r * ld + c;
+        float u[8];
+        load8(U + o, u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= gelu_grad_f(u[e]);
+        store8(dU + o, v);
     }
+    TP_STAGED_APPLY
 };
 
 // Split-K partial: part[split][r*ld + c] = v (fp32). Reduced later in split order.
 struct EpiPartial {
+    static constexpr bool kVec8 = true;
     float* part; int ld; size_t split_stride;
     int split;
     __device__ __forceinline__ void set_split(int s) { split = s; }
-    __device__ __forceinline__ void operator()(int r, int c, float v) const {
-        part[(size_t)split * split_stride + (size_t)r * ld + c] = v;
+    __device__ __forceinline__ void op8(int r, int c, float (&v)[8]) const {
+        store8(part + (size_t)split * split_stride + (size_t)r * ld + c, v);
     }
-    template <class C> __device__ __forceinline__ void apply(f32x16 (&acc)[C::TM][C::TN], int, int, int mw0, int nw0,
-                                                            int lane, int M, int N, char*) const {
-        apply_elementwise<C>(*this, acc, mw0, nw0, lane, M, N);
-    }
+    TP_STAGED_APPLY
 };
 
 // ----------------------------------------------------------------------------------------------
@@ -467,17 +546,23 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
         }
 }
 
-// Split-K reduction: out = epi(sum_{s=0}^{splits-1} part[s][r*ld + c]) in split order.
+// Split-K reduction: out = epi(sum_{s=0}^{splits-1} part[s][r*N + c]) in split order, 8 columns
+// per thread (N % 8 == 0).
 template <class Epi>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
-                                                            size_t split_stride, int M, int N, int ld, Epi epi) {
-    size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+                                                            size_t split_stride, int M, int N, Epi epi) {
+    const size_t idx = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (idx >= (size_t)M * N) return;
-    int r = (int)(idx / N), c = (int)(idx % N);
-    size_t o = (size_t)r * ld + c;
-    float acc = 0.f;
-    for (int s = 0; s < splits; ++s) acc += part[(size_t)s * split_stride + o];
-    epi(r, c, acc);
+    const int r = (int)(idx / N), c = (int)(idx % N);
+    float acc[8];
+    load8(part + idx, acc);
+    for (int s = 1; s < splits; ++s) {
+        float v[8];
+        load8(part + (size_t)s * split_stride + idx, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += v[e];
+    }
+    epi.op8(r, c, acc);
 }
 
 }  // namespace tp

@@ -18,6 +18,8 @@ static hipError_t launch_cfg(const GemmReq& r, int splits, const Epi& e, hipStre
     size_t a_bytes = (size_t)(LA == KCONTIG ? r.M : r.K) * r.lda * 2;
     size_t b_bytes = (size_t)(LB == KCONTIG ? r.N : r.K) * r.ldb * 2;
     if (a_bytes >= 0x7fff0000u || b_bytes >= 0x7fff0000u) return hipErrorInvalidValue;
+    // vector epilogues move 8 columns at a time
+    if (Epi::kVec8 && (r.N % 8 != 0 || r.ldc % 8 != 0)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_bf16_kernel<C, LA, LB, Epi>), dim3(tiles, splits), dim3(C::NT), 0, st,
                        (const bf16*)r.A, r.lda, (const bf16*)r.B, r.ldb, r.M, r.N, r.K, kps, (uint32_t)a_bytes,
                        (uint32_t)b_bytes, e);
@@ -45,8 +47,8 @@ static hipError_t gemm_run(const GemmReq& r, const GemmPlan& p, void* ws, hipStr
             if (err != hipSuccess) return err;
             EpiStore<bf16> fin{(bf16*)r.out, r.ldc, (const bf16*)r.bias, r.accumulate};
             size_t n = (size_t)r.M * r.N;
-            hipLaunchKernelGGL((splitk_reduce_kernel<EpiStore<bf16>>), dim3((unsigned)((n + 255) / 256)), dim3(256),
-                               0, st, (const float*)ws, p.splits, n, r.M, r.N, r.N, fin);
+            hipLaunchKernelGGL((splitk_reduce_kernel<EpiStore<bf16>>), dim3((unsigned)((n / 8 + 255) / 256)),
+                               dim3(256), 0, st, (const float*)ws, p.splits, n, r.M, r.N, fin);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;

@@ -34,6 +34,7 @@ __device__ __forceinline__ void xent_merge_se(float& mx, float& se, float omx, f
 }
 
 struct EpiXent {
+    static constexpr bool kVec8 = false;
     XentPartial* part;        // [tiles_m][N]
     const int32_t* targets;   // [N] global ids
     int col0;                 // global id of local row 0 (r * V_t)
