@@ -184,13 +184,19 @@ tp_status tp_layernorm_fwd(int T, int h, tp_dtype dt, float eps, const void* x, 
                            const void* beta, void* y, float* mean, float* rstd, hipStream_t stream);
 
 /* LayerNorm backward: dx = dres + d(LN)/dx^T dy; dgamma = sum_rows dy * xhat; dbeta = sum_rows dy.
- * dres [T, h] (the residual branch's gradient) may be NULL. dgamma/dbeta [h] in dt may be NULL;
- * accumulate as above. */
+ * dres [T, h] (the residual branch's gradient) may be NULL. dgamma/dbeta [h] in dt may be NULL.
+ * Optional column sums taken in the same pass, [h] in dt, may be NULL: dres_colsum = sum_rows dres
+ * (needs dres), dx_colsum = sum_rows dx (of dx before rounding to dt). Around a pre-LN block these
+ * are the replicated bias gradients of the row-parallel layers: with dres the gradient of the
+ * layer output and dy the summed MLP input gradient, dres_colsum is the MLP output bias's gradient
+ * and dx_colsum the attention output bias's ("Megatron-LM, annotated", §3.5).
+ * accumulate (0 or 1) applies to every [h] output, as above. The workspace holds four fp32
+ * partial rows per block; tp_layernorm_bwd_workspace gives its size (0 when T = 0). */
 size_t tp_layernorm_bwd_workspace(int T, int h, tp_dtype dt);
 tp_status tp_layernorm_bwd(int T, int h, tp_dtype dt, const void* x, const void* gamma,
                            const float* mean, const float* rstd, const void* dy, const void* dres,
-                           void* dx, void* dgamma, void* dbeta, int accumulate,
-                           void* ws, size_t ws_bytes, hipStream_t stream);
+                           void* dx, void* dgamma, void* dbeta, void* dres_colsum, void* dx_colsum,
+                           int accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Column sums of G [T, n] into out [n] (the replicated bias gradients of the row-parallel
  * layers), in a fixed order. */

@@ -56,7 +56,7 @@ SIGNATURES = {
     "tp_sum_partials": (_i, [_i, _i, _i, _i, _pp, _p, _p, _p, _i, _p]),
     "tp_layernorm_fwd": (_i, [_i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p]),
     "tp_layernorm_bwd_workspace": (_z, [_i, _i, _i]),
-    "tp_layernorm_bwd": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
+    "tp_layernorm_bwd": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
     "tp_colsum_workspace": (_z, [_i, _i, _i]),
     "tp_colsum": (_i, [_i, _i, _i, _p, _p, _i, _p, _z, _p]),
 }
@@ -182,11 +182,11 @@ def tp_layernorm_bwd_workspace(T, h, dt):
     return lib.tp_layernorm_bwd_workspace(T, h, _dt(dt))
 
 
-def tp_layernorm_bwd(T, h, dt, x, gamma, mean, rstd, dy, dres, dx, dgamma, dbeta, accumulate, ws, ws_bytes,
-                     stream=None):
+def tp_layernorm_bwd(T, h, dt, x, gamma, mean, rstd, dy, dres, dx, dgamma, dbeta, dres_colsum, dx_colsum,
+                     accumulate, ws, ws_bytes, stream=None):
     _check(lib.tp_layernorm_bwd(T, h, _dt(dt), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dy), _ptr(dres),
-                                _ptr(dx), _ptr(dgamma), _ptr(dbeta), accumulate, _ptr(ws), ws_bytes,
-                                _stream(stream)))
+                                _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(dres_colsum), _ptr(dx_colsum), accumulate,
+                                _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def tp_colsum_workspace(T, n, dt):

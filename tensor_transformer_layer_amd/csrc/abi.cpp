@@ -399,13 +399,14 @@ tp_status tp_layernorm_fwd(int T, int h, tp_dtype dt, float eps, const void* x, 
 
 size_t tp_layernorm_bwd_workspace(int T, int h, tp_dtype dt) {
     (void)dt;
-    if (T < 0 || h <= 0) return 0;
-    return al256(2 * (size_t)ln_bwd_blocks(T) * h * sizeof(float));
+    if (T <= 0 || h <= 0) return 0;
+    return al256(4 * (size_t)ln_bwd_blocks(T) * h * sizeof(float));   // four column-sum partials
 }
 
 tp_status tp_layernorm_bwd(int T, int h, tp_dtype dt, const void* x, const void* gamma, const float* mean,
                            const float* rstd, const void* dy, const void* dres, void* dx, void* dgamma, void* dbeta,
-                           int accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
+                           void* dres_colsum, void* dx_colsum, int accumulate, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
     const char* fn = "tp_layernorm_bwd";
     tp_status s;
     if ((s = check_dt(fn, dt)) != TP_OK) return s;
@@ -414,13 +415,15 @@ tp_status tp_layernorm_bwd(int T, int h, tp_dtype dt, const void* x, const void*
     if (h > 8192) return fail(TP_ERR_UNSUPPORTED, "%s: h=%d exceeds 8192", fn, h);
     if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_ARG, "%s: accumulate=%d must be 0 or 1", fn, accumulate);
     NEED(x); NEED(gamma); NEED(mean); NEED(rstd); NEED(dy); NEED(dx); OPT(dres); OPT(dgamma); OPT(dbeta);
-    if ((dgamma || dbeta)) {
+    OPT(dres_colsum); OPT(dx_colsum);
+    if (dres_colsum && !dres) return fail(TP_ERR_ARG, "%s: dres_colsum needs dres", fn);
+    if (dgamma || dbeta || dres_colsum || dx_colsum) {
         size_t need = tp_layernorm_bwd_workspace(T, h, dt);
         if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
         if (need > 0) NEED(ws);
     }
-    HIP_TRY(layernorm_bwd(dt == TP_BF16, T, h, x, gamma, mean, rstd, dy, dres, dx, dgamma, dbeta, accumulate,
-                          (float*)ws, stream), fn);
+    HIP_TRY(layernorm_bwd(dt == TP_BF16, T, h, x, gamma, mean, rstd, dy, dres, dx, dgamma, dbeta, dres_colsum,
+                          dx_colsum, accumulate, (float*)ws, stream), fn);
     return ok();
 }
 

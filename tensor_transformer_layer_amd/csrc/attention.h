@@ -13,9 +13,18 @@
 // row-major V tile with gfx950's transposing LDS load: no tile is ever transposed in memory.
 // Softmax runs in the log2 domain in fp32 (scores pre-scaled by log2(e)/sqrt(d)).
 //
-// Backward: D = rowsum(dO * O); dK/dV kernel owns 64 keys per block and loops over query tiles;
-// dQ kernel owns 64 queries per block and loops over key tiles. Both recompute P from lse.
-// No atomics: every output element is written by exactly one lane.
+// Work split. A block has four waves and owns 64 rows (queries in the forward and dQ kernels, keys
+// in the dK/dV kernel): waves 0/1 and 2/3 each cover the 64 rows as two 32-row groups, and the two
+// pairs take alternate 64-wide tiles of the loop dimension (keys, or queries for dK/dV), so a
+// block carries two waves per SIMD pair and half the serial chain of one wave per row group. The
+// pairs' partial results are merged through LDS at the end in a fixed order. Blocks are launched
+// heaviest first (most visible tiles under the causal mask). Up to D = 96 the kernels are held to
+// 256 registers per lane (two waves per SIMD). Loop tiles are staged through
+// registers: the next two tiles' global loads are in flight while the current two are used.
+//
+// Backward: D = rowsum(dO * O); the dK/dV kernel owns 64 keys per block and loops over query
+// tiles; the dQ kernel owns 64 queries per block and loops over key tiles. Both recompute P from
+// lse. No atomics: every output element is written by exactly one lane.
 #pragma once
 #include "common.h"
 
@@ -24,7 +33,7 @@ namespace tp {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int ATT_B = 64;        // queries per block (fwd, dQ) / keys per block (dK dV), rows per tile
-constexpr int ATT_NT = 128;      // 2 waves, 32 rows each
+constexpr int ATT_NT = 256;      // 4 waves: two 32-row groups x two loop-tile parities
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -38,11 +47,12 @@ __device__ __forceinline__ int att_off(int row, int col) {
     return row * D + ((((col >> 3) ^ ((row >> 2) & 3)) << 3) | (col & 7));
 }
 
-// Register-staged copy of rows [r0, r0+64) x D of a strided bf16 matrix (rows >= valid read 0).
+// Register-staged copy of rows [r0, r0 + 128) x D of a strided bf16 matrix (rows >= valid read 0)
+// into two consecutive LDS tiles (row r lands in tile r / 64; att_off is valid across both).
 template <int D>
 struct AttTileRegs {
-    static constexpr int CPR = D / 8, N = ATT_B * CPR / ATT_NT;
-    static_assert((ATT_B * CPR) % ATT_NT == 0, "tile/threads mismatch");
+    static constexpr int ROWS = 2 * ATT_B, CPR = D / 8, N = ROWS * CPR / ATT_NT;
+    static_assert((ROWS * CPR) % ATT_NT == 0, "tile/threads mismatch");
     u32x4 v[N];
     __device__ __forceinline__ void load(const bf16* __restrict__ src, int ld, int r0, int valid, int tid) {
 #pragma unroll
@@ -51,14 +61,27 @@ struct AttTileRegs {
             v[i] = (r0 + row < valid) ? *(const u32x4*)(src + (size_t)(r0 + row) * ld + dc * 8) : u32x4{0, 0, 0, 0};
         }
     }
-    __device__ __forceinline__ void store(bf16* tile, int tid) const {
+    __device__ __forceinline__ void store(bf16* tiles, int tid) const {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             int c = tid + i * ATT_NT, row = c / CPR, dc = c % CPR;
-            *(u32x4*)(tile + att_off<D>(row, dc * 8)) = v[i];
+            *(u32x4*)(tiles + att_off<D>(row, dc * 8)) = v[i];
         }
     }
 };
+
+// Direct copy of rows [r0, r0 + 64) x D of a strided bf16 matrix into one LDS tile (rows >= valid
+// read 0); used once per block for the block's own rows, which then serve as MFMA operands
+// straight from LDS instead of occupying registers.
+template <int D>
+__device__ __forceinline__ void load_tile(const bf16* __restrict__ src, int ld, int r0, int valid, bf16* tile, int tid) {
+    constexpr int CPR = D / 8;
+    for (int c = tid; c < ATT_B * CPR; c += ATT_NT) {
+        const int row = c / CPR, dc = c % CPR;
+        const u32x4 v = (r0 + row < valid) ? *(const u32x4*)(src + (size_t)(r0 + row) * ld + dc * 8) : u32x4{0, 0, 0, 0};
+        *(u32x4*)(tile + att_off<D>(row, dc * 8)) = v;
+    }
+}
 
 // MFMA operand with the tile's rows as M and its columns as K: rows row0 + lane%32, columns
 // col0 + 8*(lane/32) .. +7.
@@ -97,33 +120,39 @@ __device__ __forceinline__ f32x16 zero16() {
     return z;
 }
 
+// Exchange of per-lane fp32 values between the two parities of a row group (LDS, lane-fastest).
+template <int NV>
+__device__ __forceinline__ void xch_put(float* xch, int group, int j, int lane, float v) {
+    xch[(group * NV + j) * 64 + lane] = v;
+}
+template <int NV>
+__device__ __forceinline__ float xch_get(const float* xch, int group, int j, int lane) {
+    return xch[(group * NV + j) * 64 + lane];
+}
+
 // ---------------------------------------------------------------------------------------------
-// Forward. grid = (ceil(s/64) query tiles, heads_t, b); heavy (late) query tiles first.
-// K and V tiles are double-buffered; the next tile's global loads are in flight during the
-// current tile's MFMAs. Only tiles that cross the diagonal (or the sequence end) are masked.
+// Forward. grid = (b * heads_t, query tiles), query tile qt = last - blockIdx.y (heavy first).
+// Wave w: row group g = w & 1 (queries qt*64 + 32g ..), key-tile parity kp = w >> 1.
 // ---------------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(ATT_NT) void attn_fwd_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s,
-                                                          int heads_t, float scale_log2, int causal,
-                                                          bf16* __restrict__ O, int ldo, float* __restrict__ lse) {
-    __shared__ __attribute__((aligned(16))) bf16 Kb[2][ATT_B * D];
-    __shared__ __attribute__((aligned(16))) bf16 Vb[2][ATT_B * D];
-    const int qt = gridDim.x - 1 - blockIdx.x, head = blockIdx.y, bi = blockIdx.z;
+__global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(D <= 96 ? 2 : 1)))
+void attn_fwd_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int heads_t, float scale_log2,
+                     int causal, bf16* __restrict__ O, int ldo, float* __restrict__ lse) {
+    __shared__ __attribute__((aligned(16))) bf16 smem[4 * ATT_B * D];   // K tiles [2] | V tiles [2]
+    __shared__ __attribute__((aligned(16))) bf16 Qs[ATT_B * D];          // the block's queries
+    bf16* Kb = smem;
+    bf16* Vb = smem + 2 * ATT_B * D;
+    const int head = blockIdx.x % heads_t, bi = blockIdx.x / heads_t, qt = gridDim.y - 1 - blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int grp = wave & 1, kp = wave >> 1;
     const size_t tok0 = (size_t)bi * s;
     const bf16* Qp = QKV + tok0 * ld + head * D;
     const bf16* Kp = QKV + tok0 * ld + h_t + head * D;
     const bf16* Vp = QKV + tok0 * ld + 2 * h_t + head * D;
-    const int q0w = qt * ATT_B + wave * 32;
+    const int q0w = qt * ATT_B + grp * 32;
     const int myq = q0w + l32;
 
-    bf16x8 qf[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        u32x4 v = u32x4{0, 0, 0, 0};
-        if (myq < s) v = *(const u32x4*)(Qp + (size_t)myq * ld + ks * 16 + 8 * h);
-        qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
+    load_tile<D>(Qp, ld, qt * ATT_B, s, Qs, tid);
     f32x16 o[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
@@ -131,24 +160,25 @@ __global__ __launch_bounds__(ATT_NT) void attn_fwd_kernel(const bf16* __restrict
 
     const int kv_end = causal ? min(s, (qt + 1) * ATT_B) : s;
     const int ntiles = (kv_end + ATT_B - 1) / ATT_B;
+    const int niter = (ntiles + 1) / 2;
     AttTileRegs<D> kr, vr;
-    if (ntiles > 0) {
+    if (niter > 0) {
         kr.load(Kp, ld, 0, s, tid);
         vr.load(Vp, ld, 0, s, tid);
-        kr.store(Kb[0], tid);
-        vr.store(Vb[0], tid);
+        kr.store(Kb, tid);
+        vr.store(Vb, tid);
     }
     __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int k0 = kt * ATT_B, buf = kt & 1;
-        const bool more = kt + 1 < ntiles;
+    for (int it = 0; it < niter; ++it) {
+        const bool more = it + 1 < niter;
         if (more) {
-            kr.load(Kp, ld, k0 + ATT_B, s, tid);
-            vr.load(Vp, ld, k0 + ATT_B, s, tid);
+            kr.load(Kp, ld, (it + 1) * 2 * ATT_B, s, tid);
+            vr.load(Vp, ld, (it + 1) * 2 * ATT_B, s, tid);
         }
-        if (!(causal && k0 > q0w + 31)) {   // some key of this tile is visible to this wave
-            const bf16* K = Kb[buf];
-            const bf16* V = Vb[buf];
+        const int kt = 2 * it + kp, k0 = kt * ATT_B;
+        if (kt < ntiles && !(causal && k0 > q0w + 31)) {   // some key of this tile is visible to this wave
+            const bf16* K = Kb + kp * ATT_B * D;
+            const bf16* V = Vb + kp * ATT_B * D;
             const bool need_mask = (causal && k0 + ATT_B - 1 > q0w) || (k0 + ATT_B > s);
             f32x16 st[2];
 #pragma unroll
@@ -156,7 +186,8 @@ __global__ __launch_bounds__(ATT_NT) void attn_fwd_kernel(const bf16* __restrict
                 st[sub] = zero16();
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ++ks)
-                    st[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(K, sub * 32, ks * 16, lane), qf[ks],
+                    st[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(K, sub * 32, ks * 16, lane),
+                                                                      frag_rows<D>(Qs, grp * 32, ks * 16, lane),
                                                                       st[sub], 0, 0, 0);
             }
             if (need_mask) {
@@ -189,10 +220,13 @@ __global__ __launch_bounds__(ATT_NT) void attn_fwd_kernel(const bf16* __restrict
             rs += __shfl_xor(rs, 32);
             l_i = l_i * alpha + rs;
             m_i = m_new;
+            // rescale only when some lane's running max moved (alpha == 1 leaves o unchanged)
+            if (__builtin_amdgcn_read_exec() && __any(alpha != 1.0f)) {
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
+                for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+                    for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+            }
 #pragma unroll
             for (int ks = 0; ks < ATT_B / 16; ++ks) {
                 bf16x8 pb = pack8(st[ks >> 1], 8 * (ks & 1));
@@ -202,25 +236,46 @@ __global__ __launch_bounds__(ATT_NT) void attn_fwd_kernel(const bf16* __restrict
                                                                     0, 0, 0);
             }
         }
-        if (more) {   // the other buffer was last read before the previous barrier
-            kr.store(Kb[buf ^ 1], tid);
-            vr.store(Vb[buf ^ 1], tid);
+        __syncthreads();   // both tiles consumed
+        if (more) {
+            kr.store(Kb, tid);
+            vr.store(Vb, tid);
         }
         __syncthreads();
     }
-    if (myq < s) {
-        const float inv = 1.0f / l_i;
-        bf16* op = O + (tok0 + myq) * ldo + head * D;
+    // merge the odd-tile partial (m, l, o) into the even-tile one: m = max, rescale both, add
+    constexpr int NV = D / 2 + 2;
+    float* xch = (float*)smem;
+    static_assert(2 * NV * 64 * 4 <= 4 * ATT_B * D * 2, "exchange exceeds the tile buffers");
+    if (kp == 1) {
+        xch_put<NV>(xch, grp, 0, lane, m_i);
+        xch_put<NV>(xch, grp, 1, lane, l_i);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
+            for (int v = 0; v < 16; ++v) xch_put<NV>(xch, grp, 2 + dt * 16 + v, lane, o[dt][v]);
+    }
+    __syncthreads();
+    if (kp == 0 && myq < s) {
+        const float m_o = xch_get<NV>(xch, grp, 0, lane), l_o = xch_get<NV>(xch, grp, 1, lane);
+        const float m = fmaxf(m_i, m_o);
+        const float m_use = (m == -INFINITY) ? 0.f : m;
+        const float a = exp2f(m_i - m_use), c = exp2f(m_o - m_use);
+        const float l = l_i * a + l_o * c;
+        const float inv = 1.0f / l;
+        bf16* op = O + (tok0 + myq) * ldo + head * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[dt][v] = (o[dt][v] * a + xch_get<NV>(xch, grp, 2 + dt * 16 + v, lane) * c) * inv;
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
                 int d = dt * 32 + 8 * i + 4 * h;
-                u32x2 w = u32x2{pack_bf16x2(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv),
-                                pack_bf16x2(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv)};
-                *(u32x2*)(op + d) = w;
+                *(u32x2*)(op + d) = u32x2{pack_bf16x2(o[dt][4 * i], o[dt][4 * i + 1]),
+                                          pack_bf16x2(o[dt][4 * i + 2], o[dt][4 * i + 3])};
             }
-        if (h == 0) lse[((size_t)bi * heads_t + head) * s + myq] = (m_i + log2f(l_i)) * kLn2;
+        }
+        if (h == 0) lse[((size_t)bi * heads_t + head) * s + myq] = (m + log2f(l)) * kLn2;
     }
 }
 
@@ -249,23 +304,26 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(const bf16* __restric
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV. grid = (ceil(s/64) key tiles, heads_t, b). Wave w owns keys kt*64 + 32w .. +31 and loops
-// over the query tiles that can see them; Q and dO tiles (and lse, D) are double-buffered.
+// dK, dV. grid = (b * heads_t, key tiles), key tile kt = blockIdx.y (heavy first under the causal
+// mask). Wave w: key group g = w & 1 (keys kt*64 + 32g ..), query-tile parity qp = w >> 1; the
+// waves loop over the query tiles that can see their keys, two tiles (Q, dO, lse, D) per step.
 //   S = Q K^T, P = exp2(S*c - lse2), dP = dO V^T, dS = P (dP - D)      (query rows x own keys)
 //   dV^T += dO^T P,  dK^T += Q^T dS                                     (transposing reads)
 // ---------------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(ATT_NT) void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s,
-                                                               int heads_t, const bf16* __restrict__ dO, int ld_do,
-                                                               const float* __restrict__ lse,
-                                                               const float* __restrict__ Dv, float scale_log2,
-                                                               float scale, int causal, bf16* __restrict__ dQKV,
-                                                               int ld_dq) {
-    __shared__ __attribute__((aligned(16))) bf16 Qb[2][ATT_B * D];
-    __shared__ __attribute__((aligned(16))) bf16 Gb[2][ATT_B * D];
-    __shared__ float lse_s[2][ATT_B], D_s[2][ATT_B];
-    const int kt = blockIdx.x, head = blockIdx.y, bi = blockIdx.z;
+__global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(D <= 96 ? 2 : 1)))
+void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int heads_t,
+                          const bf16* __restrict__ dO, int ld_do, const float* __restrict__ lse,
+                          const float* __restrict__ Dv, float scale_log2, float scale, int causal,
+                          bf16* __restrict__ dQKV, int ld_dq) {
+    __shared__ __attribute__((aligned(16))) bf16 smem[4 * ATT_B * D];   // Q tiles [2] | dO tiles [2]
+    __shared__ __attribute__((aligned(16))) bf16 KVs[2 * ATT_B * D];    // the block's keys | values
+    __shared__ float lse_s[2 * ATT_B], D_s[2 * ATT_B];
+    bf16* Qb = smem;
+    bf16* Gb = smem + 2 * ATT_B * D;
+    const int head = blockIdx.x % heads_t, bi = blockIdx.x / heads_t, kt = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int grp = wave & 1, qp = wave >> 1;
     const size_t tok0 = (size_t)bi * s;
     const bf16* Qp = QKV + tok0 * ld + head * D;
     const bf16* Kp = QKV + tok0 * ld + h_t + head * D;
@@ -273,211 +331,244 @@ __global__ __launch_bounds__(ATT_NT) void attn_bwd_dkdv_kernel(const bf16* __res
     const bf16* dOp = dO + tok0 * ld_do + head * D;
     const float* lsep = lse + ((size_t)bi * heads_t + head) * s;
     const float* Dp = Dv + ((size_t)bi * heads_t + head) * s;
-    const int kw0 = kt * ATT_B + wave * 32;
+    const int kw0 = kt * ATT_B + grp * 32;
     const int mykey = kw0 + l32;
 
-    bf16x8 kf[D / 16], vf[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        u32x4 a = u32x4{0, 0, 0, 0}, c = u32x4{0, 0, 0, 0};
-        if (mykey < s) {
-            a = *(const u32x4*)(Kp + (size_t)mykey * ld + ks * 16 + 8 * h);
-            c = *(const u32x4*)(Vp + (size_t)mykey * ld + ks * 16 + 8 * h);
-        }
-        kf[ks] = __builtin_bit_cast(bf16x8, a);
-        vf[ks] = __builtin_bit_cast(bf16x8, c);
-    }
+    const bf16* Ks = KVs;
+    const bf16* Vs = KVs + ATT_B * D;
+    load_tile<D>(Kp, ld, kt * ATT_B, s, KVs, tid);
+    load_tile<D>(Vp, ld, kt * ATT_B, s, KVs + ATT_B * D, tid);
     f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) { dk[dt] = zero16(); dv[dt] = zero16(); }
 
     const int nqt = (s + ATT_B - 1) / ATT_B;
     const int qt0 = causal ? kt : 0;
+    const int niter = (nqt - qt0 + 1) / 2;
     AttTileRegs<D> qr, gr;
     float lse_r = INFINITY, d_r = 0.f;
-    auto fetch = [&](int qt) {
-        const int q0 = qt * ATT_B;
+    auto fetch = [&](int q0) {   // query tiles starting at row q0 (two of them)
         qr.load(Qp, ld, q0, s, tid);
         gr.load(dOp, ld_do, q0, s, tid);
-        if (tid < ATT_B) {
+        if (tid < 2 * ATT_B) {
             int q = q0 + tid;
             lse_r = (q < s) ? lsep[q] * kLog2e : INFINITY;
             d_r = (q < s) ? Dp[q] : 0.f;
         }
     };
-    auto stash = [&](int buf) {
-        qr.store(Qb[buf], tid);
-        gr.store(Gb[buf], tid);
-        if (tid < ATT_B) { lse_s[buf][tid] = lse_r; D_s[buf][tid] = d_r; }
+    auto stash = [&]() {
+        qr.store(Qb, tid);
+        gr.store(Gb, tid);
+        if (tid < 2 * ATT_B) { lse_s[tid] = lse_r; D_s[tid] = d_r; }
     };
-    if (qt0 < nqt) { fetch(qt0); stash(0); }
+    if (niter > 0) { fetch(qt0 * ATT_B); stash(); }
     __syncthreads();
-    for (int qt = qt0; qt < nqt; ++qt) {
-        const int q0 = qt * ATT_B, buf = (qt - qt0) & 1;
-        const bool more = qt + 1 < nqt;
-        if (more) fetch(qt + 1);
-        const bf16* Q = Qb[buf];
-        const bf16* Gt = Gb[buf];
+    for (int it = 0; it < niter; ++it) {
+        const bool more = it + 1 < niter;
+        if (more) fetch((qt0 + 2 * it + 2) * ATT_B);
+        const int qt = qt0 + 2 * it + qp;
+        if (qt < nqt) {
+            const int q0 = qt * ATT_B;
+            const bf16* Q = Qb + qp * ATT_B * D;
+            const bf16* Gt = Gb + qp * ATT_B * D;
+            const float* ls = lse_s + qp * ATT_B;
+            const float* ds_ = D_s + qp * ATT_B;
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int qs0 = q0 + sub * 32;
-            if (causal && qs0 + 31 < kw0) continue;  // every query of this half precedes every key of this wave
-            const bool need_mask = (causal && qs0 < kw0 + 31) || (qs0 + 32 > s) || (kw0 + 32 > s);
-            f32x16 sacc = zero16(), dpacc = zero16();
+            for (int sub = 0; sub < 2; ++sub) {
+                const int qs0 = q0 + sub * 32;
+                if (causal && qs0 + 31 < kw0) continue;  // every query of this half precedes every key of this wave
+                const bool need_mask = (causal && qs0 < kw0 + 31) || (qs0 + 32 > s) || (kw0 + 32 > s);
+                f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(Q, sub * 32, ks * 16, lane), kf[ks], sacc, 0, 0, 0);
-                dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(Gt, sub * 32, ks * 16, lane), vf[ks], dpacc, 0, 0, 0);
-            }
-            f32x16 p, ds;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                int qi = sub * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                float pv = exp2f(fmaf(sacc[v], scale_log2, -lse_s[buf][qi]));
-                if (need_mask) {
-                    int q = q0 + qi;
-                    if ((causal && mykey > q) || mykey >= s) pv = 0.f;
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(Q, sub * 32, ks * 16, lane),
+                                                                   frag_rows<D>(Ks, grp * 32, ks * 16, lane), sacc, 0, 0, 0);
+                    dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(Gt, sub * 32, ks * 16, lane),
+                                                                    frag_rows<D>(Vs, grp * 32, ks * 16, lane), dpacc, 0, 0, 0);
                 }
-                p[v] = pv;
-                ds[v] = pv * (dpacc[v] - D_s[buf][qi]);
-            }
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                bf16x8 pb = pack8(p, 8 * kk), dsb = pack8(ds, 8 * kk);
+                for (int v = 0; v < 16; ++v) {
+                    int qi = sub * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    float pv = exp2f(fmaf(sacc[v], scale_log2, -ls[qi]));
+                    if (need_mask) {
+                        int q = q0 + qi;
+                        if ((causal && mykey > q) || mykey >= s) pv = 0.f;
+                    }
+                    sacc[v] = pv;
+                    dpacc[v] = pv * (dpacc[v] - ds_[qi]);
+                }
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<D>(Gt, sub * 32 + 16 * kk, dt * 32, lane), pb,
-                                                                     dv[dt], 0, 0, 0);
-                    dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<D>(Q, sub * 32 + 16 * kk, dt * 32, lane), dsb,
-                                                                     dk[dt], 0, 0, 0);
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf16x8 pb = pack8(sacc, 8 * kk), dsb = pack8(dpacc, 8 * kk);
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt) {
+                        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<D>(Gt, sub * 32 + 16 * kk, dt * 32, lane),
+                                                                         pb, dv[dt], 0, 0, 0);
+                        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<D>(Q, sub * 32 + 16 * kk, dt * 32, lane),
+                                                                         dsb, dk[dt], 0, 0, 0);
+                    }
                 }
             }
         }
-        if (more) stash(buf ^ 1);
+        __syncthreads();
+        if (more) stash();
         __syncthreads();
     }
-    if (mykey < s) {
-        bf16* kp = dQKV + (tok0 + mykey) * ld_dq + h_t + head * D;
-        bf16* vp = dQKV + (tok0 + mykey) * ld_dq + 2 * h_t + head * D;
+    // merge: odd-parity waves hand dK, dV to the even-parity wave of the same key group
+    constexpr int NV = D;   // dk (D/2) + dv (D/2) per lane
+    float* xch = (float*)smem;
+    static_assert(2 * NV * 64 * 4 <= 4 * ATT_B * D * 2, "exchange exceeds the tile buffers");
+    if (qp == 1) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                xch_put<NV>(xch, grp, dt * 16 + v, lane, dk[dt][v]);
+                xch_put<NV>(xch, grp, D / 2 + dt * 16 + v, lane, dv[dt][v]);
+            }
+    }
+    __syncthreads();
+    if (qp == 0 && mykey < s) {
+        bf16* kp_ = dQKV + (tok0 + mykey) * ld_dq + h_t + head * D;
+        bf16* vp_ = dQKV + (tok0 + mykey) * ld_dq + 2 * h_t + head * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                dk[dt][v] = (dk[dt][v] + xch_get<NV>(xch, grp, dt * 16 + v, lane)) * scale;
+                dv[dt][v] += xch_get<NV>(xch, grp, D / 2 + dt * 16 + v, lane);
+            }
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
                 int d = dt * 32 + 8 * i + 4 * h;
-                *(u32x2*)(kp + d) = u32x2{pack_bf16x2(dk[dt][4 * i] * scale, dk[dt][4 * i + 1] * scale),
-                                          pack_bf16x2(dk[dt][4 * i + 2] * scale, dk[dt][4 * i + 3] * scale)};
-                *(u32x2*)(vp + d) = u32x2{pack_bf16x2(dv[dt][4 * i], dv[dt][4 * i + 1]),
-                                          pack_bf16x2(dv[dt][4 * i + 2], dv[dt][4 * i + 3])};
+                *(u32x2*)(kp_ + d) = u32x2{pack_bf16x2(dk[dt][4 * i], dk[dt][4 * i + 1]),
+                                           pack_bf16x2(dk[dt][4 * i + 2], dk[dt][4 * i + 3])};
+                *(u32x2*)(vp_ + d) = u32x2{pack_bf16x2(dv[dt][4 * i], dv[dt][4 * i + 1]),
+                                           pack_bf16x2(dv[dt][4 * i + 2], dv[dt][4 * i + 3])};
             }
+        }
     }
 }
 
 // ---------------------------------------------------------------------------------------------
-// dQ. grid = (ceil(s/64) query tiles, heads_t, b); heavy tiles first. Wave w owns 32 queries and
-// loops over the key tiles they can see; K and V tiles are double-buffered.
+// dQ. grid = (b * heads_t, query tiles), qt = last - blockIdx.y (heavy first). Wave w: row group
+// g = w & 1 (32 queries), key-tile parity kp = w >> 1; K and V tiles two per step.
 //   S^T = K Q^T, P^T = exp2(S^T*c - lse2), dP^T = V dO^T, dS^T = P^T (dP^T - D); dQ^T += K^T dS^T
 // ---------------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(ATT_NT) void attn_bwd_dq_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s,
-                                                             int heads_t, const bf16* __restrict__ dO, int ld_do,
-                                                             const float* __restrict__ lse,
-                                                             const float* __restrict__ Dv, float scale_log2,
-                                                             float scale, int causal, bf16* __restrict__ dQKV,
-                                                             int ld_dq) {
-    __shared__ __attribute__((aligned(16))) bf16 Kb[2][ATT_B * D];
-    __shared__ __attribute__((aligned(16))) bf16 Vb[2][ATT_B * D];
-    const int qt = gridDim.x - 1 - blockIdx.x, head = blockIdx.y, bi = blockIdx.z;
+__global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(D <= 96 ? 2 : 1)))
+void attn_bwd_dq_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int heads_t,
+                        const bf16* __restrict__ dO, int ld_do, const float* __restrict__ lse,
+                        const float* __restrict__ Dv, float scale_log2, float scale, int causal,
+                        bf16* __restrict__ dQKV, int ld_dq) {
+    __shared__ __attribute__((aligned(16))) bf16 smem[4 * ATT_B * D];   // K tiles [2] | V tiles [2]
+    __shared__ __attribute__((aligned(16))) bf16 QGs[2 * ATT_B * D];    // the block's queries | their dO
+    bf16* Kb = smem;
+    bf16* Vb = smem + 2 * ATT_B * D;
+    const int head = blockIdx.x % heads_t, bi = blockIdx.x / heads_t, qt = gridDim.y - 1 - blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int grp = wave & 1, kp = wave >> 1;
     const size_t tok0 = (size_t)bi * s;
     const bf16* Qp = QKV + tok0 * ld + head * D;
     const bf16* Kp = QKV + tok0 * ld + h_t + head * D;
     const bf16* Vp = QKV + tok0 * ld + 2 * h_t + head * D;
     const bf16* dOp = dO + tok0 * ld_do + head * D;
-    const int q0w = qt * ATT_B + wave * 32;
+    const bf16* Qs = QGs;
+    const bf16* Gs = QGs + ATT_B * D;
+    const int q0w = qt * ATT_B + grp * 32;
     const int myq = q0w + l32;
     const float lse2 = (myq < s) ? lse[((size_t)bi * heads_t + head) * s + myq] * kLog2e : INFINITY;
     const float Dq = (myq < s) ? Dv[((size_t)bi * heads_t + head) * s + myq] : 0.f;
 
-    bf16x8 qf[D / 16], gf[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        u32x4 a = u32x4{0, 0, 0, 0}, c = u32x4{0, 0, 0, 0};
-        if (myq < s) {
-            a = *(const u32x4*)(Qp + (size_t)myq * ld + ks * 16 + 8 * h);
-            c = *(const u32x4*)(dOp + (size_t)myq * ld_do + ks * 16 + 8 * h);
-        }
-        qf[ks] = __builtin_bit_cast(bf16x8, a);
-        gf[ks] = __builtin_bit_cast(bf16x8, c);
-    }
+    load_tile<D>(Qp, ld, qt * ATT_B, s, QGs, tid);
+    load_tile<D>(dOp, ld_do, qt * ATT_B, s, QGs + ATT_B * D, tid);
     f32x16 dq[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) dq[dt] = zero16();
 
     const int kv_end = causal ? min(s, (qt + 1) * ATT_B) : s;
     const int ntiles = (kv_end + ATT_B - 1) / ATT_B;
+    const int niter = (ntiles + 1) / 2;
     AttTileRegs<D> kr, vr;
-    if (ntiles > 0) {
+    if (niter > 0) {
         kr.load(Kp, ld, 0, s, tid);
         vr.load(Vp, ld, 0, s, tid);
-        kr.store(Kb[0], tid);
-        vr.store(Vb[0], tid);
+        kr.store(Kb, tid);
+        vr.store(Vb, tid);
     }
     __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int k0 = kt * ATT_B, buf = kt & 1;
-        const bool more = kt + 1 < ntiles;
+    for (int it = 0; it < niter; ++it) {
+        const bool more = it + 1 < niter;
         if (more) {
-            kr.load(Kp, ld, k0 + ATT_B, s, tid);
-            vr.load(Vp, ld, k0 + ATT_B, s, tid);
+            kr.load(Kp, ld, (it + 1) * 2 * ATT_B, s, tid);
+            vr.load(Vp, ld, (it + 1) * 2 * ATT_B, s, tid);
         }
-        const bf16* K = Kb[buf];
-        const bf16* V = Vb[buf];
+        const int kt = 2 * it + kp, k0 = kt * ATT_B;
+        if (kt < ntiles) {
+            const bf16* K = Kb + kp * ATT_B * D;
+            const bf16* V = Vb + kp * ATT_B * D;
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int ks0 = k0 + sub * 32;
-            if (causal && ks0 > q0w + 31) continue;
-            const bool need_mask = (causal && ks0 + 31 > q0w) || (ks0 + 32 > s);
-            f32x16 sacc = zero16(), dpacc = zero16();
+            for (int sub = 0; sub < 2; ++sub) {
+                const int ks0 = k0 + sub * 32;
+                if (causal && ks0 > q0w + 31) continue;
+                const bool need_mask = (causal && ks0 + 31 > q0w) || (ks0 + 32 > s);
+                f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(K, sub * 32, ks * 16, lane), qf[ks], sacc, 0, 0, 0);
-                dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(V, sub * 32, ks * 16, lane), gf[ks], dpacc, 0, 0, 0);
-            }
-            f32x16 ds;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                float pv = exp2f(fmaf(sacc[v], scale_log2, -lse2));
-                if (need_mask) {
-                    int key = ks0 + 8 * (v >> 2) + 4 * h + (v & 3);
-                    if ((causal && key > myq) || key >= s) pv = 0.f;
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(K, sub * 32, ks * 16, lane),
+                                                                   frag_rows<D>(Qs, grp * 32, ks * 16, lane), sacc, 0, 0, 0);
+                    dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(V, sub * 32, ks * 16, lane),
+                                                                    frag_rows<D>(Gs, grp * 32, ks * 16, lane), dpacc, 0, 0, 0);
                 }
-                ds[v] = pv * (dpacc[v] - Dq);
-            }
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                bf16x8 dsb = pack8(ds, 8 * kk);
+                for (int v = 0; v < 16; ++v) {
+                    float pv = exp2f(fmaf(sacc[v], scale_log2, -lse2));
+                    if (need_mask) {
+                        int key = ks0 + 8 * (v >> 2) + 4 * h + (v & 3);
+                        if ((causal && key > myq) || key >= s) pv = 0.f;
+                    }
+                    dpacc[v] = pv * (dpacc[v] - Dq);
+                }
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-                    dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<D>(K, sub * 32 + 16 * kk, dt * 32, lane), dsb,
-                                                                     dq[dt], 0, 0, 0);
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf16x8 dsb = pack8(dpacc, 8 * kk);
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt)
+                        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<D>(K, sub * 32 + 16 * kk, dt * 32, lane),
+                                                                         dsb, dq[dt], 0, 0, 0);
+                }
             }
         }
+        __syncthreads();
         if (more) {
-            kr.store(Kb[buf ^ 1], tid);
-            vr.store(Vb[buf ^ 1], tid);
+            kr.store(Kb, tid);
+            vr.store(Vb, tid);
         }
         __syncthreads();
     }
-    if (myq < s) {
-        bf16* qp = dQKV + (tok0 + myq) * ld_dq + head * D;
+    constexpr int NV = D / 2;
+    float* xch = (float*)smem;
+    static_assert(2 * NV * 64 * 4 <= 4 * ATT_B * D * 2, "exchange exceeds the tile buffers");
+    if (kp == 1) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
+            for (int v = 0; v < 16; ++v) xch_put<NV>(xch, grp, dt * 16 + v, lane, dq[dt][v]);
+    }
+    __syncthreads();
+    if (kp == 0 && myq < s) {
+        bf16* qp_ = dQKV + (tok0 + myq) * ld_dq + head * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dq[dt][v] = (dq[dt][v] + xch_get<NV>(xch, grp, dt * 16 + v, lane)) * scale;
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
                 int d = dt * 32 + 8 * i + 4 * h;
-                *(u32x2*)(qp + d) = u32x2{pack_bf16x2(dq[dt][4 * i] * scale, dq[dt][4 * i + 1] * scale),
-                                          pack_bf16x2(dq[dt][4 * i + 2] * scale, dq[dt][4 * i + 3] * scale)};
+                *(u32x2*)(qp_ + d) = u32x2{pack_bf16x2(dq[dt][4 * i], dq[dt][4 * i + 1]),
+                                           pack_bf16x2(dq[dt][4 * i + 2], dq[dt][4 * i + 3])};
             }
+        }
     }
 }
 

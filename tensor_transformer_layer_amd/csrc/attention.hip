@@ -8,7 +8,7 @@ namespace tp {
 template <int D>
 static hipError_t fwd_d(int b, int s, int h_t, int heads_t, int causal, const void* QKV, void* O, float* lse,
                         hipStream_t st) {
-    dim3 grid((s + ATT_B - 1) / ATT_B, heads_t, b);
+    dim3 grid(b * heads_t, (s + ATT_B - 1) / ATT_B);
     float scale_log2 = kLog2e / sqrtf((float)D);
     hipLaunchKernelGGL((attn_fwd_kernel<D>), grid, dim3(ATT_NT), 0, st, (const bf16*)QKV, 3 * h_t, h_t, s, heads_t,
                        scale_log2, causal, (bf16*)O, h_t, lse);
@@ -23,7 +23,7 @@ static hipError_t bwd_d(int b, int s, int h_t, int heads_t, int causal, const vo
                        (const bf16*)dO, (const bf16*)O, h_t, b, s, heads_t, Dws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((s + ATT_B - 1) / ATT_B, heads_t, b);
+    dim3 grid(b * heads_t, (s + ATT_B - 1) / ATT_B);
     float scale = 1.0f / sqrtf((float)D);
     float scale_log2 = kLog2e * scale;
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), grid, dim3(ATT_NT), 0, st, (const bf16*)QKV, 3 * h_t, h_t, s,

@@ -67,9 +67,11 @@ hipError_t xent_combine(int N, int t, const float* const* mx, const float* const
 int ln_bwd_blocks(int rows);
 hipError_t layernorm_fwd(int dt, int rows, int h, float eps, const void* x, const void* g, const void* b, void* y,
                          float* mean, float* rstd, hipStream_t st);
+// dres_sum / dx_sum: optional column sums of dres and of dx (the bias gradients of the row-parallel
+// layers on either side of the residual branch)
 hipError_t layernorm_bwd(int dt, int rows, int h, const void* x, const void* g, const float* mean,
                          const float* rstd, const void* dy, const void* dres, void* dx, void* dg, void* db,
-                         int accumulate, float* ws, hipStream_t st);
+                         void* dres_sum, void* dx_sum, int accumulate, float* ws, hipStream_t st);
 int colsum_row_blocks(int rows);
 hipError_t colsum(int dt, int rows, int n, const void* G, void* out, int accumulate, float* ws, hipStream_t st);
 hipError_t sum_partials(int in_dt, int out_dt, size_t rows, int cols, int t, const void* const* parts,

@@ -12,6 +12,42 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+constexpr int LN_MAX_H = 8192;
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+    u32x4 v;
+    __device__ __forceinline__ void load(const bf16* p) { v = *(const u32x4*)p; }
+    __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ float operator[](int e) const {
+        uint32_t w = v[e >> 1];
+        return __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+template <> struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) { a = *(const f32x4*)p; b = *(const f32x4*)(p + 4); }
+    __device__ __forceinline__ void zero() { a = f32x4{0.f, 0.f, 0.f, 0.f}; b = a; }
+    __device__ __forceinline__ float operator[](int e) const { return e < 4 ? a[e] : b[e - 4]; }
+};
+
+// Sums NV per-thread values over the block: returns the totals in v (every thread).
+template <int NV>
+__device__ __forceinline__ void block_sum(float (&v)[NV], float (*red)[NV], int lane, int wave, int nw) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] = wave_sum(v[k]);
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) red[wave][k] = v[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        float a = red[0][k];
+        for (int w = 1; w < nw; ++w) a += red[w][k];
+        v[k] = a;
+    }
+}
+
 // ---------------------------------------------------------------------------------------------
 // LayerNorm forward: one wave per row, the row held in registers (C chunks of 8 per lane).
 // ---------------------------------------------------------------------------------------------
@@ -65,145 +101,161 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int h, float eps,
 }
 
 // ---------------------------------------------------------------------------------------------
-// LayerNorm backward. Block b handles rows b*4 + w + k*(4*nblocks) (wave w). dx is written per
-// row; dgamma/dbeta partials are accumulated per lane, merged over the block's waves in wave
-// order through LDS, and written as one row per block into part[b][h] (reduced afterwards).
-// The row's x and dy stay in registers in their storage type (packed bf16) between the two passes.
+// LayerNorm backward: a block of ceil(h/512)*64 threads spans a row, 8 columns per thread
+// (h <= 8192), and takes RPI rows per iteration, fetched together (x, dy and dres of RPI rows in
+// flight per block). Row sums are wave butterflies followed by a sum over the block's waves in
+// wave order through LDS (double-buffered: one barrier per iteration). Block b takes rows
+// b*RPI + j + k*(RPI*nblocks); NTMAX bounds the block size, which sets the register budget.
+// dx is written per row; each thread accumulates, for its 8 columns over the block's rows, the
+// column sums wanted (dgamma, dbeta, and the plain sums of dres and of dx) and writes them as row
+// b of part_* [nblocks][h] (NULL: not wanted); they are reduced afterwards.
 // ---------------------------------------------------------------------------------------------
-template <typename T> struct Raw8;
-template <> struct Raw8<bf16> {
-    u32x4 v;
-    __device__ __forceinline__ void load(const bf16* p) { v = *(const u32x4*)p; }
-    __device__ __forceinline__ float operator[](int e) const {
-        uint32_t w = v[e >> 1];
-        return __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
-    }
-};
-template <> struct Raw8<float> {
-    f32x4 a, b;
-    __device__ __forceinline__ void load(const float* p) { a = *(const f32x4*)p; b = *(const f32x4*)(p + 4); }
-    __device__ __forceinline__ float operator[](int e) const { return e < 4 ? a[e] : b[e - 4]; }
-};
-
-template <typename T, int C>
-__global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int h, const T* __restrict__ x,
-                                                     const T* __restrict__ gamma, const float* __restrict__ mean,
-                                                     const float* __restrict__ rstd, const T* __restrict__ dy,
-                                                     const T* __restrict__ dres, T* __restrict__ dx,
-                                                     float* __restrict__ part_g, float* __restrict__ part_b) {
-    extern __shared__ float lds[];   // [2][h]
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float pg[C][8], pb[C][8];
-#pragma unroll
-    for (int k = 0; k < C; ++k)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { pg[k][e] = 0.f; pb[k][e] = 0.f; }
+template <typename T, int NTMAX, int RPI>
+__global__ __launch_bounds__(NTMAX) void ln_bwd_kernel(int rows, int h, const T* __restrict__ x,
+                                                      const T* __restrict__ gamma, const float* __restrict__ mean,
+                                                      const float* __restrict__ rstd, const T* __restrict__ dy,
+                                                      const T* __restrict__ dres, T* __restrict__ dx,
+                                                      float* __restrict__ part_g, float* __restrict__ part_b,
+                                                      float* __restrict__ part_r, float* __restrict__ part_x) {
+    __shared__ float red[2][16][2 * RPI];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int c = tid * 8;
+    const bool act = c < h;
     const float inv_h = 1.0f / (float)h;
-    for (int row = blockIdx.x * 4 + wave; row < rows; row += 4 * gridDim.x) {
-        const float mu = mean[row], rs = rstd[row];
-        Raw8<T> xr[C], dr[C];
-        float s1 = 0.f, s2 = 0.f;
+    Raw8<T> gm;
+    if (act) gm.load(gamma + c);
+    else gm.zero();
+    float pg[8], pb[8], pr[8], px[8];
 #pragma unroll
-        for (int k = 0; k < C; ++k) {
-            int c = (lane + 64 * k) * 8;
-            if (c < h) {
-                xr[k].load(x + (size_t)row * h + c);
-                dr[k].load(dy + (size_t)row * h + c);
-                float gm[8];
-                load8(gamma + c, gm);
+    for (int e = 0; e < 8; ++e) { pg[e] = 0.f; pb[e] = 0.f; pr[e] = 0.f; px[e] = 0.f; }
+    int it = 0;
+    for (int r0 = blockIdx.x * RPI; r0 < rows; r0 += RPI * gridDim.x, ++it) {
+        Raw8<T> xr[RPI], dr[RPI], rr[RPI];
+        float mu[RPI], rs[RPI];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float xh = (xr[k][e] - mu) * rs, d = dr[k][e];
-                    float g = d * gm[e];
-                    s1 += g;
-                    s2 += g * xh;
-                    pg[k][e] += d * xh;
-                    pb[k][e] += d;
-                }
+        for (int j = 0; j < RPI; ++j) {
+            const int row = r0 + j;
+            const size_t ro = (size_t)row * h + c;
+            if (act && row < rows) {
+                xr[j].load(x + ro);
+                dr[j].load(dy + ro);
+                if (dres) rr[j].load(dres + ro);
+                else rr[j].zero();
+            } else {
+                xr[j].zero(); dr[j].zero(); rr[j].zero();
             }
+            mu[j] = row < rows ? mean[row] : 0.f;
+            rs[j] = row < rows ? rstd[row] : 0.f;
         }
-        s1 = wave_sum(s1) * inv_h;
-        s2 = wave_sum(s2) * inv_h;
+        float s[2 * RPI];
 #pragma unroll
-        for (int k = 0; k < C; ++k) {
-            int c = (lane + 64 * k) * 8;
-            if (c < h) {
-                float o[8], rr[8], gm[8];
-                load8(gamma + c, gm);
-                if (dres) load8(dres + (size_t)row * h + c, rr);
+        for (int j = 0; j < RPI; ++j) {
+            float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float xh = (xr[j][e] - mu[j]) * rs[j], d = dr[j][e];
+                float g = d * gm[e];
+                s1 += g;
+                s2 += g * xh;
+                pg[e] += d * xh;
+                pb[e] += d;
+            }
+            s[2 * j] = s1;
+            s[2 * j + 1] = s2;
+        }
+        block_sum<2 * RPI>(s, red[it & 1], lane, wave, nw);
+#pragma unroll
+        for (int j = 0; j < RPI; ++j) {
+            const int row = r0 + j;
+            if (act && row < rows) {
+                const float s1 = s[2 * j] * inv_h, s2 = s[2 * j + 1] * inv_h;
+                float o[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    float xh = (xr[k][e] - mu) * rs;
-                    o[e] = rs * (dr[k][e] * gm[e] - s1 - xh * s2);
-                    if (dres) o[e] += rr[e];
+                    float xh = (xr[j][e] - mu[j]) * rs[j];
+                    o[e] = rs[j] * (dr[j][e] * gm[e] - s1 - xh * s2) + rr[j][e];
+                    pr[e] += rr[j][e];
+                    px[e] += o[e];
                 }
                 store8(dx + (size_t)row * h + c, o);
             }
         }
     }
-    if (!part_g) return;   // uniform across the block
-    for (int w = 0; w < 4; ++w) {
-        if (wave == w) {
-#pragma unroll
-            for (int k = 0; k < C; ++k) {
-                int c = (lane + 64 * k) * 8;
-                if (c < h) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        if (w == 0) { lds[c + e] = pg[k][e]; lds[h + c + e] = pb[k][e]; }
-                        else { lds[c + e] += pg[k][e]; lds[h + c + e] += pb[k][e]; }
-                    }
-                }
-            }
-        }
-        __syncthreads();
-    }
-    for (int c = threadIdx.x; c < h; c += 256) {
-        part_g[(size_t)blockIdx.x * h + c] = lds[c];
-        part_b[(size_t)blockIdx.x * h + c] = lds[h + c];
-    }
+    if (!act) return;
+    const size_t po = (size_t)blockIdx.x * h + c;
+    if (part_g) store8(part_g + po, pg);
+    if (part_b) store8(part_b + po, pb);
+    if (part_r) store8(part_r + po, pr);
+    if (part_x) store8(part_x + po, px);
 }
 
-// out[c] (+)= sum_{b=0}^{nb-1} part[b][c]. Block = 64 columns x 4 row phases: phase p sums rows
-// p, p+4, ... in order, then the four phase sums are added in phase order.
+// out_j[c] (+)= sum_{b=0}^{nb-1} part_j[b][c] for job j = blockIdx.y (n % 4 == 0). Block = 16
+// columns (4 per thread) x 64 row phases: phase p sums rows p, p+64, ... in order, then the 64
+// phase sums are added in a fixed pairwise tree.
+constexpr int RR_COLS = 16;
+constexpr int RR_JOBS = 4;
+struct RowSumJobs { const float* part[RR_JOBS]; void* out[RR_JOBS]; };
 template <typename T>
-__global__ __launch_bounds__(256) void reduce_rows_kernel(const float* __restrict__ part, int nb, int n,
-                                                          T* __restrict__ out, int accumulate) {
-    __shared__ float red[4][64];
-    const int cl = threadIdx.x & 63, ph = threadIdx.x >> 6;
-    const int c = blockIdx.x * 64 + cl;
-    float a = 0.f;
+__global__ __launch_bounds__(256) void reduce_rows_kernel(RowSumJobs jobs, int nb, int n, int accumulate) {
+    __shared__ f32x4 red[64][4];
+    const float* __restrict__ part = jobs.part[blockIdx.y];
+    T* __restrict__ out = (T*)jobs.out[blockIdx.y];
+    const int cg = threadIdx.x & 3, ph = threadIdx.x >> 2;
+    const int c = blockIdx.x * RR_COLS + cg * 4;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
     if (c < n) {
 #pragma unroll 8
-        for (int b = ph; b < nb; b += 4) a += part[(size_t)b * n + c];
+        for (int b = ph; b < nb; b += 64) a += *(const f32x4*)(part + (size_t)b * n + c);
     }
-    red[ph][cl] = a;
+    red[ph][cg] = a;
     __syncthreads();
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) {
+        if (ph < s) red[ph][cg] += red[ph + s][cg];
+        __syncthreads();
+    }
     if (ph == 0 && c < n) {
-        a = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
-        if (accumulate) a += to_f32(out[c]);
-        out[c] = from_f32<T>(a);
+        f32x4 r = red[0][cg];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = r[e];
+            if (accumulate) v += to_f32(out[c + e]);
+            out[c + e] = from_f32<T>(v);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------------------------
-// Column sums of G [rows, n]: grid (ceil(n/8/64), RB), 64 threads; a thread owns 8 columns and
-// rows y, y + RB, ...; partial row y goes to part[y][n].
+// Column partial sums of G [rows, n] (n % 8 == 0): grid (ceil(n/512), RB), 256 threads. Lane owns
+// 8 columns; block y covers the row range [y*rpb, (y+1)*rpb), wave w its rows w, w+4, ...; the
+// four wave sums are added in wave order and written as part[y][n].
 // ---------------------------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(64) void colsum_partial_kernel(int rows, int n, const T* __restrict__ G,
+__global__ __launch_bounds__(256) void colsum_partial_kernel(int rows, int n, int rpb, const T* __restrict__ G,
                                                             float* __restrict__ part) {
-    int c = (blockIdx.x * 64 + threadIdx.x) * 8;
-    if (c >= n) return;
+    __shared__ float red[4][512];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = (blockIdx.x * 64 + lane) * 8;
+    const int r0 = blockIdx.y * rpb, r1 = min(rows, r0 + rpb);
     float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 16
-    for (int r = blockIdx.y; r < rows; r += gridDim.y) {
-        float v[8];
-        load8(G + (size_t)r * n + c, v);
+    if (c < n) {
+#pragma unroll 8
+        for (int r = r0 + wave; r < r1; r += 4) {
+            float v[8];
+            load8(G + (size_t)r * n + c, v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] += v[e];
+            for (int e = 0; e < 8; ++e) a[e] += v[e];
+        }
     }
-    store8(part + (size_t)blockIdx.y * n + c, a);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave][lane * 8 + e] = a[e];
+    __syncthreads();
+    if (wave == 0 && c < n) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            a[e] = ((red[0][lane * 8 + e] + red[1][lane * 8 + e]) + red[2][lane * 8 + e]) + red[3][lane * 8 + e];
+        store8(part + (size_t)blockIdx.y * n + c, a);
+    }
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -41,77 +41,83 @@ hipError_t layernorm_fwd(int dt, int rows, int h, float eps, const void* x, cons
                    : ln_fwd_t<float>(rows, h, eps, x, g, b, y, mean, rstd, st);
 }
 
+// threads of a LayerNorm backward block: 8 columns each, whole waves
+static int ln_threads(int h) { return (h + 511) / 512 * 64; }
+
+// Blocks of the LayerNorm backward: at least eight rows each, at most 512 (partial rows).
 int ln_bwd_blocks(int rows) {
     int nb = (rows + 7) / 8;
-    return nb < 512 ? nb : 512;
+    return nb < 512 ? (nb > 0 ? nb : 1) : 512;
+}
+
+// out_j (+)= column sums of part_j [nb][n] for the non-null outputs (nb may be 0: zeros)
+template <typename T>
+static hipError_t reduce_rows(const float* const* parts, void* const* outs, int nb, int n, int accumulate,
+                              hipStream_t st) {
+    RowSumJobs jobs;
+    int nj = 0;
+    for (int j = 0; j < RR_JOBS; ++j)
+        if (outs[j]) { jobs.part[nj] = parts[j]; jobs.out[nj] = outs[j]; ++nj; }
+    if (nj == 0) return hipSuccess;
+    hipLaunchKernelGGL((reduce_rows_kernel<T>), dim3((n + RR_COLS - 1) / RR_COLS, nj), dim3(256), 0, st, jobs, nb, n,
+                       accumulate);
+    return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t ln_bwd_t(int rows, int h, const void* x, const void* g, const float* mean, const float* rstd,
-                           const void* dy, const void* dres, void* dx, void* dg, void* db, int accumulate, float* ws,
-                           hipStream_t st) {
-    int nb = ln_bwd_blocks(rows);
-    bool params = dg != nullptr || db != nullptr;
-    float* pg = params ? ws : nullptr;
-    float* pb = params ? ws + (size_t)nb * h : nullptr;
-    size_t lds = params ? 2 * (size_t)h * sizeof(float) : 0;
-#define LNB(C) hipLaunchKernelGGL((ln_bwd_kernel<T, C>), dim3(nb), dim3(256), lds, st, rows, h, (const T*)x, \
-                                  (const T*)g, mean, rstd, (const T*)dy, (const T*)dres, (T*)dx, pg, pb)
-    switch (ln_chunks(h)) {
-        case 1: LNB(1); break;
-        case 2: LNB(2); break;
-        case 3: LNB(3); break;
-        case 4: LNB(4); break;
-        case 6: LNB(6); break;
-        case 8: LNB(8); break;
-        case 12: LNB(12); break;
-        case 16: LNB(16); break;
-        default: return hipErrorInvalidValue;
+                           const void* dy, const void* dres, void* dx, void* dg, void* db, void* dsr, void* dsx,
+                           int accumulate, float* ws, hipStream_t st) {
+    if (h <= 0 || h > LN_MAX_H) return hipErrorInvalidValue;
+    const int nb = rows > 0 ? ln_bwd_blocks(rows) : 0;
+    void* outs[RR_JOBS] = {dg, db, dsr, dsx};
+    float* parts[RR_JOBS];
+    for (int j = 0; j < RR_JOBS; ++j) parts[j] = outs[j] ? ws + (size_t)j * ln_bwd_blocks(rows) * h : nullptr;
+    if (rows > 0) {
+        // two rows per iteration (measured faster than one or four at h = 3072)
+        const int nt = ln_threads(h);
+        if (nt <= 512)
+            hipLaunchKernelGGL((ln_bwd_kernel<T, 512, 2>), dim3(nb), dim3(nt), 0, st, rows, h, (const T*)x, (const T*)g,
+                               mean, rstd, (const T*)dy, (const T*)dres, (T*)dx, parts[0], parts[1], parts[2], parts[3]);
+        else
+            hipLaunchKernelGGL((ln_bwd_kernel<T, 1024, 2>), dim3(nb), dim3(nt), 0, st, rows, h, (const T*)x, (const T*)g,
+                               mean, rstd, (const T*)dy, (const T*)dres, (T*)dx, parts[0], parts[1], parts[2], parts[3]);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-#undef LNB
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !params) return e;
-    dim3 rg((h + 63) / 64);
-    if (dg) hipLaunchKernelGGL((reduce_rows_kernel<T>), rg, dim3(256), 0, st, (const float*)pg, nb, h, (T*)dg, accumulate);
-    if (db) hipLaunchKernelGGL((reduce_rows_kernel<T>), rg, dim3(256), 0, st, (const float*)pb, nb, h, (T*)db, accumulate);
-    return hipGetLastError();
+    // no rows: a zero-row reduction writes zero gradients (unchanged when accumulating)
+    return reduce_rows<T>(parts, outs, nb, h, accumulate, st);
 }
 
 hipError_t layernorm_bwd(int dt, int rows, int h, const void* x, const void* g, const float* mean,
                          const float* rstd, const void* dy, const void* dres, void* dx, void* dg, void* db,
-                         int accumulate, float* ws, hipStream_t st) {
-    if (rows == 0) {
-        // no rows: parameter gradients are zero (unchanged when accumulating); a zero-block reduction writes them
-        dim3 rg((h + 63) / 64);
-        if (dt == 1) {
-            if (dg) hipLaunchKernelGGL((reduce_rows_kernel<bf16>), rg, dim3(256), 0, st, (const float*)ws, 0, h, (bf16*)dg, accumulate);
-            if (db) hipLaunchKernelGGL((reduce_rows_kernel<bf16>), rg, dim3(256), 0, st, (const float*)ws, 0, h, (bf16*)db, accumulate);
-        } else {
-            if (dg) hipLaunchKernelGGL((reduce_rows_kernel<float>), rg, dim3(256), 0, st, (const float*)ws, 0, h, (float*)dg, accumulate);
-            if (db) hipLaunchKernelGGL((reduce_rows_kernel<float>), rg, dim3(256), 0, st, (const float*)ws, 0, h, (float*)db, accumulate);
-        }
-        return hipGetLastError();
-    }
-    return dt == 1 ? ln_bwd_t<bf16>(rows, h, x, g, mean, rstd, dy, dres, dx, dg, db, accumulate, ws, st)
-                   : ln_bwd_t<float>(rows, h, x, g, mean, rstd, dy, dres, dx, dg, db, accumulate, ws, st);
+                         void* dres_sum, void* dx_sum, int accumulate, float* ws, hipStream_t st) {
+    return dt == 1 ? ln_bwd_t<bf16>(rows, h, x, g, mean, rstd, dy, dres, dx, dg, db, dres_sum, dx_sum, accumulate, ws, st)
+                   : ln_bwd_t<float>(rows, h, x, g, mean, rstd, dy, dres, dx, dg, db, dres_sum, dx_sum, accumulate, ws, st);
 }
 
-int colsum_row_blocks(int rows) { return rows < 512 ? (rows > 0 ? rows : 1) : 512; }
+// Row blocks of the column-sum pass: about 64 rows each, at most 128 blocks.
+int colsum_row_blocks(int rows) {
+    if (rows <= 0) return 1;
+    int rb = (rows + 63) / 64;
+    return rb < 128 ? rb : 128;
+}
 
 hipError_t colsum(int dt, int rows, int n, const void* G, void* out, int accumulate, float* ws, hipStream_t st) {
     int rb = colsum_row_blocks(rows);
     if (rows > 0) {
+        int rpb = (rows + rb - 1) / rb;
         dim3 grid((n / 8 + 63) / 64, rb);
-        if (dt == 1) hipLaunchKernelGGL((colsum_partial_kernel<bf16>), grid, dim3(64), 0, st, rows, n, (const bf16*)G, ws);
-        else hipLaunchKernelGGL((colsum_partial_kernel<float>), grid, dim3(64), 0, st, rows, n, (const float*)G, ws);
+        if (dt == 1) hipLaunchKernelGGL((colsum_partial_kernel<bf16>), grid, dim3(256), 0, st, rows, n, rpb, (const bf16*)G, ws);
+        else hipLaunchKernelGGL((colsum_partial_kernel<float>), grid, dim3(256), 0, st, rows, n, rpb, (const float*)G, ws);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     int nb = rows > 0 ? rb : 0;
-    dim3 rg((n + 63) / 64);
-    if (dt == 1) hipLaunchKernelGGL((reduce_rows_kernel<bf16>), rg, dim3(256), 0, st, (const float*)ws, nb, n, (bf16*)out, accumulate);
-    else hipLaunchKernelGGL((reduce_rows_kernel<float>), rg, dim3(256), 0, st, (const float*)ws, nb, n, (float*)out, accumulate);
-    return hipGetLastError();
+    const float* parts[RR_JOBS] = {ws, nullptr, nullptr, nullptr};
+    void* outs[RR_JOBS] = {out, nullptr, nullptr, nullptr};
+    return dt == 1 ? reduce_rows<bf16>(parts, outs, nb, n, accumulate, st)
+                   : reduce_rows<float>(parts, outs, nb, n, accumulate, st);
 }
 
 hipError_t sum_partials(int in_dt, int out_dt, size_t rows, int cols, int t, const void* const* parts,

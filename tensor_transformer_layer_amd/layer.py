@@ -7,9 +7,9 @@ digest, §3.4, f and g operators):
     forward   xn1 = LN1(x); Z_attn_r = Attn_r(xn1)          [g: x1 = sum_r Z_attn_r + bo + x]
               xn2 = LN2(x1); Z_mlp_r = MLP_r(xn2)           [g: x2 = sum_r Z_mlp_r + b2 + x1]
     backward  dXn2_r, dA_r, dB_r, db1_r = MLP_r^T(G)        [f: dXn2 = sum_r dXn2_r]
-              dx1 = G + LN2^T(dXn2);  db2 = colsum(G)
+              dx1 = G + LN2^T(dXn2);  db2 = colsum(G), dbo = colsum(dx1) (same pass)
               dXn1_r, dWqkv_r, dbqkv_r, dWo_r = Attn_r^T(dx1)  [f: dXn1 = sum_r dXn1_r]
-              dx = dx1 + LN1^T(dXn1); dbo = colsum(dx1)
+              dx = dx1 + LN1^T(dXn1)
 
 The sums in brackets are the all-reduces of a multi-GPU run. Each stage method takes the summed
 tensor it needs as an argument, so a caller can run all t ranks on one device and sum their
@@ -18,8 +18,8 @@ Only torch.empty is used here (device allocation); every computation is a librar
 """
 import torch
 
-from . import (TP_BF16, tp_attn_shard_bwd, tp_attn_shard_bwd_workspace, tp_attn_shard_fwd, tp_colsum,
-               tp_colsum_workspace, tp_layernorm_bwd, tp_layernorm_bwd_workspace, tp_layernorm_fwd,
+from . import (TP_BF16, tp_attn_shard_bwd, tp_attn_shard_bwd_workspace, tp_attn_shard_fwd,
+               tp_layernorm_bwd, tp_layernorm_bwd_workspace, tp_layernorm_fwd,
                tp_mlp_shard_bwd, tp_mlp_shard_bwd_workspace, tp_mlp_shard_fwd, tp_sum_partials)
 
 EPS = 1e-5
@@ -55,7 +55,7 @@ class LayerShard:
         self.dln1_g, self.dln1_b = e((h,), **bf), e((h,), **bf)
         self.ws_bytes = max(tp_mlp_shard_bwd_workspace(T, h, ffn, t, TP_BF16),
                             tp_attn_shard_bwd_workspace(b, s, h, heads, t, TP_BF16),
-                            tp_layernorm_bwd_workspace(T, h, TP_BF16), tp_colsum_workspace(T, h, TP_BF16))
+                            tp_layernorm_bwd_workspace(T, h, TP_BF16))
         self.ws = e((self.ws_bytes,), dtype=torch.uint8, device=device)
 
     # ---- forward stages ---------------------------------------------------------------------
@@ -84,12 +84,12 @@ class LayerShard:
         p, T, h = self.p, self.T, self.h
         tp_mlp_shard_bwd(T, h, self.ffn, self.t, self.r, TP_BF16, self.xn2, p["A_r"], p["B_r"], self.U, self.Y, G,
                          self.dXn2, self.dA, self.db1, self.dB, 0, self.ws, self.ws_bytes)
-        tp_colsum(T, h, TP_BF16, G, self.db2, 0, self.ws, self.ws_bytes)
         return self.dXn2
 
     def ln2_bwd(self, dxn2_sum, G):
+        """dx1 = G + LN2^T(dXn2), with db2 = colsum(G) and dbo = colsum(dx1) taken in the same pass."""
         tp_layernorm_bwd(self.T, self.h, TP_BF16, self.x1_in, self.p["ln2_g"], self.mean2, self.rstd2, dxn2_sum, G,
-                         self.dx1, self.dln2_g, self.dln2_b, 0, self.ws, self.ws_bytes)
+                         self.dx1, self.dln2_g, self.dln2_b, self.db2, self.dbo, 0, self.ws, self.ws_bytes)
         return self.dx1
 
     def attn_bwd(self, dx1):
@@ -97,12 +97,11 @@ class LayerShard:
         tp_attn_shard_bwd(self.b, self.s, h, self.heads, self.t, self.r, TP_BF16, 1, self.xn1, p["Wqkv_r"],
                           p["Wo_r"], self.QKV, self.O, self.lse, dx1, self.dXn1, self.dWqkv, self.dbqkv, self.dWo, 0,
                           self.ws, self.ws_bytes)
-        tp_colsum(T, h, TP_BF16, dx1, self.dbo, 0, self.ws, self.ws_bytes)
         return self.dXn1
 
     def ln1_bwd(self, x, dxn1_sum, dx1):
         tp_layernorm_bwd(self.T, self.h, TP_BF16, x, self.p["ln1_g"], self.mean1, self.rstd1, dxn1_sum, dx1,
-                         self.dx, self.dln1_g, self.dln1_b, 0, self.ws, self.ws_bytes)
+                         self.dx, self.dln1_g, self.dln1_b, None, None, 0, self.ws, self.ws_bytes)
         return self.dx
 
     # ---- one rank's whole step with the peers' sums handed in -----------------------------

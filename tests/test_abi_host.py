@@ -92,3 +92,18 @@ def test_sum_partials_argument_errors():
     arr, _keep = tp._ptr_array([FAKE])
     assert tp.lib.tp_sum_partials(4, 60, 1, tp.TP_BF16, arr, None, None, FAKE, tp.TP_F32, None) == tp.TP_ERR_SHAPE
     assert tp.lib.tp_sum_partials(4, 64, 0, tp.TP_BF16, arr, None, None, FAKE, tp.TP_F32, None) == tp.TP_ERR_ARG
+
+
+def test_layernorm_argument_errors():
+    f = tp.lib.tp_layernorm_bwd
+    ws = tp.lib.tp_layernorm_bwd_workspace(64, 256, tp.TP_BF16)
+    assert ws >= 4 * 4 * 256 and tp.lib.tp_layernorm_bwd_workspace(0, 256, tp.TP_BF16) == 0
+    base = [FAKE] * 6   # x, gamma, mean, rstd, dy, dres
+    # the column sum of dres needs dres
+    assert f(64, 256, tp.TP_BF16, *base[:5], None, FAKE, None, None, FAKE, None, 0, FAKE, ws, None) == tp.TP_ERR_ARG
+    # h beyond the supported row width; h not a multiple of 8
+    assert f(64, 8200, tp.TP_BF16, *base, FAKE, None, None, None, None, 0, None, 0, None) == tp.TP_ERR_UNSUPPORTED
+    assert f(64, 252, tp.TP_BF16, *base, FAKE, None, None, None, None, 0, None, 0, None) == tp.TP_ERR_SHAPE
+    # a requested column sum needs the workspace
+    assert f(64, 256, tp.TP_BF16, *base, FAKE, None, None, None, FAKE, 0, FAKE, ws - 256, None) == tp.TP_ERR_WORKSPACE
+    assert f(64, 256, tp.TP_BF16, *base, FAKE, None, None, None, None, 2, None, 0, None) == tp.TP_ERR_ARG

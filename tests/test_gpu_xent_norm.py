@@ -113,14 +113,18 @@ def test_layernorm_fwd_bwd(dtype, h):
     y, mean, rstd = empty((T, h), dtype), empty((T,), "f32"), empty((T,), "f32")
     tp.tp_layernorm_fwd(T, h, dt, 1e-5, xd, gd, bd, y, mean, rstd)
     dx, dg, db = empty((T, h), dtype), empty((h,), dtype), empty((h,), dtype)
+    sr, sx = empty((h,), dtype), empty((h,), dtype)
     nb = tp.tp_layernorm_bwd_workspace(T, h, dt)
-    tp.tp_layernorm_bwd(T, h, dt, xd, gd, mean, rstd, dev(dy, dtype), dev(dres, dtype), dx, dg, db, 0, ws(nb), nb)
+    tp.tp_layernorm_bwd(T, h, dt, xd, gd, mean, rstd, dev(dy, dtype), dev(dres, dtype), dx, dg, db, sr, sx, 0,
+                        ws(nb), nb)
     f = oracle.layernorm_fwd(x, gam, bet)
     b = oracle.layernorm_bwd(x, gam, f["mean"], f["rstd"], dy)
     tol = 1e-5 if dtype == "f32" else 1e-2
+    dx_ref = b["dx"] + dres
     errs = {"y": rel_l2(host(y), f["y"]), "mean": rel_l2(host(mean), f["mean"]), "rstd": rel_l2(host(rstd), f["rstd"]),
-            "dx": rel_l2(host(dx), b["dx"] + dres), "dgamma": rel_l2(host(dg), b["dgamma"]),
-            "dbeta": rel_l2(host(db), b["dbeta"])}
+            "dx": rel_l2(host(dx), dx_ref), "dgamma": rel_l2(host(dg), b["dgamma"]),
+            "dbeta": rel_l2(host(db), b["dbeta"]), "colsum_dres": rel_l2(host(sr), dres.sum(axis=0)),
+            "colsum_dx": rel_l2(host(sx), dx_ref.sum(axis=0))}
     say(f"[ln] {dtype} h={h}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for k, e in errs.items():
         assert e <= tol, (k, e)
@@ -141,3 +145,28 @@ def test_sum_partials_and_colsum_exact():
     nb = tp.tp_colsum_workspace(rows, cols, tp.TP_F32)
     tp.tp_colsum(rows, cols, tp.TP_F32, dev(parts[0], "f32"), cs, 0, ws(nb), nb)
     assert np.array_equal(host(cs), parts[0].sum(axis=0))
+
+
+def test_layernorm_bwd_colsums_exact_and_zero_rows():
+    """The fused column sum of dres is an exact integer sum for small-integer dres; with no rows
+    every requested column sum is written as zero (accumulate=0) or left unchanged (accumulate=1)."""
+    g = np.random.default_rng(98)
+    T, h = 203, 264
+    x = tp_synth.round_to_dtype(g.standard_normal((T, h)), "f32")
+    gam = tp_synth.round_to_dtype(1 + 0.1 * g.standard_normal(h), "f32")
+    dy = tp_synth.round_to_dtype(g.standard_normal((T, h)), "f32")
+    dres = g.integers(-8, 8, (T, h)).astype(np.float64)
+    f = oracle.layernorm_fwd(x, gam, np.zeros(h))
+    xd, gd = dev(x, "f32"), dev(gam, "f32")
+    mean, rstd = dev(f["mean"], "f32"), dev(f["rstd"], "f32")
+    dx, sr = empty((T, h), "f32"), empty((h,), "f32")
+    nb = tp.tp_layernorm_bwd_workspace(T, h, tp.TP_F32)
+    tp.tp_layernorm_bwd(T, h, tp.TP_F32, xd, gd, mean, rstd, dev(dy, "f32"), dev(dres, "f32"), dx, None, None, sr,
+                        None, 0, ws(nb), nb)
+    assert np.array_equal(host(sr), dres.sum(axis=0))
+    outs = [torch.full((h,), 3.0, dtype=torch.float32, device="cuda:0") for _ in range(4)]
+    for acc, want in ((1, 3.0), (0, 0.0)):
+        tp.tp_layernorm_bwd(0, h, tp.TP_F32, xd, gd, mean, rstd, dev(dy, "f32"), dev(dres, "f32"), dx, *outs, acc,
+                            None, 0)
+        for o in outs:
+            assert np.array_equal(host(o), np.full(h, want))
