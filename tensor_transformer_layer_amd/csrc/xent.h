@@ -48,6 +48,10 @@ struct EpiXent {
         XentPartial* red = (XentPartial*)smem;   // [WGM][BN]; the main loop ended on a barrier
         const int h = lane >> 5, l32 = lane & 31;
         const int wm = (mw0 - m0) / C::WM;
+        // a wave whose rows are all inside M and unmasked skips the per-row validity tests; a
+        // lane visits its rows in increasing order, so a strict > keeps the lowest row on ties
+        const bool full = (mw0 + C::WM <= M) && (!mask || col0 + mw0 + C::WM <= Vreal);
+        constexpr float kL2e = 1.4426950408889634f;
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
             const int nloc = (nw0 - n0) + j * 32 + l32;
@@ -55,27 +59,41 @@ struct EpiXent {
             const int trow = (n < N) ? targets[n] - col0 : -1;
             float mx = -INFINITY, tv = 0.f;
             int am = INT_MAX;
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    int row = mw0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                    bool valid = row < M && (!mask || col0 + row < Vreal);
-                    float x = acc[i][j][v];
-                    if (valid && (x > mx || (x == mx && row < am))) { mx = x; am = row; }
-                    if (row == trow && row < M) tv = x;
-                }
-            xent_better(mx, am, __shfl_xor(mx, 32), __shfl_xor(am, 32));
-            tv += __shfl_xor(tv, 32);
-            float se = 0.f;
-            if (mx != -INFINITY) {
+            if (full) {
 #pragma unroll
                 for (int i = 0; i < C::TM; ++i)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        int row = mw0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                        bool valid = row < M && (!mask || col0 + row < Vreal);
-                        if (valid) se += expf(acc[i][j][v] - mx);
+                        const int row = mw0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                        const float x = acc[i][j][v];
+                        if (x > mx) { mx = x; am = row; }
+                        tv = (row == trow) ? x : tv;
+                    }
+            } else {
+#pragma unroll
+                for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int row = mw0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                        const bool valid = row < M && (!mask || col0 + row < Vreal);
+                        const float x = acc[i][j][v];
+                        if (valid && x > mx) { mx = x; am = row; }
+                        if (row == trow && row < M) tv = x;
+                    }
+            }
+            xent_better(mx, am, __shfl_xor(mx, 32), __shfl_xor(am, 32));
+            tv += __shfl_xor(tv, 32);
+            float se = 0.f;
+            if (mx != -INFINITY) {
+                const float nb = -mx * kL2e;
+#pragma unroll
+                for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int row = mw0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                        const bool valid = full || (row < M && (!mask || col0 + row < Vreal));
+                        // hardware exp2: terms below 2^-126 of the max flush to zero
+                        if (valid) se += __builtin_amdgcn_exp2f(fmaf(acc[i][j][v], kL2e, nb));
                     }
             }
             se += __shfl_xor(se, 32);

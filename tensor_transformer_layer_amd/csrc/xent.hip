@@ -5,28 +5,48 @@
 
 namespace tp {
 
-// Per token: merge the tiles' partials in tile order.
+// Per token: merge the tiles' partials. Block = 64 tokens x 4 phases; phase p merges tiles
+// p, p+4, ... in order, then the four phase results are merged in phase order.
+struct XentAcc {
+    float mx, se, tv;
+    int am;
+    __device__ __forceinline__ void init() { mx = -INFINITY; se = 0.f; tv = 0.f; am = INT_MAX; }
+    __device__ __forceinline__ void add(float pmx, float pse, float ptv, int pam) {
+        float m2 = mx;
+        int a2 = am;
+        xent_better(m2, a2, pmx, pam);
+        xent_merge_se(mx, se, pmx, pse);
+        am = a2;
+        tv += ptv;
+    }
+};
+
 __global__ __launch_bounds__(256) void xent_merge_kernel(const XentPartial* __restrict__ part, int tiles_m, int N,
                                                          int col0, float* __restrict__ max_r,
                                                          float* __restrict__ sumexp_r, float* __restrict__ tgt_r,
                                                          int32_t* __restrict__ argmax_r) {
-    int n = blockIdx.x * 256 + threadIdx.x;
-    if (n >= N) return;
-    float mx = -INFINITY, se = 0.f, tv = 0.f;
-    int am = INT_MAX;
-    for (int tm = 0; tm < tiles_m; ++tm) {
-        XentPartial p = part[(size_t)tm * N + n];
-        float m2 = mx;
-        int a2 = am;
-        xent_better(m2, a2, p.mx, p.am);
-        xent_merge_se(mx, se, p.mx, p.se);
-        am = a2;
-        tv += p.tv;
+    __shared__ XentPartial red[4][64];
+    const int tl = threadIdx.x & 63, ph = threadIdx.x >> 6;
+    const int n = blockIdx.x * 64 + tl;
+    XentAcc a;
+    a.init();
+    if (n < N) {
+        for (int tm = ph; tm < tiles_m; tm += 4) {
+            XentPartial p = part[(size_t)tm * N + n];
+            a.add(p.mx, p.se, p.tv, p.am);
+        }
     }
-    max_r[n] = mx;
-    sumexp_r[n] = se;
-    tgt_r[n] = tv;
-    if (argmax_r) argmax_r[n] = (am == INT_MAX) ? -1 : col0 + am;
+    red[ph][tl] = XentPartial{a.mx, a.se, a.tv, a.am};
+    __syncthreads();
+    if (ph != 0 || n >= N) return;
+    for (int q = 1; q < 4; ++q) {
+        XentPartial p = red[q][tl];
+        a.add(p.mx, p.se, p.tv, p.am);
+    }
+    max_r[n] = a.mx;
+    sumexp_r[n] = a.se;
+    tgt_r[n] = a.tv;
+    if (argmax_r) argmax_r[n] = (a.am == INT_MAX) ? -1 : col0 + a.am;
 }
 
 constexpr int XENT_MAX_T = 64;
@@ -36,29 +56,53 @@ struct XentPtrs {
     const float* tg[XENT_MAX_T];
 };
 
-// loss_n = M + log(sum_r se_r exp(mx_r - M)) - sum_r tg_r, ranks merged in order.
-__global__ __launch_bounds__(256) void xent_combine_kernel(int N, int t, XentPtrs p, float* __restrict__ loss) {
-    int n = blockIdx.x * 256 + threadIdx.x;
+// loss_n = M + log(sum_r se_r exp(mx_r - M)) - sum_r tg_r: the global max first, then the sums
+// relative to it, ranks in order. Ranks are read eight at a time so their loads are in flight
+// together.
+__global__ __launch_bounds__(64) void xent_combine_kernel(int N, int t, XentPtrs p, float* __restrict__ loss) {
+    int n = blockIdx.x * 64 + threadIdx.x;
     if (n >= N) return;
     float M = -INFINITY;
-    for (int r = 0; r < t; ++r) M = fmaxf(M, p.mx[r][n]);
+    for (int r0 = 0; r0 < t; r0 += 8) {
+        float mx[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) mx[k] = (r0 + k < t) ? p.mx[r0 + k][n] : -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) M = fmaxf(M, mx[k]);
+    }
     float S = 0.f, T = 0.f;
-    for (int r = 0; r < t; ++r) {
-        float m = p.mx[r][n];
-        if (m != -INFINITY) S += p.se[r][n] * expf(m - M);
-        T += p.tg[r][n];
+    for (int r0 = 0; r0 < t; r0 += 8) {
+        float mx[8], se[8], tg[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const bool in = r0 + k < t;
+            mx[k] = in ? p.mx[r0 + k][n] : -INFINITY;
+            se[k] = in ? p.se[r0 + k][n] : 0.f;
+            tg[k] = in ? p.tg[r0 + k][n] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (mx[k] != -INFINITY) S += se[k] * expf(mx[k] - M);
+            T += tg[k];
+        }
     }
     loss[n] = M + logf(S) - T;
 }
 
-// mean of x[0..N) with one block, fixed order: thread partials over a stride, then a tree.
-__global__ __launch_bounds__(256) void mean_kernel(const float* __restrict__ x, int N, float* __restrict__ out) {
-    __shared__ float red[256];
-    float a = 0.f;
-    for (int i = threadIdx.x; i < N; i += 256) a += x[i];
-    red[threadIdx.x] = a;
+// mean of x[0..N) with one block, fixed order: each thread sums a stride with four running
+// partials (added in order), then a tree over the threads.
+__global__ __launch_bounds__(1024) void mean_kernel(const float* __restrict__ x, int N, float* __restrict__ out) {
+    __shared__ float red[1024];
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    int i = threadIdx.x;
+    for (; i + 3 * 1024 < N; i += 4 * 1024) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[k] += x[i + k * 1024];
+    }
+    for (int k = 0; i < N; i += 1024, ++k) a[k] += x[i];
+    red[threadIdx.x] = (a[0] + a[1]) + (a[2] + a[3]);
     __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
+    for (int w = 512; w > 0; w >>= 1) {
         if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
@@ -69,7 +113,7 @@ __global__ __launch_bounds__(256) void mean_kernel(const float* __restrict__ x, 
 hipError_t xent_merge(const void* part, int tiles_m, int N, int col0, float* mx, float* se, float* tg,
                       int32_t* am, hipStream_t st) {
     if (N == 0) return hipSuccess;
-    hipLaunchKernelGGL(xent_merge_kernel, dim3((N + 255) / 256), dim3(256), 0, st, (const XentPartial*)part,
+    hipLaunchKernelGGL(xent_merge_kernel, dim3((N + 63) / 64), dim3(256), 0, st, (const XentPartial*)part,
                        tiles_m, N, col0, mx, se, tg, am);
     return hipGetLastError();
 }
@@ -79,10 +123,10 @@ hipError_t xent_combine(int N, int t, const float* const* mx, const float* const
     if (N == 0) return hipSuccess;
     XentPtrs p;
     for (int r = 0; r < t; ++r) { p.mx[r] = mx[r]; p.se[r] = se[r]; p.tg[r] = tg[r]; }
-    hipLaunchKernelGGL(xent_combine_kernel, dim3((N + 255) / 256), dim3(256), 0, st, N, t, p, loss);
+    hipLaunchKernelGGL(xent_combine_kernel, dim3((N + 63) / 64), dim3(64), 0, st, N, t, p, loss);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !mean) return e;
-    hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, st, (const float*)loss, N, mean);
+    hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, st, (const float*)loss, N, mean);
     return hipGetLastError();
 }
 
