@@ -14,13 +14,14 @@
 // Softmax runs in the log2 domain in fp32 (scores pre-scaled by log2(e)/sqrt(d)).
 //
 // Work split. A block has four waves and owns 64 rows (queries in the forward and dQ kernels, keys
-// in the dK/dV kernel): waves 0/1 and 2/3 each cover the 64 rows as two 32-row groups, and the two
-// pairs take alternate 64-wide tiles of the loop dimension (keys, or queries for dK/dV), so a
-// block carries two waves per SIMD pair and half the serial chain of one wave per row group. The
-// pairs' partial results are merged through LDS at the end in a fixed order. Blocks are launched
-// heaviest first (most visible tiles under the causal mask). Up to D = 96 the kernels are held to
-// 256 registers per lane (two waves per SIMD). Loop tiles are staged through
-// registers: the next two tiles' global loads are in flight while the current two are used.
+// in the dK/dV kernel): waves 0/1 and 2/3 each cover the 64 rows as two 32-row groups. In the
+// forward and dQ kernels the two pairs take alternate 64-wide key tiles; in the dK/dV kernel they
+// take the two 32-query halves of each query tile (one tile per step keeps its staging registers
+// within the two-waves-per-SIMD budget). The pairs' partial results are merged through LDS at the
+// end in a fixed order. Blocks are launched heaviest first (most visible tiles under the causal
+// mask). Up to D = 96 the kernels are held to 256 registers per lane (two waves per SIMD). Loop
+// tiles are staged through registers: the next step's global loads are in flight while the
+// current step's tiles are used.
 //
 // Backward: D = rowsum(dO * O); the dK/dV kernel owns 64 keys per block and loops over query
 // tiles; the dQ kernel owns 64 queries per block and loops over key tiles. Both recompute P from
@@ -49,9 +50,9 @@ __device__ __forceinline__ int att_off(int row, int col) {
 
 // Register-staged copy of rows [r0, r0 + 128) x D of a strided bf16 matrix (rows >= valid read 0)
 // into two consecutive LDS tiles (row r lands in tile r / 64; att_off is valid across both).
-template <int D>
+template <int D, int ROWS = 2 * ATT_B>
 struct AttTileRegs {
-    static constexpr int ROWS = 2 * ATT_B, CPR = D / 8, N = ROWS * CPR / ATT_NT;
+    static constexpr int CPR = D / 8, N = ROWS * CPR / ATT_NT;
     static_assert((ROWS * CPR) % ATT_NT == 0, "tile/threads mismatch");
     u32x4 v[N];
     __device__ __forceinline__ void load(const bf16* __restrict__ src, int ld, int r0, int valid, int tid) {
@@ -305,8 +306,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(const bf16* __restric
 
 // ---------------------------------------------------------------------------------------------
 // dK, dV. grid = (b * heads_t, key tiles), key tile kt = blockIdx.y (heavy first under the causal
-// mask). Wave w: key group g = w & 1 (keys kt*64 + 32g ..), query-tile parity qp = w >> 1; the
-// waves loop over the query tiles that can see their keys, two tiles (Q, dO, lse, D) per step.
+// mask). Wave w: key group g = w & 1 (keys kt*64 + 32g ..), query half q = w >> 1 of each query
+// tile; the waves loop over the query tiles that can see their keys, one tile (Q, dO, lse, D) per
+// step, and the two query halves' dK, dV are added at the end.
 //   S = Q K^T, P = exp2(S*c - lse2), dP = dO V^T, dS = P (dP - D)      (query rows x own keys)
 //   dV^T += dO^T P,  dK^T += Q^T dS                                     (transposing reads)
 // ---------------------------------------------------------------------------------------------
@@ -316,14 +318,14 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
                           const bf16* __restrict__ dO, int ld_do, const float* __restrict__ lse,
                           const float* __restrict__ Dv, float scale_log2, float scale, int causal,
                           bf16* __restrict__ dQKV, int ld_dq) {
-    __shared__ __attribute__((aligned(16))) bf16 smem[4 * ATT_B * D];   // Q tiles [2] | dO tiles [2]
-    __shared__ __attribute__((aligned(16))) bf16 KVs[2 * ATT_B * D];    // the block's keys | values
-    __shared__ float lse_s[2 * ATT_B], D_s[2 * ATT_B];
+    __shared__ __attribute__((aligned(16))) bf16 smem[4 * ATT_B * D];   // Q tile | dO tile | K | V
+    __shared__ float lse_s[ATT_B], D_s[ATT_B];
     bf16* Qb = smem;
-    bf16* Gb = smem + 2 * ATT_B * D;
+    bf16* Gb = smem + ATT_B * D;
+    bf16* KVs = smem + 2 * ATT_B * D;
     const int head = blockIdx.x % heads_t, bi = blockIdx.x / heads_t, kt = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
-    const int grp = wave & 1, qp = wave >> 1;
+    const int grp = wave & 1, qh = wave >> 1;
     const size_t tok0 = (size_t)bi * s;
     const bf16* Qp = QKV + tok0 * ld + head * D;
     const bf16* Kp = QKV + tok0 * ld + h_t + head * D;
@@ -344,13 +346,12 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
 
     const int nqt = (s + ATT_B - 1) / ATT_B;
     const int qt0 = causal ? kt : 0;
-    const int niter = (nqt - qt0 + 1) / 2;
-    AttTileRegs<D> qr, gr;
+    AttTileRegs<D, ATT_B> qr, gr;
     float lse_r = INFINITY, d_r = 0.f;
-    auto fetch = [&](int q0) {   // query tiles starting at row q0 (two of them)
+    auto fetch = [&](int q0) {
         qr.load(Qp, ld, q0, s, tid);
         gr.load(dOp, ld_do, q0, s, tid);
-        if (tid < 2 * ATT_B) {
+        if (tid < ATT_B) {
             int q = q0 + tid;
             lse_r = (q < s) ? lsep[q] * kLog2e : INFINITY;
             d_r = (q < s) ? Dp[q] : 0.f;
@@ -359,54 +360,45 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
     auto stash = [&]() {
         qr.store(Qb, tid);
         gr.store(Gb, tid);
-        if (tid < 2 * ATT_B) { lse_s[tid] = lse_r; D_s[tid] = d_r; }
+        if (tid < ATT_B) { lse_s[tid] = lse_r; D_s[tid] = d_r; }
     };
-    if (niter > 0) { fetch(qt0 * ATT_B); stash(); }
+    if (qt0 < nqt) { fetch(qt0 * ATT_B); stash(); }
     __syncthreads();
-    for (int it = 0; it < niter; ++it) {
-        const bool more = it + 1 < niter;
-        if (more) fetch((qt0 + 2 * it + 2) * ATT_B);
-        const int qt = qt0 + 2 * it + qp;
-        if (qt < nqt) {
-            const int q0 = qt * ATT_B;
-            const bf16* Q = Qb + qp * ATT_B * D;
-            const bf16* Gt = Gb + qp * ATT_B * D;
-            const float* ls = lse_s + qp * ATT_B;
-            const float* ds_ = D_s + qp * ATT_B;
+    for (int qt = qt0; qt < nqt; ++qt) {
+        const bool more = qt + 1 < nqt;
+        if (more) fetch((qt + 1) * ATT_B);
+        const int q0 = qt * ATT_B;
+        const int qs0 = q0 + qh * 32;
+        if (!(causal && qs0 + 31 < kw0)) {   // some query of this half sees some key of this wave
+            const bool need_mask = (causal && qs0 < kw0 + 31) || (qs0 + 32 > s) || (kw0 + 32 > s);
+            f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-                const int qs0 = q0 + sub * 32;
-                if (causal && qs0 + 31 < kw0) continue;  // every query of this half precedes every key of this wave
-                const bool need_mask = (causal && qs0 < kw0 + 31) || (qs0 + 32 > s) || (kw0 + 32 > s);
-                f32x16 sacc = zero16(), dpacc = zero16();
+            for (int ks = 0; ks < D / 16; ++ks) {
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(Qb, qh * 32, ks * 16, lane),
+                                                               frag_rows<D>(Ks, grp * 32, ks * 16, lane), sacc, 0, 0, 0);
+                dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(Gb, qh * 32, ks * 16, lane),
+                                                                frag_rows<D>(Vs, grp * 32, ks * 16, lane), dpacc, 0, 0, 0);
+            }
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(Q, sub * 32, ks * 16, lane),
-                                                                   frag_rows<D>(Ks, grp * 32, ks * 16, lane), sacc, 0, 0, 0);
-                    dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(Gt, sub * 32, ks * 16, lane),
-                                                                    frag_rows<D>(Vs, grp * 32, ks * 16, lane), dpacc, 0, 0, 0);
+            for (int v = 0; v < 16; ++v) {
+                int qi = qh * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                float pv = exp2f(fmaf(sacc[v], scale_log2, -lse_s[qi]));
+                if (need_mask) {
+                    int q = q0 + qi;
+                    if ((causal && mykey > q) || mykey >= s) pv = 0.f;
                 }
+                sacc[v] = pv;
+                dpacc[v] = pv * (dpacc[v] - D_s[qi]);
+            }
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    int qi = sub * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                    float pv = exp2f(fmaf(sacc[v], scale_log2, -ls[qi]));
-                    if (need_mask) {
-                        int q = q0 + qi;
-                        if ((causal && mykey > q) || mykey >= s) pv = 0.f;
-                    }
-                    sacc[v] = pv;
-                    dpacc[v] = pv * (dpacc[v] - ds_[qi]);
-                }
+            for (int kk = 0; kk < 2; ++kk) {
+                bf16x8 pb = pack8(sacc, 8 * kk), dsb = pack8(dpacc, 8 * kk);
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    bf16x8 pb = pack8(sacc, 8 * kk), dsb = pack8(dpacc, 8 * kk);
-#pragma unroll
-                    for (int dt = 0; dt < D / 32; ++dt) {
-                        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<D>(Gt, sub * 32 + 16 * kk, dt * 32, lane),
-                                                                         pb, dv[dt], 0, 0, 0);
-                        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<D>(Q, sub * 32 + 16 * kk, dt * 32, lane),
-                                                                         dsb, dk[dt], 0, 0, 0);
-                    }
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<D>(Gb, qh * 32 + 16 * kk, dt * 32, lane),
+                                                                     pb, dv[dt], 0, 0, 0);
+                    dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<D>(Qb, qh * 32 + 16 * kk, dt * 32, lane),
+                                                                     dsb, dk[dt], 0, 0, 0);
                 }
             }
         }
@@ -414,11 +406,11 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
         if (more) stash();
         __syncthreads();
     }
-    // merge: odd-parity waves hand dK, dV to the even-parity wave of the same key group
+    // merge: the second query half's waves hand dK, dV to the first half's wave of the same key group
     constexpr int NV = D;   // dk (D/2) + dv (D/2) per lane
     float* xch = (float*)smem;
     static_assert(2 * NV * 64 * 4 <= 4 * ATT_B * D * 2, "exchange exceeds the tile buffers");
-    if (qp == 1) {
+    if (qh == 1) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -428,7 +420,7 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
             }
     }
     __syncthreads();
-    if (qp == 0 && mykey < s) {
+    if (qh == 0 && mykey < s) {
         bf16* kp_ = dQKV + (tok0 + mykey) * ld_dq + h_t + head * D;
         bf16* vp_ = dQKV + (tok0 + mykey) * ld_dq + 2 * h_t + head * D;
 #pragma unroll
