@@ -178,6 +178,17 @@ tp_status tp_sum_partials(int rows, int cols, int t, tp_dtype in_dt, const void*
                           const void* bias, const void* residual, void* out, tp_dtype out_dt,
                           hipStream_t stream);
 
+/* Fused consumer of the forward g in a pre-LN block ("Megatron-LM, annotated", §2.2; the layer
+ * norm is replicated on every rank): out = sum_{r=0}^{t-1} parts[r] + bias + residual, summed in
+ * fp32 in rank order and stored in dt, then y = LayerNorm(out) exactly as tp_layernorm_fwd would
+ * compute it from the stored out. parts is a HOST array of t device pointers to [T, h] tensors;
+ * every tensor (parts, bias [h], residual [T, h], out, gamma, beta, y) is in dt; bias and residual
+ * may be NULL; mean, rstd [T] fp32 may be NULL. h <= 8192. */
+tp_status tp_sum_partials_layernorm(int T, int h, int t, tp_dtype dt, const void* const* parts,
+                                    const void* bias, const void* residual, void* out, float eps,
+                                    const void* gamma, const void* beta, void* y, float* mean,
+                                    float* rstd, hipStream_t stream);
+
 /* LayerNorm over the last dimension: y = (x - mean) / sqrt(var + eps) * gamma + beta with the
  * biased variance. x, y [T, h] and gamma, beta [h] in dt; mean, rstd [T] fp32 (may be NULL). */
 tp_status tp_layernorm_fwd(int T, int h, tp_dtype dt, float eps, const void* x, const void* gamma,

@@ -54,6 +54,7 @@ SIGNATURES = {
     "tp_vocab_logits_shard": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p]),
     "tp_vocab_xent_combine": (_i, [_i, _i, _pp, _pp, _pp, _p, _p, _p]),
     "tp_sum_partials": (_i, [_i, _i, _i, _i, _pp, _p, _p, _p, _i, _p]),
+    "tp_sum_partials_layernorm": (_i, [_i, _i, _i, _i, _pp, _p, _p, _p, _f, _p, _p, _p, _p, _p, _p]),
     "tp_layernorm_fwd": (_i, [_i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p]),
     "tp_layernorm_bwd_workspace": (_z, [_i, _i, _i]),
     "tp_layernorm_bwd": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
@@ -171,6 +172,12 @@ def tp_sum_partials(rows, cols, t, in_dt, parts, bias, residual, out, out_dt, st
     pp, _keep = _ptr_array(parts)
     _check(lib.tp_sum_partials(rows, cols, t, _dt(in_dt), pp, _ptr(bias), _ptr(residual), _ptr(out), _dt(out_dt),
                                _stream(stream)))
+
+
+def tp_sum_partials_layernorm(T, h, t, dt, parts, bias, residual, out, eps, gamma, beta, y, mean, rstd, stream=None):
+    pp, _keep = _ptr_array(parts)
+    _check(lib.tp_sum_partials_layernorm(T, h, t, _dt(dt), pp, _ptr(bias), _ptr(residual), _ptr(out), eps, _ptr(gamma),
+                                         _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), _stream(stream)))
 
 
 def tp_layernorm_fwd(T, h, dt, eps, x, gamma, beta, y, mean, rstd, stream=None):

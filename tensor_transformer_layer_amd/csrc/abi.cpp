@@ -383,6 +383,28 @@ tp_status tp_sum_partials(int rows, int cols, int t, tp_dtype in_dt, const void*
     return ok();
 }
 
+tp_status tp_sum_partials_layernorm(int T, int h, int t, tp_dtype dt, const void* const* parts, const void* bias,
+                                    const void* residual, void* out, float eps, const void* gamma, const void* beta,
+                                    void* y, float* mean, float* rstd, hipStream_t stream) {
+    const char* fn = "tp_sum_partials_layernorm";
+    tp_status s;
+    if ((s = check_dt(fn, dt)) != TP_OK) return s;
+    if (t < 1 || t > 64) return fail(TP_ERR_ARG, "%s: t=%d must be in [1, 64]", fn, t);
+    if (T < 0) return fail(TP_ERR_SHAPE, "%s: T=%d is negative", fn, T);
+    if ((s = check_mult8(fn, "h", h)) != TP_OK) return s;
+    if (h > 8192) return fail(TP_ERR_UNSUPPORTED, "%s: h=%d exceeds 8192", fn, h);
+    if (!(eps >= 0.0f)) return fail(TP_ERR_ARG, "%s: eps must be >= 0", fn);
+    if (!parts) return fail(TP_ERR_ARG, "%s: parts is NULL", fn);
+    for (int i = 0; i < t; ++i) {
+        if (!parts[i]) return fail(TP_ERR_ARG, "%s: parts[%d] is NULL", fn, i);
+        if (!aligned16(parts[i])) return fail(TP_ERR_ARG, "%s: parts[%d] is not 16-byte aligned", fn, i);
+    }
+    NEED(out); OPT(bias); OPT(residual); NEED(gamma); NEED(beta); NEED(y); OPT(mean); OPT(rstd);
+    HIP_TRY(sum_partials_layernorm(dt == TP_BF16, T, h, t, parts, bias, residual, out, eps, gamma, beta, y, mean, rstd,
+                                   stream), fn);
+    return ok();
+}
+
 tp_status tp_layernorm_fwd(int T, int h, tp_dtype dt, float eps, const void* x, const void* gamma, const void* beta,
                            void* y, float* mean, float* rstd, hipStream_t stream) {
     const char* fn = "tp_layernorm_fwd";

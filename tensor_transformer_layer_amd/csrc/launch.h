@@ -67,6 +67,10 @@ hipError_t xent_combine(int N, int t, const float* const* mx, const float* const
 int ln_bwd_blocks(int rows);
 hipError_t layernorm_fwd(int dt, int rows, int h, float eps, const void* x, const void* g, const void* b, void* y,
                          float* mean, float* rstd, hipStream_t st);
+// out = sum_r parts[r] + bias + residual (all dt), then y = LayerNorm(out as stored)
+hipError_t sum_partials_layernorm(int dt, int rows, int h, int t, const void* const* parts, const void* bias,
+                                  const void* residual, void* out, float eps, const void* g, const void* b, void* y,
+                                  float* mean, float* rstd, hipStream_t st);
 // dres_sum / dx_sum: optional column sums of dres and of dx (the bias gradients of the row-parallel
 // layers on either side of the residual branch)
 hipError_t layernorm_bwd(int dt, int rows, int h, const void* x, const void* g, const float* mean,

@@ -101,6 +101,88 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int h, float eps,
 }
 
 // ---------------------------------------------------------------------------------------------
+// Fused partial sum + LayerNorm forward (the consumer of the forward g in a pre-LN block): one
+// wave per row; out = sum_r parts[r] + bias + residual (fp32, rank order, rounded to T and
+// stored), then y = LayerNorm(out) computed from the rounded values, as a separate LN would see
+// them.
+// ---------------------------------------------------------------------------------------------
+constexpr int ADDLN_MAX_T = 64;
+struct AddLnParts { const void* p[ADDLN_MAX_T]; };
+
+template <typename T, int C>
+__global__ __launch_bounds__(256) void add_ln_fwd_kernel(int rows, int h, int t, AddLnParts parts,
+                                                         const T* __restrict__ bias, const T* __restrict__ residual,
+                                                         T* __restrict__ out, float eps, const T* __restrict__ gamma,
+                                                         const T* __restrict__ beta, T* __restrict__ y,
+                                                         float* __restrict__ mean, float* __restrict__ rstd) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const size_t ro = (size_t)row * h;
+    float v[C][8];
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+        int c = (lane + 64 * k) * 8;
+        if (c < h) {
+            float a[8];
+            load8((const T*)parts.p[0] + ro + c, a);
+            for (int r = 1; r < t; ++r) {
+                float b[8];
+                load8((const T*)parts.p[r] + ro + c, b);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] += b[e];
+            }
+            if (bias) {
+                float b[8];
+                load8(bias + c, b);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] += b[e];
+            }
+            if (residual) {
+                float b[8];
+                load8(residual + ro + c, b);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] += b[e];
+            }
+            store8(out + ro + c, a);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v[k][e] = to_f32(from_f32<T>(a[e]));   // the stored value
+                s += v[k][e];
+            }
+        }
+    }
+    const float mu = wave_sum(s) / (float)h;
+    float q = 0.f;
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+        int c = (lane + 64 * k) * 8;
+        if (c < h) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { float d = v[k][e] - mu; q += d * d; }
+        }
+    }
+    const float rs = rsqrtf(wave_sum(q) / (float)h + eps);
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+        int c = (lane + 64 * k) * 8;
+        if (c < h) {
+            float g[8], b[8], o[8];
+            load8(gamma + c, g);
+            load8(beta + c, b);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (v[k][e] - mu) * rs * g[e] + b[e];
+            store8(y + ro + c, o);
+        }
+    }
+    if (lane == 0) {
+        if (mean) mean[row] = mu;
+        if (rstd) rstd[row] = rs;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // LayerNorm backward: a block of ceil(h/512)*64 threads spans a row, 8 columns per thread
 // (h <= 8192), and takes RPI rows per iteration, fetched together (x, dy and dres of RPI rows in
 // flight per block). Row sums are wave butterflies followed by a sum over the block's waves in

@@ -41,6 +41,34 @@ hipError_t layernorm_fwd(int dt, int rows, int h, float eps, const void* x, cons
                    : ln_fwd_t<float>(rows, h, eps, x, g, b, y, mean, rstd, st);
 }
 
+hipError_t sum_partials_layernorm(int dt, int rows, int h, int t, const void* const* parts, const void* bias,
+                                  const void* residual, void* out, float eps, const void* g, const void* b, void* y,
+                                  float* mean, float* rstd, hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    if (t < 1 || t > ADDLN_MAX_T) return hipErrorInvalidValue;
+    AddLnParts pp;
+    for (int r = 0; r < t; ++r) pp.p[r] = parts[r];
+    dim3 grid((rows + 3) / 4);
+#define ADDLN(TT, C) hipLaunchKernelGGL((add_ln_fwd_kernel<TT, C>), grid, dim3(256), 0, st, rows, h, t, pp, (const TT*)bias, \
+                                        (const TT*)residual, (TT*)out, eps, (const TT*)g, (const TT*)b, (TT*)y, mean, rstd)
+#define ADDLN_T(TT)                        \
+    switch (ln_chunks(h)) {                \
+        case 1: ADDLN(TT, 1); break;       \
+        case 2: ADDLN(TT, 2); break;       \
+        case 3: ADDLN(TT, 3); break;       \
+        case 4: ADDLN(TT, 4); break;       \
+        case 6: ADDLN(TT, 6); break;       \
+        case 8: ADDLN(TT, 8); break;       \
+        case 12: ADDLN(TT, 12); break;     \
+        case 16: ADDLN(TT, 16); break;     \
+        default: return hipErrorInvalidValue; \
+    }
+    if (dt == 1) { ADDLN_T(bf16) } else { ADDLN_T(float) }
+#undef ADDLN_T
+#undef ADDLN
+    return hipGetLastError();
+}
+
 // threads of a LayerNorm backward block: 8 columns each, whole waves
 static int ln_threads(int h) { return (h + 511) / 512 * 64; }
 

@@ -20,7 +20,8 @@ import torch
 
 from . import (TP_BF16, tp_attn_shard_bwd, tp_attn_shard_bwd_workspace, tp_attn_shard_fwd,
                tp_layernorm_bwd, tp_layernorm_bwd_workspace, tp_layernorm_fwd,
-               tp_mlp_shard_bwd, tp_mlp_shard_bwd_workspace, tp_mlp_shard_fwd, tp_sum_partials)
+               tp_mlp_shard_bwd, tp_mlp_shard_bwd_workspace, tp_mlp_shard_fwd, tp_sum_partials,
+               tp_sum_partials_layernorm)
 
 EPS = 1e-5
 
@@ -70,7 +71,20 @@ class LayerShard:
         p, T, h = self.p, self.T, self.h
         self.x1_in = x1
         tp_layernorm_fwd(T, h, TP_BF16, EPS, x1, p["ln2_g"], p["ln2_b"], self.xn2, self.mean2, self.rstd2)
-        tp_mlp_shard_fwd(T, h, self.ffn, self.t, self.r, TP_BF16, self.xn2, p["A_r"], p["b1_r"], p["B_r"], self.U,
+        return self._mlp(self.xn2)
+
+    def combine_mlp_fwd(self, attn_parts, x):
+        """g after the attention block fused with LN2: x1 = sum(attn_parts) + bo + x and
+        xn2 = LN2(x1) in one pass, then the MLP shard on xn2."""
+        p, T, h = self.p, self.T, self.h
+        tp_sum_partials_layernorm(T, h, len(attn_parts), TP_BF16, attn_parts, p["bo"], x, self.x1, EPS, p["ln2_g"],
+                                  p["ln2_b"], self.xn2, self.mean2, self.rstd2)
+        self.x1_in = self.x1
+        return self._mlp(self.xn2)
+
+    def _mlp(self, xn2):
+        p = self.p
+        tp_mlp_shard_fwd(self.T, self.h, self.ffn, self.t, self.r, TP_BF16, xn2, p["A_r"], p["b1_r"], p["B_r"], self.U,
                          self.Y, self.Z_mlp)
         return self.Z_mlp
 
@@ -110,8 +124,7 @@ class LayerShard:
         from the all-reduces (the sum over ranks of the partials, before bias and residual)."""
         p = self.p
         self.attn_fwd(x)
-        self.combine([attn_sum], p["bo"], x, self.x1)
-        self.mlp_fwd(self.x1)
+        self.combine_mlp_fwd([attn_sum], x)
         self.combine([mlp_sum], p["b2"], self.x1, self.x2)
         self.mlp_bwd(G)
         self.ln2_bwd(dxn2_sum, G)

@@ -107,3 +107,21 @@ def test_layernorm_argument_errors():
     # a requested column sum needs the workspace
     assert f(64, 256, tp.TP_BF16, *base, FAKE, None, None, None, FAKE, 0, FAKE, ws - 256, None) == tp.TP_ERR_WORKSPACE
     assert f(64, 256, tp.TP_BF16, *base, FAKE, None, None, None, None, 2, None, 0, None) == tp.TP_ERR_ARG
+
+
+def test_sum_partials_layernorm_argument_errors():
+    f = tp.lib.tp_sum_partials_layernorm
+    arr, _keep = tp._ptr_array([FAKE, FAKE])
+    ok = dict(out=FAKE, gamma=FAKE, beta=FAKE, y=FAKE)
+
+    def call(T=4, h=64, t=2, dt=tp.TP_BF16, parts=arr, eps=1e-5, **kw):
+        a = {**ok, **kw}
+        return f(T, h, t, dt, parts, None, None, a["out"], eps, a["gamma"], a["beta"], a["y"], None, None, None)
+
+    assert call(t=0) == tp.TP_ERR_ARG
+    assert call(h=60) == tp.TP_ERR_SHAPE
+    assert call(h=8200) == tp.TP_ERR_UNSUPPORTED
+    assert call(eps=-1.0) == tp.TP_ERR_ARG
+    assert call(y=None) == tp.TP_ERR_ARG
+    bad, _k2 = tp._ptr_array([FAKE, None])
+    assert call(parts=bad) == tp.TP_ERR_ARG

@@ -66,3 +66,34 @@ def test_layer_step_every_output(b, s, h, heads, ffn, t):
     say(f"[layer] b={b} s={s} h={h} t={t}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     for k, e in errs.items():
         assert e <= 1e-2, (k, e)
+
+
+def test_layer_step_method_rank0():
+    """LayerShard.step (the sequence bench.py times: fused g + LN2, pre-summed all-reduce inputs)
+    for rank 0 of t = 2 against the oracle."""
+    b, s, h, heads, ffn, t = 2, 128, 256, 4, 1024, 2
+    p = tp_synth.layer_inputs(4343, b, s, h, ffn, "bf16", bias_std=0.05, ln_random=True)
+    shards, _x1, _x2, _dx1, _dx = run_layer(p, b, s, h, heads, ffn, t)   # sums every rank would receive
+    dev = "cuda:0"
+    T = b * s
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    x = torch.from_numpy(np.ascontiguousarray(p["x"])).to(torch.bfloat16).to(dev)
+    G = torch.from_numpy(np.ascontiguousarray(p["G"])).to(torch.bfloat16).to(dev)
+    attn_sum, mlp_sum, dxn2_sum, dxn1_sum = (torch.empty((T, h), **bf) for _ in range(4))
+    shards[0].combine([sh.attn_fwd(x) for sh in shards], None, None, attn_sum)
+    x1 = torch.empty((T, h), **bf)
+    shards[0].combine([attn_sum], shards[0].p["bo"], x, x1)
+    shards[0].combine([sh.mlp_fwd(x1) for sh in shards], None, None, mlp_sum)
+    shards[0].combine([sh.mlp_bwd(G) for sh in shards], None, None, dxn2_sum)
+    dx1 = shards[0].ln2_bwd(dxn2_sum, G)
+    shards[0].combine([sh.attn_bwd(dx1) for sh in shards], None, None, dxn1_sum)
+    x2, dx = shards[0].step(x, G, attn_sum, mlp_sum, dxn2_sum, dxn1_sum)
+    torch.cuda.synchronize()
+    f = oracle.layer_split_fwd(p["x"], p, b, s, heads, t)
+    g = oracle.layer_split_bwd(p["x"], p, f, p["G"], b, s, heads, t)
+    errs = {"x2": rel_l2(host(x2), f["x2"]), "dx": rel_l2(host(dx), g["dx"]),
+            "dln2_g": rel_l2(host(shards[0].dln2_g), g["dln2_g"]), "db2": rel_l2(host(shards[0].db2), g["mlp"]["db2"]),
+            "dA[0]": rel_l2(host(shards[0].dA), g["mlp"]["dA"][:, :ffn // t])}
+    say("[layer.step] " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    for k, e in errs.items():
+        assert e <= 1e-2, (k, e)

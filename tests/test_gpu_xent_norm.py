@@ -170,3 +170,29 @@ def test_layernorm_bwd_colsums_exact_and_zero_rows():
                             None, 0)
         for o in outs:
             assert np.array_equal(host(o), np.full(h, want))
+
+
+@pytest.mark.parametrize("dtype,h,t", [("bf16", 3072, 1), ("bf16", 1920, 3), ("f32", 136, 2)])
+def test_sum_partials_layernorm(dtype, h, t):
+    """out = sum of partials + bias + residual (exact on small integers), then LayerNorm of the
+    stored out against the oracle."""
+    T = 203
+    g = np.random.default_rng(99)
+    parts = [g.integers(-8, 8, (T, h)).astype(np.float64) for _ in range(t)]
+    bias = g.integers(-4, 4, h).astype(np.float64)
+    res = g.integers(-4, 4, (T, h)).astype(np.float64)
+    gam = tp_synth.round_to_dtype(1 + 0.1 * g.standard_normal(h), dtype)
+    bet = tp_synth.round_to_dtype(0.1 * g.standard_normal(h), dtype)
+    dt = tp.TP_BF16 if dtype == "bf16" else tp.TP_F32
+    out, y = empty((T, h), dtype), empty((T, h), dtype)
+    mean, rstd = empty((T,), "f32"), empty((T,), "f32")
+    tp.tp_sum_partials_layernorm(T, h, t, dt, [dev(p, dtype) for p in parts], dev(bias, dtype), dev(res, dtype), out,
+                                 1e-5, dev(gam, dtype), dev(bet, dtype), y, mean, rstd)
+    x = sum(parts) + bias + res
+    assert np.array_equal(host(out), x)
+    f = oracle.layernorm_fwd(x, gam, bet)
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    errs = {"y": rel_l2(host(y), f["y"]), "mean": rel_l2(host(mean), f["mean"]), "rstd": rel_l2(host(rstd), f["rstd"])}
+    say(f"[addln] {dtype} h={h} t={t}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
