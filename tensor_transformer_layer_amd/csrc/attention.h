@@ -48,18 +48,21 @@ __device__ __forceinline__ int att_off(int row, int col) {
     return row * D + ((((col >> 3) ^ ((row >> 2) & 3)) << 3) | (col & 7));
 }
 
-// Register-staged copy of rows [r0, r0 + 128) x D of a strided bf16 matrix (rows >= valid read 0)
-// into two consecutive LDS tiles (row r lands in tile r / 64; att_off is valid across both).
+// Register-staged copy of rows [r0, r0 + ROWS) x D of a strided bf16 matrix into consecutive LDS
+// tiles (row r lands in tile r / 64; att_off is valid across them). Loads go through a buffer
+// resource covering the sequence's rows: rows >= valid are fetched at an offset past the end,
+// which reads 0, so there is no branch per load.
 template <int D, int ROWS = 2 * ATT_B>
 struct AttTileRegs {
     static constexpr int CPR = D / 8, N = ROWS * CPR / ATT_NT;
     static_assert((ROWS * CPR) % ATT_NT == 0, "tile/threads mismatch");
     u32x4 v[N];
-    __device__ __forceinline__ void load(const bf16* __restrict__ src, int ld, int r0, int valid, int tid) {
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int ld, int r0, int valid, int tid) {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            int c = tid + i * ATT_NT, row = c / CPR, dc = c % CPR;
-            v[i] = (r0 + row < valid) ? *(const u32x4*)(src + (size_t)(r0 + row) * ld + dc * 8) : u32x4{0, 0, 0, 0};
+            const int c = tid + i * ATT_NT, row = c / CPR, dc = c % CPR;
+            const int off = (r0 + row < valid) ? ((r0 + row) * ld + dc * 8) * 2 : 0x7fffffff;
+            v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
         }
     }
     __device__ __forceinline__ void store(bf16* tiles, int tid) const {
@@ -70,6 +73,14 @@ struct AttTileRegs {
         }
     }
 };
+
+// Buffer resource over a sequence's s rows x D columns of a strided matrix starting at p (row
+// stride ld): exactly the bytes from the first row's start to the last row's end.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t att_rsrc(const bf16* p, int ld, int s) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(p), (short)0, (int)(((size_t)(s - 1) * ld + D) * 2),
+                                             0x00020000);
+}
 
 // Direct copy of rows [r0, r0 + 64) x D of a strided bf16 matrix into one LDS tile (rows >= valid
 // read 0); used once per block for the block's own rows, which then serve as MFMA operands
@@ -104,6 +115,10 @@ __device__ __forceinline__ bf16x8 frag_cols(const bf16* tile, int k0, int m0, in
     s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + att_off<D>(row + 8, col)));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
+
+// 2^x with the hardware instruction: results below 2^-126 flush to zero, which only drops
+// probabilities that are negligible against the row's maximum (and maps -inf to 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ bf16x8 pack8(const f32x16& a, int base) {
     u32x4 u;
@@ -163,9 +178,10 @@ void attn_fwd_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int h
     const int ntiles = (kv_end + ATT_B - 1) / ATT_B;
     const int niter = (ntiles + 1) / 2;
     AttTileRegs<D> kr, vr;
+    const auto krs = att_rsrc<D>(Kp, ld, s), vrs = att_rsrc<D>(Vp, ld, s);
     if (niter > 0) {
-        kr.load(Kp, ld, 0, s, tid);
-        vr.load(Vp, ld, 0, s, tid);
+        kr.load(krs, ld, 0, s, tid);
+        vr.load(vrs, ld, 0, s, tid);
         kr.store(Kb, tid);
         vr.store(Vb, tid);
     }
@@ -173,8 +189,8 @@ void attn_fwd_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int h
     for (int it = 0; it < niter; ++it) {
         const bool more = it + 1 < niter;
         if (more) {
-            kr.load(Kp, ld, (it + 1) * 2 * ATT_B, s, tid);
-            vr.load(Vp, ld, (it + 1) * 2 * ATT_B, s, tid);
+            kr.load(krs, ld, (it + 1) * 2 * ATT_B, s, tid);
+            vr.load(vrs, ld, (it + 1) * 2 * ATT_B, s, tid);
         }
         const int kt = 2 * it + kp, k0 = kt * ATT_B;
         if (kt < ntiles && !(causal && k0 > q0w + 31)) {   // some key of this tile is visible to this wave
@@ -208,13 +224,13 @@ void attn_fwd_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int h
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float m_new = fmaxf(m_i, mx * scale_log2);
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2f(m_i - m_use);
+            const float alpha = fast_exp2(m_i - m_use);
             float rs = 0.f;
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    float p = exp2f(fmaf(st[sub][v], scale_log2, -m_use));
+                    float p = fast_exp2(fmaf(st[sub][v], scale_log2, -m_use));
                     st[sub][v] = p;
                     rs += p;
                 }
@@ -261,7 +277,7 @@ void attn_fwd_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int h
         const float m_o = xch_get<NV>(xch, grp, 0, lane), l_o = xch_get<NV>(xch, grp, 1, lane);
         const float m = fmaxf(m_i, m_o);
         const float m_use = (m == -INFINITY) ? 0.f : m;
-        const float a = exp2f(m_i - m_use), c = exp2f(m_o - m_use);
+        const float a = fast_exp2(m_i - m_use), c = fast_exp2(m_o - m_use);
         const float l = l_i * a + l_o * c;
         const float inv = 1.0f / l;
         bf16* op = O + (tok0 + myq) * ldo + head * D;
@@ -347,10 +363,11 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
     const int nqt = (s + ATT_B - 1) / ATT_B;
     const int qt0 = causal ? kt : 0;
     AttTileRegs<D, ATT_B> qr, gr;
+    const auto qrs = att_rsrc<D>(Qp, ld, s), grs = att_rsrc<D>(dOp, ld_do, s);
     float lse_r = INFINITY, d_r = 0.f;
     auto fetch = [&](int q0) {
-        qr.load(Qp, ld, q0, s, tid);
-        gr.load(dOp, ld_do, q0, s, tid);
+        qr.load(qrs, ld, q0, s, tid);
+        gr.load(grs, ld_do, q0, s, tid);
         if (tid < ATT_B) {
             int q = q0 + tid;
             lse_r = (q < s) ? lsep[q] * kLog2e : INFINITY;
@@ -382,7 +399,7 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 int qi = qh * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                float pv = exp2f(fmaf(sacc[v], scale_log2, -lse_s[qi]));
+                float pv = fast_exp2(fmaf(sacc[v], scale_log2, -lse_s[qi]));
                 if (need_mask) {
                     int q = q0 + qi;
                     if ((causal && mykey > q) || mykey >= s) pv = 0.f;
@@ -482,9 +499,10 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, in
     const int ntiles = (kv_end + ATT_B - 1) / ATT_B;
     const int niter = (ntiles + 1) / 2;
     AttTileRegs<D> kr, vr;
+    const auto krs = att_rsrc<D>(Kp, ld, s), vrs = att_rsrc<D>(Vp, ld, s);
     if (niter > 0) {
-        kr.load(Kp, ld, 0, s, tid);
-        vr.load(Vp, ld, 0, s, tid);
+        kr.load(krs, ld, 0, s, tid);
+        vr.load(vrs, ld, 0, s, tid);
         kr.store(Kb, tid);
         vr.store(Vb, tid);
     }
@@ -492,8 +510,8 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, in
     for (int it = 0; it < niter; ++it) {
         const bool more = it + 1 < niter;
         if (more) {
-            kr.load(Kp, ld, (it + 1) * 2 * ATT_B, s, tid);
-            vr.load(Vp, ld, (it + 1) * 2 * ATT_B, s, tid);
+            kr.load(krs, ld, (it + 1) * 2 * ATT_B, s, tid);
+            vr.load(vrs, ld, (it + 1) * 2 * ATT_B, s, tid);
         }
         const int kt = 2 * it + kp, k0 = kt * ATT_B;
         if (kt < ntiles) {
@@ -514,7 +532,7 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, in
                 }
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    float pv = exp2f(fmaf(sacc[v], scale_log2, -lse2));
+                    float pv = fast_exp2(fmaf(sacc[v], scale_log2, -lse2));
                     if (need_mask) {
                         int key = ks0 + 8 * (v >> 2) + 4 * h + (v & 3);
                         if ((causal && key > myq) || key >= s) pv = 0.f;
