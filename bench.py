@@ -83,7 +83,7 @@ def stage_inputs():
     return p, xe
 
 
-def cpu_baseline(p, xe, seqs=8):
+def cpu_baseline(p, xe, seqs=8, heads=HEADS):
     """The float64 oracle on rank 0's work for `seqs` sequences (the same step, fewer tokens)."""
     import oracle
     try:
@@ -94,24 +94,24 @@ def cpu_baseline(p, xe, seqs=8):
     T = seqs * S
     ht, Ft, Vt = H // TP, FFN // TP, VOCAB_PAD // TP
     x, G = p["x"][:T], p["G"][:T]
-    Wqkv_r = oracle.qkv_shard(p["Wqkv"], HEADS, TP, 0)
-    bq = oracle.qkv_shard(p["bqkv"], HEADS, TP, 0)
-    Wo_r = oracle.wo_shard(p["Wo"], HEADS, TP, 0)
+    Wqkv_r = oracle.qkv_shard(p["Wqkv"], heads, TP, 0)
+    bq = oracle.qkv_shard(p["bqkv"], heads, TP, 0)
+    Wo_r = oracle.wo_shard(p["Wo"], heads, TP, 0)
     A_r, b1_r, B_r = p["A"][:, :Ft], p["b1"][:Ft], p["B"][:Ft]
     t0 = time.perf_counter()
     l1 = oracle.layernorm_fwd(x, p["ln1_g"], p["ln1_b"])
-    fa = oracle.attn_shard_fwd(l1["y"], Wqkv_r, bq, Wo_r, seqs, S, HEADS // TP)
+    fa = oracle.attn_shard_fwd(l1["y"], Wqkv_r, bq, Wo_r, seqs, S, heads // TP)
     x1 = x + fa["Z"] + p["bo"]                 # rank 0's partial stands in for the all-reduced sum
     l2 = oracle.layernorm_fwd(x1, p["ln2_g"], p["ln2_b"])
     fm = oracle.mlp_shard_fwd(l2["y"], A_r, b1_r, B_r)
     gm = oracle.mlp_shard_bwd(l2["y"], A_r, B_r, fm["U"], fm["Y"], G)
     b2 = oracle.layernorm_bwd(x1, p["ln2_g"], l2["mean"], l2["rstd"], gm["dX"])
     dx1 = G + b2["dx"]
-    ga = oracle.attn_shard_bwd(l1["y"], Wqkv_r, Wo_r, fa, dx1, seqs, S, HEADS // TP)
+    ga = oracle.attn_shard_bwd(l1["y"], Wqkv_r, Wo_r, fa, dx1, seqs, S, heads // TP)
     oracle.layernorm_bwd(x, p["ln1_g"], l1["mean"], l1["rstd"], ga["dXn"])
     oracle.xent_shard_stats(xe["X"][:T], xe["E0"], xe["targets"][:T], TP, 0, VOCAB)
     dt = time.perf_counter() - t0
-    flops = layer_flops(seqs, S, H, HEADS, FFN, TP) + xent_flops(T, H, Vt)
+    flops = layer_flops(seqs, S, H, heads, FFN, TP) + xent_flops(T, H, Vt)
     return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"rank 0 step (layer fwd+bwd + vocab-shard statistics) on {seqs} of {B} sequences "
                       f"({T} tokens), float64 NumPy, {dt:.1f} s"}
@@ -125,6 +125,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="copy 512 MiB device-to-device once before the steps (calibrates HBM byte counters)")
+    ap.add_argument("--heads", type=int, default=HEADS,
+                    help="attention heads of the layer (the pages' 8.3B head-count sweep uses 16, 24, 32; the "
+                         "FLOPs and all other shapes are unchanged, heads per rank = heads / 8)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
@@ -145,7 +148,11 @@ def main():
 
     x, G = d(p["x"]), d(p["G"])
     # verification run over all ranks: the sums rank 0 would receive
-    shards = [LayerShard(B, S, H, HEADS, FFN, TP, r, rank_params(p, HEADS, TP, r, dev), dev) for r in range(TP)]
+    heads = args.heads
+    if heads % TP or H % heads:
+        print(f"--heads {heads}: must be a multiple of t={TP} and divide h={H}", file=sys.stderr)
+        sys.exit(2)
+    shards = [LayerShard(B, S, H, heads, FFN, TP, r, rank_params(p, heads, TP, r, dev), dev) for r in range(TP)]
     attn_sum = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     mlp_sum, dxn2_sum, dxn1_sum = (torch.empty_like(attn_sum) for _ in range(3))
     shards[0].combine([sh.attn_fwd(x) for sh in shards], None, None, attn_sum)
@@ -209,7 +216,7 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    fl_layer = layer_flops(B, S, H, HEADS, FFN, TP)
+    fl_layer = layer_flops(B, S, H, heads, FFN, TP)
     fl_xent = xent_flops(T, H, Vt)
     value = (fl_layer + fl_xent) / (ms * 1e-3) / 1e12
     xent_ms = float(np.mean([a.elapsed_time(b_) for a, b_ in xev]))
@@ -229,7 +236,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, uniform targets)",
         "config": {"workload": "8.3B-shape layer shard t=8 rank 0 fwd+bwd + vocab-parallel xent shard",
-                   "batch": B, "seq_len": S, "hidden": H, "heads": HEADS, "ffn": FFN, "tp": TP,
+                   "batch": B, "seq_len": S, "hidden": H, "heads": heads, "ffn": FFN, "tp": TP,
                    "vocab_padded": VOCAB_PAD, "parallelism": "one rank of tp8 (sums pre-staged)"},
         "pct_bf16_peak": round(100 * value * 1e12 / PEAK_BF16, 2),
         "breakdown": {"layer_gflop": round(fl_layer / 1e9, 2), "xent_gflop": round(fl_xent / 1e9, 2),
@@ -243,7 +250,7 @@ def main():
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(p, xe)
+        out["cpu_baseline"] = cpu_baseline(p, xe, heads=heads)
     print(json.dumps(out), flush=True)
 
 

@@ -146,7 +146,8 @@ tp_status check_attn(const char* fn, int b, int s, int h, int heads, int t, int 
     if (heads <= 0 || heads % t != 0) return fail(TP_ERR_SHAPE, "%s: heads=%d must be a positive multiple of t=%d", fn, heads, t);
     if (h % heads != 0) return fail(TP_ERR_SHAPE, "%s: h=%d is not a multiple of heads=%d", fn, h, heads);
     int d = h / heads;
-    if (d != 64 && d != 96 && d != 128) return fail(TP_ERR_UNSUPPORTED, "%s: head width %d (supported: 64, 96, 128)", fn, d);
+    if (d != 64 && d != 96 && d != 128 && d != 192)
+        return fail(TP_ERR_UNSUPPORTED, "%s: head width %d (supported: 64, 96, 128, 192)", fn, d);
     return TP_OK;
 }
 

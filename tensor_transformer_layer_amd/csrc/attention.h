@@ -1,7 +1,8 @@
 // Causal multi-head attention for one rank's heads on gfx950, forward and backward.
 //
 // Per (sequence, head): S = Q K^T / sqrt(d), masked, P = softmax(S), O = P V, saved lse.
-// Head width D = 96 is handled as 6 k-steps of 16 (scores) and 3 tiles of 32 (outputs).
+// Head width D (64, 96, 128 or 192) is handled as D/16 k-steps of 16 (scores) and D/32 tiles of 32
+// (outputs); D = 96 is the 8.3B shape's.
 //
 // Orientation. The kernels compute S^T = K Q^T so that an MFMA accumulator lane holds ONE query
 // (column = lane % 32) and 16 keys in registers: the softmax row reductions are in-lane plus one
@@ -423,30 +424,68 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
         if (more) stash();
         __syncthreads();
     }
-    // merge: the second query half's waves hand dK, dV to the first half's wave of the same key group
-    constexpr int NV = D;   // dk (D/2) + dv (D/2) per lane
+    // merge: the second query half's waves hand dK, dV to the first half's wave of the same key
+    // group, through the tile buffers (in two rounds, dK then dV, when both do not fit at once)
     float* xch = (float*)smem;
-    static_assert(2 * NV * 64 * 4 <= 4 * ATT_B * D * 2, "exchange exceeds the tile buffers");
-    if (qh == 1) {
+    constexpr int NH = D / 2;   // floats per lane per accumulator set
+    constexpr bool ONE_ROUND = 2 * (2 * NH) * 64 * 4 <= 4 * ATT_B * D * 2;
+    static_assert(2 * NH * 64 * 4 <= 4 * ATT_B * D * 2, "exchange exceeds the tile buffers");
+    if constexpr (ONE_ROUND) {
+        if (qh == 1) {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+            for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                xch_put<NV>(xch, grp, dt * 16 + v, lane, dk[dt][v]);
-                xch_put<NV>(xch, grp, D / 2 + dt * 16 + v, lane, dv[dt][v]);
-            }
+                for (int v = 0; v < 16; ++v) {
+                    xch_put<2 * NH>(xch, grp, dt * 16 + v, lane, dk[dt][v]);
+                    xch_put<2 * NH>(xch, grp, NH + dt * 16 + v, lane, dv[dt][v]);
+                }
+        }
+        __syncthreads();
+        if (qh == 0) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    dk[dt][v] += xch_get<2 * NH>(xch, grp, dt * 16 + v, lane);
+                    dv[dt][v] += xch_get<2 * NH>(xch, grp, NH + dt * 16 + v, lane);
+                }
+        }
+    } else {
+        if (qh == 1) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) xch_put<NH>(xch, grp, dt * 16 + v, lane, dk[dt][v]);
+        }
+        __syncthreads();
+        if (qh == 0) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) dk[dt][v] += xch_get<NH>(xch, grp, dt * 16 + v, lane);
+        }
+        __syncthreads();
+        if (qh == 1) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) xch_put<NH>(xch, grp, dt * 16 + v, lane, dv[dt][v]);
+        }
+        __syncthreads();
+        if (qh == 0) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) dv[dt][v] += xch_get<NH>(xch, grp, dt * 16 + v, lane);
+        }
     }
-    __syncthreads();
     if (qh == 0 && mykey < s) {
         bf16* kp_ = dQKV + (tok0 + mykey) * ld_dq + h_t + head * D;
         bf16* vp_ = dQKV + (tok0 + mykey) * ld_dq + 2 * h_t + head * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                dk[dt][v] = (dk[dt][v] + xch_get<NV>(xch, grp, dt * 16 + v, lane)) * scale;
-                dv[dt][v] += xch_get<NV>(xch, grp, D / 2 + dt * 16 + v, lane);
-            }
+            for (int v = 0; v < 16; ++v) dk[dt][v] *= scale;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 int d = dt * 32 + 8 * i + 4 * h;

@@ -43,6 +43,7 @@ hipError_t attn_fwd(int b, int s, int h_t, int heads_t, int d, int causal, const
         case 64: return fwd_d<64>(b, s, h_t, heads_t, causal, QKV, O, lse, st);
         case 96: return fwd_d<96>(b, s, h_t, heads_t, causal, QKV, O, lse, st);
         case 128: return fwd_d<128>(b, s, h_t, heads_t, causal, QKV, O, lse, st);
+        case 192: return fwd_d<192>(b, s, h_t, heads_t, causal, QKV, O, lse, st);
     }
     return hipErrorInvalidValue;
 }
@@ -53,6 +54,7 @@ hipError_t attn_bwd(int b, int s, int h_t, int heads_t, int d, int causal, const
         case 64: return bwd_d<64>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dQKV, st);
         case 96: return bwd_d<96>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dQKV, st);
         case 128: return bwd_d<128>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dQKV, st);
+        case 192: return bwd_d<192>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dQKV, st);
     }
     return hipErrorInvalidValue;
 }

@@ -66,7 +66,7 @@ def test_attn_ragged_small(causal):
     check_attn(inp, b, s, h, heads, t, causal, f"ragged causal={causal}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 192])
 def test_attn_other_head_widths(d):
     b, s, heads, t = 1, 256, 4, 2
     h = heads * d
@@ -137,3 +137,12 @@ def test_attn_1p2b_workload_full_size():
 def test_attn_8p3b_shard_full_size():
     """The 8.3B layer's attention shard (h=3072, 32 heads, t=8), rank 0 and rank 7."""
     _sampled_full_size(tp_synth.WORKLOADS["layer_8p3b_t8"], [0, 7], seq=2)
+
+
+@pytest.mark.parametrize("heads", [16, 24])
+def test_attn_8p3b_head_sweep_full_size(heads):
+    """The pages' 8.3B head-count sweep: the same shard with 16 heads of 192 or 24 heads of 128
+    (2 or 3 heads per rank), rank 0 at full size."""
+    import dataclasses
+    w = dataclasses.replace(tp_synth.WORKLOADS["layer_8p3b_t8"], heads=heads, name=f"layer_8p3b_t8_h{heads}")
+    _sampled_full_size(w, [0], seq=3)
