@@ -32,7 +32,7 @@ from .attention import (head_columns, attn_core_fwd, attn_core_bwd, attn_fwd, at
 from .layernorm import layernorm_fwd, layernorm_bwd
 from .layer import layer_fwd, layer_bwd, layer_split_fwd, layer_split_bwd
 from .xent import (xent_full, xent_shard_stats, xent_combine, xent_two_round, vocab_shard,
-                   pad_vocab)
+                   pad_vocab, xent_full_grad, xent_shard_grad, xent_merged_stats)
 
 __all__ = [
     "gelu", "gelu_grad", "gelu_scalar",
@@ -43,4 +43,5 @@ __all__ = [
     "layernorm_fwd", "layernorm_bwd",
     "layer_fwd", "layer_bwd", "layer_split_fwd", "layer_split_bwd",
     "xent_full", "xent_shard_stats", "xent_combine", "xent_two_round", "vocab_shard", "pad_vocab",
+    "xent_full_grad", "xent_shard_grad", "xent_merged_stats",
 ]

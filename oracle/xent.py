@@ -22,7 +22,10 @@ Readings where the pages are silent or garbled:
 
 Pins: the padding arithmetic of "Megatron-LM, annotated" §3.4 (tests/golden); PyTorch CPU
 float64 cross_entropy for the unsplit loss; one-round == two-round == unsplit; argmax and max
-against numpy on the full logits.
+against numpy on the full logits. Backward: PyTorch CPU float64 autograd of the weighted
+cross-entropy (with and without the padding mask); central finite differences of the forward
+loss on every input entry; the rank split (sum of dX_r, stacked dE_r) against the unsplit
+gradients; per-token logits gradients summing to zero; the uniform-logits closed form.
 """
 import numpy as np
 
@@ -96,3 +99,52 @@ def xent_two_round(X, E, targets, t, Vreal, mask_padding=False):
         owned = (local >= 0) & (local < Vt)
         tgt += np.where(owned, y[n, np.clip(local, 0, Vt - 1)], 0.0)
     return Mx + np.log(s) - tgt
+
+
+# ------------------------------------------------------------------------------------------
+# Backward. The pages give only the forward; the gradient is the textbook derivative of the
+# same loss: d loss_n / d y_{n,v} = softmax_v(y_n) - [v == target_n]. Readings: the upstream
+# gradient is a per-token weight dloss_n (1/N for the mean loss); masked padding columns have
+# zero probability and so zero gradient; rank r's share of the logits gradient uses the merged
+# (all-rank) per-token max M and sum S = sum_v exp(y_v - M), which is what the forward's
+# exchange leaves on every rank.
+# ------------------------------------------------------------------------------------------
+def xent_full_grad(X, E, targets, Vreal, mask_padding=False, dloss=None):
+    """Unsplit gradients of sum_n dloss_n * loss_n: dlogits = dloss * (softmax(y) - onehot),
+    dX = dlogits E, dE = dlogits^T X (y = X E^T)."""
+    N = X.shape[0]
+    if dloss is None:
+        dloss = np.full(N, 1.0 / N)
+    y = _masked_logits(X, E, 0, Vreal, mask_padding)
+    m = y.max(axis=1, keepdims=True)
+    p = np.exp(y - m)
+    p = p / p.sum(axis=1, keepdims=True)
+    onehot = np.zeros_like(p)
+    onehot[np.arange(N), targets] = 1.0
+    dl = dloss[:, None] * (p - onehot)
+    return {"dlogits": dl, "dX": dl @ E, "dE": dl.T @ X}
+
+
+def xent_shard_grad(X, E_r, targets, t, r, Vreal, mask_padding, M, S, dloss):
+    """Rank r's share given the merged per-token max M and sum S (over every rank's columns):
+    dlogits_r = dloss * (exp(y_r - M) / S - onehot on the rank's columns), dX_r = dlogits_r E_r
+    (a partial; the sum over ranks is dX) and dE_r = dlogits_r^T X (rank r's rows of dE)."""
+    N, Vt = X.shape[0], E_r.shape[0]
+    col0 = r * Vt
+    y = _masked_logits(X, E_r, col0, Vreal, mask_padding)
+    p = np.exp(y - M[:, None]) / S[:, None]
+    local = targets.astype(np.int64) - col0
+    owned = (local >= 0) & (local < Vt)
+    onehot = np.zeros_like(p)
+    n = np.arange(N)
+    onehot[n[owned], local[owned]] = 1.0
+    dl = dloss[:, None] * (p - onehot)
+    return {"dlogits": dl, "dX": dl @ E_r, "dE": dl.T @ X}
+
+
+def xent_merged_stats(X, E, targets, Vreal, mask_padding=False):
+    """The merged per-token max M and sum S = sum_v exp(y_v - M) over the whole vocabulary
+    (what the forward exchange yields on every rank)."""
+    y = _masked_logits(X, E, 0, Vreal, mask_padding)
+    M = y.max(axis=1)
+    return M, np.exp(y - M[:, None]).sum(axis=1)

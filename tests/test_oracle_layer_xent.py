@@ -157,3 +157,78 @@ def test_xent_argmax_ties_lowest_index():
     st = [oracle.xent_shard_stats(X, oracle.vocab_shard(E, 2, r), np.array([0]), 2, r, 4) for r in range(2)]
     assert st[0]["argmax"][0] == 0 and st[1]["argmax"][0] == 3
     assert st[0]["max"][0] == st[1]["max"][0] == 1.0
+
+
+# ---- cross-entropy backward ----------------------------------------------------------------
+def _xent_case(seed, N, h, V, Vreal):
+    g = np.random.default_rng(seed)
+    X = g.standard_normal((N, h))
+    E = 0.3 * g.standard_normal((V, h))
+    tg = g.integers(0, Vreal, N)
+    dl = g.uniform(0.5, 1.5, N)
+    return X, E, tg, dl
+
+
+@pytest.mark.parametrize("mask", [0, 1])
+def test_xent_grad_against_torch_autograd(mask):
+    """Unsplit gradients against PyTorch CPU float64 autograd of sum_n dloss_n * cross_entropy_n."""
+    X, E, tg, dl = _xent_case(21, 9, 7, 24, 20)
+    ours = oracle.xent_full_grad(X, E, tg, 20, bool(mask), dl)
+    Xt = torch.tensor(X, requires_grad=True)
+    Et = torch.tensor(E, requires_grad=True)
+    y = Xt @ Et.T
+    if mask:
+        y = y.masked_fill(torch.arange(24)[None, :] >= 20, float("-inf"))
+    loss = (torch.tensor(dl) * torch.nn.functional.cross_entropy(y, torch.tensor(tg), reduction="none")).sum()
+    loss.backward()
+    assert np.allclose(ours["dX"], Xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(ours["dE"], Et.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_xent_grad_finite_differences():
+    """Central differences of the forward loss definition (step 1e-6) against the analytic
+    gradient, on every entry of X and of E."""
+    X, E, tg, dl = _xent_case(22, 4, 3, 10, 10)
+    gr = oracle.xent_full_grad(X, E, tg, 10, False, dl)
+
+    def L(Xv, Ev):
+        return float((dl * oracle.xent_full(Xv, Ev, tg, 10)["loss"]).sum())
+
+    eps = 1e-6
+    for A, key in ((X, "dX"), (E, "dE")):
+        num = np.zeros_like(A)
+        for idx in np.ndindex(A.shape):
+            Ap, Am = A.copy(), A.copy()
+            Ap[idx] += eps
+            Am[idx] -= eps
+            args_p = (Ap, E) if key == "dX" else (X, Ap)
+            args_m = (Am, E) if key == "dX" else (X, Am)
+            num[idx] = (L(*args_p) - L(*args_m)) / (2 * eps)
+        assert np.allclose(num, gr[key], rtol=1e-6, atol=1e-8), key
+
+
+@pytest.mark.parametrize("mask", [0, 1])
+@pytest.mark.parametrize("t", [2, 4])
+def test_xent_grad_split_sums_to_unsplit(mask, t):
+    """With the merged (M, S): sum over ranks of dX_r equals the unsplit dX, the ranks' dE_r
+    stack to the unsplit dE, and each token's logits gradient sums to zero over the vocabulary."""
+    V, Vreal = 32, 29
+    X, E, tg, dl = _xent_case(23 + t, 11, 6, V, Vreal)
+    full = oracle.xent_full_grad(X, E, tg, Vreal, bool(mask), dl)
+    M, S = oracle.xent_merged_stats(X, E, tg, Vreal, bool(mask))
+    parts = [oracle.xent_shard_grad(X, oracle.vocab_shard(E, t, r), tg, t, r, Vreal, bool(mask), M, S, dl)
+             for r in range(t)]
+    assert np.allclose(sum(p["dX"] for p in parts), full["dX"], rtol=1e-12, atol=1e-13)
+    assert np.allclose(np.concatenate([p["dE"] for p in parts]), full["dE"], rtol=1e-12, atol=1e-13)
+    rows = np.concatenate([p["dlogits"] for p in parts], axis=1).sum(axis=1)
+    assert np.allclose(rows, 0.0, atol=1e-14)
+    if mask:
+        assert np.all(np.concatenate([p["dlogits"] for p in parts], axis=1)[:, Vreal:] == 0.0)
+
+
+def test_xent_grad_uniform_logits():
+    """E = 0: every logit is 0, the softmax is uniform, dlogits = dloss * (1/V - onehot)."""
+    X, _, tg, dl = _xent_case(24, 5, 4, 8, 8)
+    gr = oracle.xent_full_grad(X, np.zeros((8, 4)), tg, 8, False, dl)
+    want = dl[:, None] * (np.full((5, 8), 1.0 / 8) - np.eye(8)[tg])
+    assert np.allclose(gr["dlogits"], want, rtol=0, atol=1e-15)
