@@ -125,6 +125,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="copy 512 MiB device-to-device once before the steps (calibrates HBM byte counters)")
+    ap.add_argument("--vocab-bwd", action="store_true",
+                    help="time the vocabulary-parallel cross-entropy backward of rank 0 instead (logits gradient "
+                         "+ dX_r + dE_r GEMMs: 3 x 322 GFLOP per call) and print its own JSON line")
     ap.add_argument("--heads", type=int, default=HEADS,
                     help="attention heads of the layer (the pages' 8.3B head-count sweep uses 16, 24, 32; the "
                          "FLOPs and all other shapes are unchanged, heads per rank = heads / 8)")
@@ -185,6 +188,8 @@ def main():
     mean = torch.empty(1, dtype=torch.float32, device=dev)
 
     stream = torch.cuda.current_stream()
+    if args.vocab_bwd:
+        return bench_vocab_bwd(args, tp, torch, T, Vt, Xv, E0, tg, peers, stream)
     xev = []
     if args.copy_probe:
         src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -252,6 +257,44 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, xe, heads=heads)
     print(json.dumps(out), flush=True)
+
+
+def bench_vocab_bwd(args, tp, torch, T, Vt, Xv, E0, tg, peers, stream):
+    """Rank 0's cross-entropy backward with the merged statistics of the (pre-staged) forward."""
+    dev = "cuda:0"
+    f32 = dict(dtype=torch.float32, device=dev)
+    loss, M, S = torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(T, **f32)
+    tp.tp_vocab_xent_combine(T, TP, [q[0] for q in peers], [q[1] for q in peers], [q[2] for q in peers], loss, None,
+                             M, S)
+    g = torch.full((T,), 1.0 / T, **f32)
+    dX = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    dE = torch.empty((Vt, H), dtype=torch.bfloat16, device=dev)
+    nb = tp.tp_vocab_xent_shard_bwd_workspace(T, H, VOCAB_PAD, TP, tp.TP_BF16)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+    def call():
+        tp.tp_vocab_xent_shard_bwd(T, H, VOCAB_PAD, VOCAB, TP, 0, tp.TP_BF16, 0, Xv, E0, tg, M, S, g, dX, dE, 0, ws, nb)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    fl = 3 * xent_flops(T, H, Vt)
+    value = fl / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "vocab-parallel cross-entropy backward TFLOP/s, 8.3B vocabulary shard t=8, 1 GPU",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) embedding, uniform targets)",
+        "config": {"workload": "rank 0 vocab shard backward: logits gradient + dX_r + dE_r", "tokens": T,
+                   "hidden": H, "vocab_padded": VOCAB_PAD, "tp": TP},
+        "pct_bf16_peak": round(100 * value * 1e12 / PEAK_BF16, 2)}), flush=True)
 
 
 if __name__ == "__main__":

@@ -160,10 +160,31 @@ tp_status tp_vocab_logits_shard(int N, int h, int Vpad, int t, int r, tp_dtype d
 /* Merge of t ranks' statistics into per-token losses, standing in for the cross-entropy's
  * all-reduces on one device: M = max_r max_r; S = sum_r sumexp_r exp(max_r - M);
  * loss = M + log S - sum_r tgt_r. max_r/sumexp_r/tgt_r are HOST arrays of t device pointers.
- * loss [N] fp32; mean_loss (1 float, may be NULL) gets the mean over N. */
+ * loss [N] fp32; mean_loss (1 float, may be NULL) gets the mean over N; max_all and sumexp_all
+ * ([N] fp32, may be NULL) receive M and S, the merged statistics the backward needs. */
 tp_status tp_vocab_xent_combine(int N, int t, const float* const* max_r, const float* const* sumexp_r,
                                 const float* const* tgt_r, float* loss, float* mean_loss,
-                                hipStream_t stream);
+                                float* max_all, float* sumexp_all, hipStream_t stream);
+
+/* Backward of the vocabulary-parallel cross-entropy for rank r (the pages give the forward,
+ * "Megatron-LM ..." digest §3.4 steps 1-6; the gradient is the textbook derivative of the same
+ * loss). With the merged per-token statistics M = max_all and S = sumexp_all (from
+ * tp_vocab_xent_combine) and the upstream gradient dloss ([N] fp32; 1/N each for the mean loss):
+ *   dlogits[n, v] = dloss[n] * (exp(y[n, v] - M[n]) / S[n] - [r*V_t + v == targets[n]])
+ * over the rank's columns (0 on padding columns when mask_padding = 1), y = X E_r^T recomputed
+ * (the logits are never kept), and
+ *   dX_r [N, h]  = dlogits E_r    a full-size partial: the sum over ranks is dL/dX (the f point)
+ *   dE_r [V_t, h] (+)= dlogits^T X   rank r's rows of dL/dE (accumulate = 1 adds, for the tied
+ *                                    input embedding's share)
+ * X, E_r, dX_r, dE_r in bf16 (dt = TP_BF16 only), row-major. The workspace holds dlogits twice in
+ * bf16 (vocabulary-major and token-major, 2 x V_t x N elements, the token count rounded up to 8
+ * in the first). N = 0 writes zeros into dE_r (or leaves it unchanged when accumulating). */
+size_t tp_vocab_xent_shard_bwd_workspace(int N, int h, int Vpad, int t, tp_dtype dt);
+tp_status tp_vocab_xent_shard_bwd(int N, int h, int Vpad, int Vreal, int t, int r, tp_dtype dt,
+                                  int mask_padding, const void* X, const void* E_r,
+                                  const int32_t* targets, const float* max_all,
+                                  const float* sumexp_all, const float* dloss, void* dX_r, void* dE_r,
+                                  int accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Helpers for the replicated parts of the layer ("Megatron-LM ..." digest §3.4, "Duplicate

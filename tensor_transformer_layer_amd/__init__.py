@@ -52,7 +52,9 @@ SIGNATURES = {
     "tp_vocab_xent_shard_fwd_workspace": (_z, [_i, _i, _i, _i, _i]),
     "tp_vocab_xent_shard_fwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _z, _p]),
     "tp_vocab_logits_shard": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p]),
-    "tp_vocab_xent_combine": (_i, [_i, _i, _pp, _pp, _pp, _p, _p, _p]),
+    "tp_vocab_xent_combine": (_i, [_i, _i, _pp, _pp, _pp, _p, _p, _p, _p, _p]),
+    "tp_vocab_xent_shard_bwd_workspace": (_z, [_i, _i, _i, _i, _i]),
+    "tp_vocab_xent_shard_bwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
     "tp_sum_partials": (_i, [_i, _i, _i, _i, _pp, _p, _p, _p, _i, _p]),
     "tp_sum_partials_layernorm": (_i, [_i, _i, _i, _i, _pp, _p, _p, _p, _f, _p, _p, _p, _p, _p, _p]),
     "tp_layernorm_fwd": (_i, [_i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p]),
@@ -161,11 +163,24 @@ def tp_vocab_logits_shard(N, h, Vpad, t, r, dt, X, E_r, logits, stream=None):
     _check(lib.tp_vocab_logits_shard(N, h, Vpad, t, r, _dt(dt), _ptr(X), _ptr(E_r), _ptr(logits), _stream(stream)))
 
 
-def tp_vocab_xent_combine(N, t, max_r, sumexp_r, tgt_r, loss, mean_loss=None, stream=None):
+def tp_vocab_xent_combine(N, t, max_r, sumexp_r, tgt_r, loss, mean_loss=None, max_all=None, sumexp_all=None,
+                          stream=None):
     pm, _a = _ptr_array(max_r)
     ps, _b = _ptr_array(sumexp_r)
     pt, _c = _ptr_array(tgt_r)
-    _check(lib.tp_vocab_xent_combine(N, t, pm, ps, pt, _ptr(loss), _ptr(mean_loss), _stream(stream)))
+    _check(lib.tp_vocab_xent_combine(N, t, pm, ps, pt, _ptr(loss), _ptr(mean_loss), _ptr(max_all), _ptr(sumexp_all),
+                                     _stream(stream)))
+
+
+def tp_vocab_xent_shard_bwd_workspace(N, h, Vpad, t, dt):
+    return lib.tp_vocab_xent_shard_bwd_workspace(N, h, Vpad, t, _dt(dt))
+
+
+def tp_vocab_xent_shard_bwd(N, h, Vpad, Vreal, t, r, dt, mask_padding, X, E_r, targets, max_all, sumexp_all, dloss,
+                            dX_r, dE_r, accumulate, ws, ws_bytes, stream=None):
+    _check(lib.tp_vocab_xent_shard_bwd(N, h, Vpad, Vreal, t, r, _dt(dt), mask_padding, _ptr(X), _ptr(E_r),
+                                       _ptr(targets), _ptr(max_all), _ptr(sumexp_all), _ptr(dloss), _ptr(dX_r),
+                                       _ptr(dE_r), accumulate, _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def tp_sum_partials(rows, cols, t, in_dt, parts, bias, residual, out, out_dt, stream=None):

@@ -350,8 +350,57 @@ tp_status tp_vocab_logits_shard(int N, int h, int Vpad, int t, int r, tp_dtype d
     return ok();
 }
 
+// dlogits copies: vocab-major [Vt][ldd] (ldd = N rounded up to 8) and token-major [N][Vt]
+static size_t xent_bwd_ld(int N) { return ((size_t)N + 7) / 8 * 8; }
+size_t tp_vocab_xent_shard_bwd_workspace(int N, int h, int Vpad, int t, tp_dtype dt) {
+    (void)h; (void)dt;
+    if (N < 0 || t < 1 || Vpad <= 0 || Vpad % t) return 0;
+    const size_t Vt = (size_t)(Vpad / t);
+    return al256(Vt * xent_bwd_ld(N) * 2) + al256((size_t)N * Vt * 2);
+}
+
+tp_status tp_vocab_xent_shard_bwd(int N, int h, int Vpad, int Vreal, int t, int r, tp_dtype dt, int mask_padding,
+                                  const void* X, const void* E_r, const int32_t* targets, const float* max_all,
+                                  const float* sumexp_all, const float* dloss, void* dX_r, void* dE_r, int accumulate,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "tp_vocab_xent_shard_bwd";
+    tp_status st = check_vocab(fn, N, h, Vpad, t, r, dt);
+    if (st != TP_OK) return st;
+    if (Vreal <= 0 || Vreal > Vpad) return fail(TP_ERR_SHAPE, "%s: Vreal=%d must be in [1, Vpad=%d]", fn, Vreal, Vpad);
+    if (mask_padding != 0 && mask_padding != 1) return fail(TP_ERR_ARG, "%s: mask_padding=%d must be 0 or 1", fn, mask_padding);
+    if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_ARG, "%s: accumulate=%d must be 0 or 1", fn, accumulate);
+    NEED(X); NEED(E_r); NEED(targets); NEED(max_all); NEED(sumexp_all); NEED(dloss); NEED(dX_r); NEED(dE_r);
+    const int Vt = Vpad / t;
+    const size_t need = tp_vocab_xent_shard_bwd_workspace(N, h, Vpad, t, dt);
+    if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    if (need > 0) NEED(ws);
+    const int ldd = (int)xent_bwd_ld(N);
+    void* D = ws;
+    void* DT = (char*)ws + al256((size_t)Vt * ldd * 2);
+    GemmReq g;
+    if (N > 0) {
+        // 1. logits again (E_r X^T), their gradient in the epilogue, stored in both layouts
+        g = req(Vt, N, h, E_r, h, 0, X, h, 0, EPI_XENT_GRAD, D, ldd);
+        g.out2 = DT; g.ld2 = Vt;
+        g.targets = targets; g.col0 = r * Vt; g.Vreal = Vreal; g.mask = mask_padding;
+        g.stat_m = max_all; g.stat_s = sumexp_all; g.dloss = dloss;
+        HIP_TRY(gemm_bf16(g, plan_gemm_bf16(Vt, N, h, false), nullptr, stream),
+                "tp_vocab_xent_shard_bwd: logits gradient");
+        // 2. dX_r = dlogits E_r   (token-major dlogits, E_r read MN-contiguous)
+        g = req(N, h, Vt, DT, Vt, 0, E_r, h, 1, EPI_STORE, dX_r, h);
+        HIP_TRY(gemm_bf16(g, plan_gemm_bf16(N, h, Vt, false), nullptr, stream), "tp_vocab_xent_shard_bwd: dX GEMM");
+    }
+    // 3. dE_r (+)= dlogits^T X   (vocab-major dlogits, X read MN-contiguous; with no tokens the
+    //    K = 0 product writes zeros, or leaves dE_r unchanged when accumulating)
+    g = req(Vt, h, N, D, ldd, 0, X, h, 1, EPI_STORE, dE_r, h);
+    g.accumulate = accumulate;
+    HIP_TRY(gemm_bf16(g, plan_gemm_bf16(Vt, h, N, false), nullptr, stream), "tp_vocab_xent_shard_bwd: dE GEMM");
+    return ok();
+}
+
 tp_status tp_vocab_xent_combine(int N, int t, const float* const* max_r, const float* const* sumexp_r,
-                                const float* const* tgt_r, float* loss, float* mean_loss, hipStream_t stream) {
+                                const float* const* tgt_r, float* loss, float* mean_loss, float* max_all,
+                                float* sumexp_all, hipStream_t stream) {
     const char* fn = "tp_vocab_xent_combine";
     if (t < 1 || t > 64) return fail(TP_ERR_ARG, "%s: t=%d must be in [1, 64]", fn, t);
     if (N < 0) return fail(TP_ERR_SHAPE, "%s: N=%d is negative", fn, N);
@@ -360,7 +409,9 @@ tp_status tp_vocab_xent_combine(int N, int t, const float* const* max_r, const f
         if (!max_r[i] || !sumexp_r[i] || !tgt_r[i]) return fail(TP_ERR_ARG, "%s: rank %d pointer is NULL", fn, i);
     NEED(loss);
     if (N == 0) return ok();
-    HIP_TRY(xent_combine(N, t, max_r, sumexp_r, tgt_r, loss, mean_loss, stream), "tp_vocab_xent_combine");
+    OPT(max_all); OPT(sumexp_all);
+    HIP_TRY(xent_combine(N, t, max_r, sumexp_r, tgt_r, loss, mean_loss, max_all, sumexp_all, stream),
+            "tp_vocab_xent_combine");
     return ok();
 }
 

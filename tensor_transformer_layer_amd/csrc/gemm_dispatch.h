@@ -74,6 +74,14 @@ static hipError_t gemm_run(const GemmReq& r, const GemmPlan& p, void* ws, hipStr
             if constexpr ((KINDS & (1 << EPI_XENT)) != 0)
                 return launch_plan<LA, LB>(r, p, EpiXent{(XentPartial*)r.out, r.targets, r.col0, r.Vreal, r.mask}, st);
             break;
+        case EPI_XENT_GRAD:
+            if constexpr ((KINDS & (1 << EPI_XENT_GRAD)) != 0) {
+                if (r.ldc % 8 != 0 || r.ldc < r.N || r.ld2 % 4 != 0) return hipErrorInvalidValue;
+                return launch_plan<LA, LB>(r, p, EpiXentGrad{(bf16*)r.out, r.ldc, (bf16*)r.out2, r.ld2, r.stat_m,
+                                                             r.stat_s, r.dloss, r.targets, r.col0, r.Vreal, r.mask},
+                                           st);
+            }
+            break;
     }
     return hipErrorInvalidValue;
 }

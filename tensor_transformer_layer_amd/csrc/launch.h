@@ -13,6 +13,7 @@ enum EpiKind {
     EPI_DGELU = 2,      // out = acc * GeLU'(aux)
     EPI_STORE_T = 3,    // fp32 out[col*ldc + row] = acc (transposed store)
     EPI_XENT = 4,       // cross-entropy tile statistics (xent.h)
+    EPI_XENT_GRAD = 5,  // cross-entropy logits gradient, stored vocab-major and token-major (xent.h)
 };
 
 // C[M,N] = sum_k A(m,k) B(k,n). a_mn / b_mn: operand is MN-contiguous (element (mn,k) at
@@ -24,8 +25,10 @@ struct GemmReq {
     int epi;
     void* out; void* out2; int ldc;
     const void* bias; const void* aux; int accumulate;
-    // EPI_XENT
+    // EPI_XENT, EPI_XENT_GRAD
     const int32_t* targets; int col0, Vreal, mask;
+    // EPI_XENT_GRAD: merged per-token max and sum, upstream gradient; out2 = token-major copy (ld2)
+    const float* stat_m; const float* stat_s; const float* dloss; int ld2;
 };
 
 struct GemmPlan {
@@ -61,7 +64,7 @@ size_t xent_tiles_m(int Vt);
 hipError_t xent_merge(const void* part, int tiles_m, int N, int col0, float* mx, float* se, float* tg,
                       int32_t* am, hipStream_t st);
 hipError_t xent_combine(int N, int t, const float* const* mx, const float* const* se, const float* const* tg,
-                        float* loss, float* mean, hipStream_t st);
+                        float* loss, float* mean, float* max_all, float* sumexp_all, hipStream_t st);
 
 // Norm / elementwise (dt: 0 fp32, 1 bf16)
 int ln_bwd_blocks(int rows);

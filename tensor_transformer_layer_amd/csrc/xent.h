@@ -120,4 +120,66 @@ struct EpiXent {
     }
 };
 
+// ---------------------------------------------------------------------------------------------
+// Logits gradient of the vocabulary-parallel cross-entropy (the backward of the fused logits). The
+// GEMM recomputes C[v][n] = E_r[v] . X[n]; the epilogue turns each logit into
+//     dl = dloss_n * (exp(y - M_n) / S_n - [v == target_n]),     0 on masked padding rows,
+// with the merged (all-rank) per-token max M and sum S, and stores it twice in bf16: token-major
+// DT[n][v] straight from the accumulator layout (a lane holds 4 consecutive vocabulary rows of
+// one token: 8-byte stores) and vocab-major D[v][n] through the staged row-major epilogue. The two
+// copies feed dX_r = DT E_r and dE_r = D X, both with a K-contiguous A operand.
+// ---------------------------------------------------------------------------------------------
+struct EpiXentGrad {
+    static constexpr bool kVec8 = false;
+    bf16* D; int ldd;          // [Vt][ldd], ldd >= N, multiple of 8
+    bf16* DT; int ldt;         // [N][ldt], ldt = Vt
+    const float* Mx; const float* Sx; const float* g; const int32_t* targets;
+    int col0, Vreal, mask;
+    __device__ __forceinline__ void set_split(int) {}
+
+    struct StoreRows {   // op8 for the staged pass: 8 consecutive tokens of one vocabulary row
+        bf16* out; int ld;
+        __device__ __forceinline__ void op8(int r, int c, float (&v)[8]) const { store8(out + (size_t)r * ld + c, v); }
+    };
+
+    template <class C>
+    __device__ __forceinline__ void apply(f32x16 (&acc)[C::TM][C::TN], int m0, int n0, int mw0, int nw0, int lane,
+                                          int M, int N, char* smem) const {
+        const int h = lane >> 5, l32 = lane & 31;
+        constexpr float kL2e = 1.4426950408889634f;
+        const bool full = (mw0 + C::WM <= M) && (!mask || col0 + mw0 + C::WM <= Vreal);
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const int n = nw0 + j * 32 + l32;
+            const bool vn = n < N;
+            const float nb = vn ? -Mx[n] * kL2e : 0.f;
+            const float inv = vn ? 1.0f / Sx[n] : 0.f;
+            const float gn = vn ? g[n] : 0.f;
+            const int trow = vn ? targets[n] - col0 : -1;
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = mw0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    float p = __builtin_amdgcn_exp2f(fmaf(acc[i][j][v], kL2e, nb)) * inv;
+                    if (!full && mask && col0 + row >= Vreal) p = 0.f;
+                    acc[i][j][v] = gn * (p - (row == trow ? 1.0f : 0.0f));
+                }
+            if (vn) {
+                bf16* dt = DT + (size_t)n * ldt;
+#pragma unroll
+                for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int row = mw0 + i * 32 + 8 * q + 4 * h;
+                        if (row < M)
+                            *(u32x2*)(dt + row) = u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                                        pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+                    }
+            }
+        }
+        apply_staged<C>(StoreRows{D, ldd}, acc, mw0, nw0, lane, (int)(threadIdx.x >> 6), M, N, smem);
+    }
+};
+
 }  // namespace tp

@@ -59,7 +59,8 @@ struct XentPtrs {
 // loss_n = M + log(sum_r se_r exp(mx_r - M)) - sum_r tg_r: the global max first, then the sums
 // relative to it, ranks in order. Ranks are read eight at a time so their loads are in flight
 // together.
-__global__ __launch_bounds__(64) void xent_combine_kernel(int N, int t, XentPtrs p, float* __restrict__ loss) {
+__global__ __launch_bounds__(64) void xent_combine_kernel(int N, int t, XentPtrs p, float* __restrict__ loss,
+                                                          float* __restrict__ max_all, float* __restrict__ sumexp_all) {
     int n = blockIdx.x * 64 + threadIdx.x;
     if (n >= N) return;
     float M = -INFINITY;
@@ -87,6 +88,8 @@ __global__ __launch_bounds__(64) void xent_combine_kernel(int N, int t, XentPtrs
         }
     }
     loss[n] = M + logf(S) - T;
+    if (max_all) max_all[n] = M;
+    if (sumexp_all) sumexp_all[n] = S;
 }
 
 // mean of x[0..N) with one block, fixed order: each thread sums a stride with four running
@@ -119,11 +122,11 @@ hipError_t xent_merge(const void* part, int tiles_m, int N, int col0, float* mx,
 }
 
 hipError_t xent_combine(int N, int t, const float* const* mx, const float* const* se, const float* const* tg,
-                        float* loss, float* mean, hipStream_t st) {
+                        float* loss, float* mean, float* max_all, float* sumexp_all, hipStream_t st) {
     if (N == 0) return hipSuccess;
     XentPtrs p;
     for (int r = 0; r < t; ++r) { p.mx[r] = mx[r]; p.se[r] = se[r]; p.tg[r] = tg[r]; }
-    hipLaunchKernelGGL(xent_combine_kernel, dim3((N + 63) / 64), dim3(64), 0, st, N, t, p, loss);
+    hipLaunchKernelGGL(xent_combine_kernel, dim3((N + 63) / 64), dim3(64), 0, st, N, t, p, loss, max_all, sumexp_all);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !mean) return e;
     hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, st, (const float*)loss, N, mean);

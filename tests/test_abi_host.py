@@ -125,3 +125,21 @@ def test_sum_partials_layernorm_argument_errors():
     assert call(y=None) == tp.TP_ERR_ARG
     bad, _k2 = tp._ptr_array([FAKE, None])
     assert call(parts=bad) == tp.TP_ERR_ARG
+
+
+def test_vocab_bwd_argument_errors():
+    f = tp.lib.tp_vocab_xent_shard_bwd
+    need = tp.lib.tp_vocab_xent_shard_bwd_workspace(16, 64, 1024, 8, tp.TP_BF16)
+    assert need >= 2 * 16 * 128 * 2
+    p = [FAKE] * 6   # X, E_r, targets, max_all, sumexp_all, dloss
+
+    def call(N=16, Vpad=1024, Vreal=1000, mask=0, acc=0, dt=tp.TP_BF16, ptrs=p, dX=FAKE, dE=FAKE, wsb=need):
+        return f(N, 64, Vpad, Vreal, 8, 0, dt, mask, *ptrs, dX, dE, acc, FAKE, wsb, None)
+
+    assert call(Vreal=1025) == tp.TP_ERR_SHAPE
+    assert call(mask=2) == tp.TP_ERR_ARG
+    assert call(acc=2) == tp.TP_ERR_ARG
+    assert call(dt=tp.TP_F32) == tp.TP_ERR_UNSUPPORTED
+    assert call(ptrs=[FAKE] * 5 + [None]) == tp.TP_ERR_ARG
+    assert call(dE=None) == tp.TP_ERR_ARG
+    assert call(wsb=need - 1) == tp.TP_ERR_WORKSPACE
