@@ -98,7 +98,35 @@ def cpu_baseline(p, xe, seqs=8, heads=HEADS):
     bq = oracle.qkv_shard(p["bqkv"], heads, TP, 0)
     Wo_r = oracle.wo_shard(p["Wo"], heads, TP, 0)
     A_r, b1_r, B_r = p["A"][:, :Ft], p["b1"][:Ft], p["B"][:Ft]
-    t0 = time.perf_counter()
+
+    def run():
+        _oracle_step(oracle, p, xe, x, G, Wqkv_r, bq, Wo_r, A_r, b1_r, B_r, seqs, heads)
+
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    flops = layer_flops(seqs, S, H, heads, FFN, TP) + xent_flops(T, H, Vt)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except Exception:
+        cores = os.cpu_count()
+    blas = "unknown BLAS"
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('num_threads')} threads" for i in threadpool_info()}))
+    except Exception:
+        pass
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"rank 0 step (layer fwd+bwd + vocab-shard statistics) on {seqs} of {B} sequences "
+                      f"({T} tokens), float64 NumPy, median of 3 runs ({', '.join(f'{t:.1f}' for t in times)} s); "
+                      f"{cores} cores in the affinity mask, {blas}"}
+
+
+def _oracle_step(oracle, p, xe, x, G, Wqkv_r, bq, Wo_r, A_r, b1_r, B_r, seqs, heads):
+    T = seqs * S
     l1 = oracle.layernorm_fwd(x, p["ln1_g"], p["ln1_b"])
     fa = oracle.attn_shard_fwd(l1["y"], Wqkv_r, bq, Wo_r, seqs, S, heads // TP)
     x1 = x + fa["Z"] + p["bo"]                 # rank 0's partial stands in for the all-reduced sum
@@ -110,11 +138,6 @@ def cpu_baseline(p, xe, seqs=8, heads=HEADS):
     ga = oracle.attn_shard_bwd(l1["y"], Wqkv_r, Wo_r, fa, dx1, seqs, S, heads // TP)
     oracle.layernorm_bwd(x, p["ln1_g"], l1["mean"], l1["rstd"], ga["dXn"])
     oracle.xent_shard_stats(xe["X"][:T], xe["E0"], xe["targets"][:T], TP, 0, VOCAB)
-    dt = time.perf_counter() - t0
-    flops = layer_flops(seqs, S, H, heads, FFN, TP) + xent_flops(T, H, Vt)
-    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"rank 0 step (layer fwd+bwd + vocab-shard statistics) on {seqs} of {B} sequences "
-                      f"({T} tokens), float64 NumPy, {dt:.1f} s"}
 
 
 def main():
@@ -199,7 +222,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    step_ev = []
+
     def step(record):
+        if record:
+            s0 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
         rank0.step(x, G, attn_sum, mlp_sum, dxn2_sum, dxn1_sum)
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -210,6 +238,10 @@ def main():
             e1.record(stream)
             xev.append((e0, e1))
         tp.tp_vocab_xent_combine(T, TP, [q[0] for q in peers], [q[1] for q in peers], [q[2] for q in peers], loss, mean)
+        if record:
+            s1 = torch.cuda.Event(enable_timing=True)
+            s1.record(stream)
+            step_ev.append((s0, s1))
 
     for _ in range(args.warmup):
         step(False)
@@ -226,6 +258,7 @@ def main():
     value = (fl_layer + fl_xent) / (ms * 1e-3) / 1e12
     xent_ms = float(np.mean([a.elapsed_time(b_) for a, b_ in xev]))
     xent_achieved = fl_xent / (xent_ms * 1e-3) / 1e12
+    per_step = np.array([a.elapsed_time(b_) for a, b_ in step_ev])
 
     out = {
         "metric": "layer-shard TFLOP/s fwd+bwd (% bf16 MFMA peak), 8.3B shape t=8, 1 GPU",
@@ -244,6 +277,7 @@ def main():
                    "batch": B, "seq_len": S, "hidden": H, "heads": heads, "ffn": FFN, "tp": TP,
                    "vocab_padded": VOCAB_PAD, "parallelism": "one rank of tp8 (sums pre-staged)"},
         "pct_bf16_peak": round(100 * value * 1e12 / PEAK_BF16, 2),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
         "breakdown": {"layer_gflop": round(fl_layer / 1e9, 2), "xent_gflop": round(fl_xent / 1e9, 2),
                       "xent_ms": round(xent_ms, 4),
                       "layer_ms": round(ms - xent_ms, 4),
