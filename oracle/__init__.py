@@ -5,7 +5,8 @@ TEST INFRASTRUCTURE ONLY. Only the test suite, the package's smoke check and the
 routes through it, and it shares no code with the GPU library: it imports nothing from
 ``tensor_transformer_layer_amd`` and reads no file that the library writes.
 
-Every function is a plain, unfused, float64 definition written from the pages:
+Every function is a plain, unfused, float64 definition written from the pages (``fp8`` holds
+the library's own 8-bit scheme, which the pages do not define; its header says so):
 
 * "Megatron-LM: Training Multi-Billion Parameter Language Models Using Model Parallelism"
   (paper digest), §3.4 Detailed, Sentence-Based Technical Breakdown;
@@ -33,6 +34,7 @@ from .layernorm import layernorm_fwd, layernorm_bwd
 from .layer import layer_fwd, layer_bwd, layer_split_fwd, layer_split_bwd
 from .xent import (xent_full, xent_shard_stats, xent_combine, xent_two_round, vocab_shard,
                    pad_vocab, xent_full_grad, xent_shard_grad, xent_merged_stats)
+from . import fp8
 
 __all__ = [
     "gelu", "gelu_grad", "gelu_scalar",
@@ -43,5 +45,5 @@ __all__ = [
     "layernorm_fwd", "layernorm_bwd",
     "layer_fwd", "layer_bwd", "layer_split_fwd", "layer_split_bwd",
     "xent_full", "xent_shard_stats", "xent_combine", "xent_two_round", "vocab_shard", "pad_vocab",
-    "xent_full_grad", "xent_shard_grad", "xent_merged_stats",
+    "xent_full_grad", "xent_shard_grad", "xent_merged_stats", "fp8",
 ]
