@@ -16,9 +16,9 @@ Everything below is therefore the library's own scheme, written out as definitio
   is even; magnitudes above 448 saturate to 448; the sign is kept (so -0 and tiny negatives give
   code 0x80); NaN gives 0x7F.
 * Per-tensor scaling: amax = max |x| over the tensor; the scale is 2^e with e the largest
-  integer such that amax * 2^e <= 448 (e = 0 when amax = 0), clamped to [-126, 127]. A power of
-  two makes x * 2^e exact, so the only rounding is the conversion itself, and 2^-e undoes the
-  scale exactly.
+  integer such that amax * 2^e <= 448 (e = 0 when amax = 0 or is not finite), clamped to
+  [-126, 126] so that 2^e and 2^-e are both normal fp32 numbers. A power of two makes x * 2^e
+  exact, so the only rounding is the conversion itself, and 2^-e undoes the scale exactly.
 * GEMM: C[m, n] = 2^-(e_a + e_b) * sum_k dec(a[m, k]) * dec(b[n, k]) in fp64, with both code
   matrices K-contiguous (a is [M, K], b is [N, K]).
 
@@ -90,7 +90,7 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
 
 
 def scale_exponent(amax: float) -> int:
-    """Largest integer e with amax * 2^e <= 448, clamped to [-126, 127]; 0 for amax = 0.
+    """Largest integer e with amax * 2^e <= 448, clamped to [-126, 126]; 0 for amax = 0.
 
     Found by the defining inequality itself: a first guess from log2, then moved by whole
     steps until amax * 2^e <= 448 < amax * 2^(e+1) holds (products by powers of two are exact
@@ -104,7 +104,7 @@ def scale_exponent(amax: float) -> int:
         e -= 1
     while math.ldexp(amax, e + 1) <= E4M3_MAX:
         e += 1
-    return max(-126, min(127, e))
+    return max(-126, min(126, e))
 
 
 def quantize(x: np.ndarray):
