@@ -236,6 +236,49 @@ size_t tp_colsum_workspace(int T, int n, tp_dtype dt);
 tp_status tp_colsum(int T, int n, tp_dtype dt, const void* G, void* out, int accumulate,
                     void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * fp8 GEMMs for the layer shard (8-bit E4M3 operands, fp32 accumulation, bf16 outputs).
+ * The pages train in 16-bit floating point with dynamic loss scaling ("Megatron-LM, annotated",
+ * §4.2 Training optimization and hyperparameters) and define no 8-bit format; the scheme here is
+ * this library's own. Format: OCP E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * largest finite 448; 0x7F/0xFF are NaN; no infinities).
+ * ------------------------------------------------------------------------------------------- */
+typedef enum tp_epilogue {
+    TP_EPI_STORE = 0,      /* C = P (+ bias[n]) (+ C if accumulate) */
+    TP_EPI_BIAS_GELU = 1,  /* C = P (+ bias[n]) (the pre-activation U), C2 = GeLU(C) (erf form) */
+    TP_EPI_DGELU = 2       /* C = P * GeLU'(aux[m, n]) (aux = U, row stride ldc) */
+} tp_epilogue;
+
+/* Per-tensor quantisation of x [rows, cols] (row stride ldx, dt = TP_BF16 or TP_F32):
+ *   amax = max |x|; e = the largest integer with amax * 2^e <= 448 (0 when amax is 0 or not
+ *   finite), clamped to [-126, 126]; code = E4M3(x * 2^e), round to nearest even, saturating
+ *   at +-448 (x * 2^e is exact, so this is the only rounding); *descale = 2^-e.
+ * Outputs (device memory): codes [rows, ldc] (row layout) and/or codes_t [cols, ldt] (the
+ * transpose, for GEMMs whose reduction runs over x's rows); either may be NULL, not both.
+ * amax (one float) may be NULL; descale (one float) is required. The workspace holds the amax
+ * partials. NaN inputs are outside the contract (the max ignores them). cols % 8 == 0,
+ * ldx % 8 == 0, ldc and ldt multiples of 16. rows or cols = 0 writes descale = 1 (and amax = 0). */
+size_t tp_fp8_quantize_workspace(int rows, int cols);
+tp_status tp_fp8_quantize(int rows, int cols, tp_dtype dt, const void* x, int ldx, uint8_t* codes,
+                          int ldc, uint8_t* codes_t, int ldt, float* amax, float* descale,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* P[M, N] = (*a_descale) * (*b_descale) * sum_k dec(A[m, k]) * dec(B[n, k]) with A [M, lda] and
+ * B [N, ldb] E4M3 code matrices, both K-contiguous (row strides in bytes), fp32 accumulation,
+ * then the epilogue `epi` (tp_epilogue) into bf16 C [M, ldc] (and C2 for TP_EPI_BIAS_GELU).
+ * The descales are device pointers to one float each, normally those tp_fp8_quantize wrote.
+ * In the layer: X A_r is A = codes of X, B = codes_t of A_r; the input gradient G W^T is
+ * A = codes of G, B = codes of W; a weight gradient X^T G is A = codes_t of X, B = codes_t of G.
+ * K % 16 == 0, lda and ldb multiples of 16 and >= K, N % 8 == 0, ldc % 8 == 0 and >= N.
+ * accumulate (0/1) only with TP_EPI_STORE; bias is bf16 [N] or NULL (not with TP_EPI_DGELU).
+ * ws: with TP_EPI_STORE and ws_bytes >= tp_gemm_fp8_workspace(M, N, K), the call may split K
+ * (fp32 partials in ws, summed in a fixed order); otherwise ws is unused and may be NULL. */
+size_t tp_gemm_fp8_workspace(int M, int N, int K);
+tp_status tp_gemm_fp8(int M, int N, int K, const uint8_t* A, int lda, const float* a_descale,
+                      const uint8_t* B, int ldb, const float* b_descale, int epi, void* C, void* C2,
+                      int ldc, const void* bias, const void* aux, int accumulate, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libtpshard.so")
 
 TP_OK, TP_ERR_ARG, TP_ERR_SHAPE, TP_ERR_DTYPE, TP_ERR_WORKSPACE, TP_ERR_HIP, TP_ERR_UNSUPPORTED = range(7)
 TP_F32, TP_BF16 = 0, 1
+TP_EPI_STORE, TP_EPI_BIAS_GELU, TP_EPI_DGELU = 0, 1, 2
 STATUS_NAMES = {0: "TP_OK", 1: "TP_ERR_ARG", 2: "TP_ERR_SHAPE", 3: "TP_ERR_DTYPE", 4: "TP_ERR_WORKSPACE",
                 5: "TP_ERR_HIP", 6: "TP_ERR_UNSUPPORTED"}
 
@@ -62,6 +63,10 @@ SIGNATURES = {
     "tp_layernorm_bwd": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
     "tp_colsum_workspace": (_z, [_i, _i, _i]),
     "tp_colsum": (_i, [_i, _i, _i, _p, _p, _i, _p, _z, _p]),
+    "tp_fp8_quantize_workspace": (_z, [_i, _i]),
+    "tp_fp8_quantize": (_i, [_i, _i, _i, _p, _i, _p, _i, _p, _i, _p, _p, _p, _z, _p]),
+    "tp_gemm_fp8_workspace": (_z, [_i, _i, _i]),
+    "tp_gemm_fp8": (_i, [_i, _i, _i, _p, _i, _p, _p, _i, _p, _i, _p, _p, _i, _p, _p, _i, _p, _z, _p]),
 }
 for _name, (_rt, _at) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -217,3 +222,22 @@ def tp_colsum_workspace(T, n, dt):
 
 def tp_colsum(T, n, dt, G, out, accumulate, ws, ws_bytes, stream=None):
     _check(lib.tp_colsum(T, n, _dt(dt), _ptr(G), _ptr(out), accumulate, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tp_fp8_quantize_workspace(rows, cols):
+    return lib.tp_fp8_quantize_workspace(rows, cols)
+
+
+def tp_fp8_quantize(rows, cols, dt, x, ldx, codes, ldc, codes_t, ldt, amax, descale, ws, ws_bytes, stream=None):
+    _check(lib.tp_fp8_quantize(rows, cols, _dt(dt), _ptr(x), ldx, _ptr(codes), ldc, _ptr(codes_t), ldt, _ptr(amax),
+                               _ptr(descale), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tp_gemm_fp8_workspace(M, N, K):
+    return lib.tp_gemm_fp8_workspace(M, N, K)
+
+
+def tp_gemm_fp8(M, N, K, A, lda, a_descale, B, ldb, b_descale, epi, C_, C2, ldc, bias, aux, accumulate, ws,
+                ws_bytes, stream=None):
+    _check(lib.tp_gemm_fp8(M, N, K, _ptr(A), lda, _ptr(a_descale), _ptr(B), ldb, _ptr(b_descale), epi, _ptr(C_),
+                           _ptr(C2), ldc, _ptr(bias), _ptr(aux), accumulate, _ptr(ws), ws_bytes, _stream(stream)))

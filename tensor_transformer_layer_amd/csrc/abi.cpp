@@ -523,4 +523,77 @@ tp_status tp_colsum(int T, int n, tp_dtype dt, const void* G, void* out, int acc
     return ok();
 }
 
+/* ---- fp8 (E4M3) quantisation and GEMM ---- */
+
+size_t tp_fp8_quantize_workspace(int rows, int cols) {
+    (void)rows; (void)cols;
+    return al256(fp8_quantize_ws_bytes());
+}
+
+tp_status tp_fp8_quantize(int rows, int cols, tp_dtype dt, const void* x, int ldx, uint8_t* codes, int ldc,
+                          uint8_t* codes_t, int ldt, float* amax, float* descale, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+    const char* fn = "tp_fp8_quantize";
+    tp_status s;
+    if ((s = check_dt(fn, dt)) != TP_OK) return s;
+    if (rows < 0 || cols < 0) return fail(TP_ERR_SHAPE, "%s: rows=%d cols=%d must be >= 0", fn, rows, cols);
+    if (cols % 8 != 0) return fail(TP_ERR_SHAPE, "%s: cols=%d must be a multiple of 8", fn, cols);
+    if ((long)rows * (cols / 8) >= (1L << 31)) return fail(TP_ERR_SHAPE, "%s: tensor too large", fn);
+    if (ldx < cols || ldx % 8 != 0) return fail(TP_ERR_SHAPE, "%s: ldx=%d must be >= cols and a multiple of 8", fn, ldx);
+    if (!codes && !codes_t) return fail(TP_ERR_ARG, "%s: codes and codes_t are both NULL", fn);
+    NEED(x); OPT(codes); OPT(codes_t);
+    if (codes && (ldc < cols || ldc % 16 != 0))
+        return fail(TP_ERR_SHAPE, "%s: ldc=%d must be >= cols and a multiple of 16", fn, ldc);
+    if (codes_t && (ldt < rows || ldt % 16 != 0))
+        return fail(TP_ERR_SHAPE, "%s: ldt=%d must be >= rows and a multiple of 16", fn, ldt);
+    if (!descale || ((uintptr_t)descale & 3u)) return fail(TP_ERR_ARG, "%s: descale is NULL or misaligned", fn);
+    if (amax && ((uintptr_t)amax & 3u)) return fail(TP_ERR_ARG, "%s: amax is misaligned", fn);
+    size_t need = tp_fp8_quantize_workspace(rows, cols);
+    if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    NEED(ws);
+    HIP_TRY(fp8_quantize(dt == TP_BF16, rows, cols, x, ldx, codes, ldc, codes_t, ldt, amax, descale, (float*)ws,
+                         stream), fn);
+    return ok();
+}
+
+size_t tp_gemm_fp8_workspace(int M, int N, int K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return al256(split_ws_bytes(plan_gemm_fp8(M, N, K, true), M, N));
+}
+
+tp_status tp_gemm_fp8(int M, int N, int K, const uint8_t* A, int lda, const float* a_descale, const uint8_t* B,
+                      int ldb, const float* b_descale, int epi, void* C, void* C2, int ldc, const void* bias,
+                      const void* aux, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "tp_gemm_fp8";
+    if (M < 0 || N < 0 || K < 0) return fail(TP_ERR_SHAPE, "%s: M=%d N=%d K=%d must be >= 0", fn, M, N, K);
+    if (K % 16 != 0) return fail(TP_ERR_SHAPE, "%s: K=%d must be a multiple of 16", fn, K);
+    if (N % 8 != 0) return fail(TP_ERR_SHAPE, "%s: N=%d must be a multiple of 8", fn, N);
+    if (lda < K || lda % 16 != 0 || ldb < K || ldb % 16 != 0)
+        return fail(TP_ERR_SHAPE, "%s: lda=%d, ldb=%d must be >= K and multiples of 16", fn, lda, ldb);
+    if (ldc < N || ldc % 8 != 0) return fail(TP_ERR_SHAPE, "%s: ldc=%d must be >= N and a multiple of 8", fn, ldc);
+    if (epi != TP_EPI_STORE && epi != TP_EPI_BIAS_GELU && epi != TP_EPI_DGELU)
+        return fail(TP_ERR_ARG, "%s: unknown epilogue %d", fn, epi);
+    if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_ARG, "%s: accumulate=%d must be 0 or 1", fn, accumulate);
+    if (accumulate && epi != TP_EPI_STORE) return fail(TP_ERR_ARG, "%s: accumulate needs TP_EPI_STORE", fn);
+    NEED(A); NEED(B); NEED(C); OPT(bias);
+    if (!a_descale || !b_descale || ((uintptr_t)a_descale & 3u) || ((uintptr_t)b_descale & 3u))
+        return fail(TP_ERR_ARG, "%s: a_descale / b_descale NULL or misaligned", fn);
+    if (epi == TP_EPI_BIAS_GELU) NEED(C2);
+    if (epi == TP_EPI_DGELU) {
+        NEED(aux);
+        if (bias) return fail(TP_ERR_ARG, "%s: TP_EPI_DGELU takes no bias", fn);
+    }
+    if ((size_t)M * lda >= 0x7fff0000u || (size_t)N * ldb >= 0x7fff0000u)
+        return fail(TP_ERR_SHAPE, "%s: an operand is 2 GiB or larger", fn);
+    if (M == 0 || N == 0) return ok();
+    const size_t need = tp_gemm_fp8_workspace(M, N, K);
+    const bool split_ok = epi == TP_EPI_STORE && ws && aligned16(ws) && ws_bytes >= need;
+    GemmPlan p = plan_gemm_fp8(M, N, K, split_ok);
+    GemmReq g = req(M, N, K, A, lda, 0, B, ldb, 0, epi, C, ldc);
+    g.out2 = C2; g.bias = bias; g.aux = aux; g.accumulate = accumulate;
+    g.descale_a = a_descale; g.descale_b = b_descale;
+    HIP_TRY(gemm_fp8(g, p, split_ok ? ws : nullptr, stream), fn);
+    return ok();
+}
+
 }  // extern "C"

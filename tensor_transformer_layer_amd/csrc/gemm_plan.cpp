@@ -31,23 +31,24 @@ static const TunedPlan kTuned[] = {
     {3072, 1152, 8192, 1, 2, 3},   // dWqkv
 };
 
-GemmPlan plan_gemm_bf16(int M, int N, int K, bool allow_split) {
-    for (const TunedPlan& t : kTuned)
-        if (t.M == M && t.N == N && t.K == K && (t.splits == 1 || (allow_split && t.split_ok)))
-            return GemmPlan{t.cfg, t.splits, kBM[t.cfg], kBN[t.cfg]};
-    const double cu_flops = 2.5e15 / kCUs * 0.8;   // sustained per-CU rate at full efficiency
+// Time model over the three tile shapes and split counts: rounds of resident tiles x per-tile
+// MFMA time + a fixed per-round cost, plus the split-K reduction's traffic. bk = K tile depth,
+// peak = dense MFMA rate of the element type; cfg_mask = tile shapes allowed (bit c).
+static GemmPlan plan_model(int M, int N, int K, bool allow_split, int bk, double peak, int cfg_mask) {
+    const double cu_flops = peak / kCUs * 0.8;     // sustained per-CU rate at full efficiency
     const double round_overhead = 2.0e-6;          // prologue + epilogue per wave of tiles
-    GemmPlan best{1, 1, 128, 128};
+    GemmPlan best{1, 1, 128, 128};   // cfg 1 is always allowed
     double best_t = 1e30;
     static const int splits_opt[] = {1, 2, 3, 4, 6, 8};
     for (int c = 0; c < kNCfg; ++c) {
+        if (!((cfg_mask >> c) & 1)) continue;
         for (int s : splits_opt) {
             if (s > 1 && (!allow_split || K / s < 512)) continue;
             long tiles = (long)((M + kBM[c] - 1) / kBM[c]) * ((N + kBN[c] - 1) / kBN[c]);
             long units = tiles * s;
             long slots = (long)kCUs * kPerCU[c];
             long rounds = (units + slots - 1) / slots;
-            long kc = ((K + s - 1) / s + 63) / 64 * 64;
+            long kc = ((K + s - 1) / s + bk - 1) / bk * bk;
             double t_tile = 2.0 * kBM[c] * kBN[c] * (double)kc * kPerCU[c] / (cu_flops * kEff[c]);
             double t = rounds * (t_tile + round_overhead);
             if (s > 1) t += (s + 1.0) * 4.0 * (double)M * N / 4.0e12 + 3.0e-6;
@@ -55,6 +56,19 @@ GemmPlan plan_gemm_bf16(int M, int N, int K, bool allow_split) {
         }
     }
     return best;
+}
+
+GemmPlan plan_gemm_bf16(int M, int N, int K, bool allow_split) {
+    for (const TunedPlan& t : kTuned)
+        if (t.M == M && t.N == N && t.K == K && (t.splits == 1 || (allow_split && t.split_ok)))
+            return GemmPlan{t.cfg, t.splits, kBM[t.cfg], kBN[t.cfg]};
+    return plan_model(M, N, K, allow_split, 64, 2.5e15, 7);
+}
+
+// fp8: 256x256 is left out (its fragments and accumulators exceed 256 registers per lane and
+// spill).
+GemmPlan plan_gemm_fp8(int M, int N, int K, bool allow_split) {
+    return plan_model(M, N, K, allow_split, 128, 5.0e15, 6);
 }
 
 size_t split_ws_bytes(const GemmPlan& p, int M, int N) {

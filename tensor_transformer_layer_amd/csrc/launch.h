@@ -29,6 +29,8 @@ struct GemmReq {
     const int32_t* targets; int col0, Vreal, mask;
     // EPI_XENT_GRAD: merged per-token max and sum, upstream gradient; out2 = token-major copy (ld2)
     const float* stat_m; const float* stat_s; const float* dloss; int ld2;
+    // fp8 GEMM: device pointers to the per-tensor descales of A and B
+    const float* descale_a; const float* descale_b;
 };
 
 struct GemmPlan {
@@ -47,6 +49,16 @@ size_t split_ws_bytes(const GemmPlan& p, int M, int N);
 hipError_t gemm_bf16(const GemmReq& r, const GemmPlan& plan, void* ws, hipStream_t st);
 // Launch one fp32 SIMT GEMM.
 hipError_t gemm_f32(const GemmReq& r, hipStream_t st);
+
+// fp8 (E4M3) GEMM, both operands K-contiguous code matrices (lda/ldb in bytes); epilogues
+// EPI_STORE (split-K allowed), EPI_BIAS_GELU, EPI_DGELU with bf16 outputs.
+GemmPlan plan_gemm_fp8(int M, int N, int K, bool allow_split);
+hipError_t gemm_fp8(const GemmReq& r, const GemmPlan& plan, void* ws, hipStream_t st);
+// Per-tensor E4M3 quantisation of x [rows, cols] (dt 0 fp32, 1 bf16): codes [rows, ldc] and/or
+// codes_t [cols, ldt] (transposed), amax (optional) and descale = 2^-e, each one float.
+size_t fp8_quantize_ws_bytes();
+hipError_t fp8_quantize(int dt, int rows, int cols, const void* x, int ldx, uint8_t* codes, int ldc,
+                        uint8_t* codes_t, int ldt, float* amax, float* descale, float* ws, hipStream_t st);
 
 // Per-layout instantiations (separate translation units).
 hipError_t gemm_bf16_nn(const GemmReq& r, const GemmPlan& p, void* ws, hipStream_t st);   // A K-contig, B MN-contig

@@ -143,3 +143,51 @@ def test_vocab_bwd_argument_errors():
     assert call(ptrs=[FAKE] * 5 + [None]) == tp.TP_ERR_ARG
     assert call(dE=None) == tp.TP_ERR_ARG
     assert call(wsb=need - 1) == tp.TP_ERR_WORKSPACE
+
+
+def test_fp8_quantize_argument_errors():
+    f = tp.lib.tp_fp8_quantize
+    nb = tp.lib.tp_fp8_quantize_workspace(64, 128)
+    assert nb >= 512 * 4
+    ok = dict(rows=64, cols=128, dt=tp.TP_BF16, x=FAKE, ldx=128, codes=FAKE, ldc=128, codes_t=FAKE, ldt=64,
+              amax=FAKE, descale=FAKE, ws=FAKE, nb=nb, st=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(*a.values())
+    assert call(cols=124) == tp.TP_ERR_SHAPE                 # cols not a multiple of 8
+    assert call(ldx=120) == tp.TP_ERR_SHAPE                  # ldx < cols
+    assert call(ldc=136) == tp.TP_ERR_SHAPE                  # ldc not a multiple of 16
+    assert call(ldt=48) == tp.TP_ERR_SHAPE                   # ldt < rows
+    assert call(codes=None, codes_t=None) == tp.TP_ERR_ARG   # no output at all
+    assert call(descale=None) == tp.TP_ERR_ARG
+    assert call(descale=FAKE + 2) == tp.TP_ERR_ARG           # misaligned float
+    assert call(nb=nb - 4) == tp.TP_ERR_WORKSPACE
+    assert call(dt=7) == tp.TP_ERR_DTYPE
+    assert call(rows=-1) == tp.TP_ERR_SHAPE
+    assert "tp_fp8_quantize" in tp.tp_last_error()
+
+
+def test_gemm_fp8_argument_errors():
+    f = tp.lib.tp_gemm_fp8
+    ok = dict(M=256, N=128, K=512, A=FAKE, lda=512, sa=FAKE, B=FAKE, ldb=512, sb=FAKE, epi=tp.TP_EPI_STORE,
+              C=FAKE, C2=None, ldc=128, bias=None, aux=None, acc=0, ws=None, nb=0, st=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(*a.values())
+    assert call(K=520, lda=528, ldb=528) == tp.TP_ERR_SHAPE   # K not a multiple of 16
+    assert call(N=132, ldc=136) == tp.TP_ERR_SHAPE             # N not a multiple of 8
+    assert call(lda=504) == tp.TP_ERR_SHAPE                    # lda < K
+    assert call(ldb=520) == tp.TP_ERR_SHAPE                    # ldb not a multiple of 16
+    assert call(ldc=120) == tp.TP_ERR_SHAPE                    # ldc < N
+    assert call(epi=3) == tp.TP_ERR_ARG
+    assert call(acc=2) == tp.TP_ERR_ARG
+    assert call(epi=tp.TP_EPI_BIAS_GELU, acc=1, C2=FAKE) == tp.TP_ERR_ARG   # accumulate only with STORE
+    assert call(epi=tp.TP_EPI_BIAS_GELU) == tp.TP_ERR_ARG      # C2 missing
+    assert call(epi=tp.TP_EPI_DGELU) == tp.TP_ERR_ARG          # aux missing
+    assert call(epi=tp.TP_EPI_DGELU, aux=FAKE, bias=FAKE) == tp.TP_ERR_ARG
+    assert call(sa=None) == tp.TP_ERR_ARG
+    assert call(A=FAKE + 8) == tp.TP_ERR_ARG                   # misaligned operand
+    assert call(M=-1) == tp.TP_ERR_SHAPE
+    assert "tp_gemm_fp8" in tp.tp_last_error()
