@@ -35,28 +35,40 @@ PEAK_HBM = 8.0e12         # bytes/s
 COPY_PROBE_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "vocab_xent_gemm_8p3b.md")
 KERNEL_SOURCES = ["common.h", "gemm.h", "gemm_dispatch.h", "xent.h"]
+FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp8_layer_gemms_8p3b.md")
+FP8_KERNEL_SOURCES = ["common.h", "gemm.h", "gemm_fp8.hip"]
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "tensor_transformer_layer_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the fused vocabulary GEMM, from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources; else None."""
+def measured_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
+    """HBM bytes per launch of the roofline kernel, from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources; else None."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
     except OSError:
         return None
     src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not src or not val or src.group(1) != kernel_source_hash():
+    if not src or not val or src.group(1) != kernel_source_hash(sources):
         return None
     return float(val.group(1))
+
+
+def copy_probe(torch, dev):
+    """One 512 MiB device-to-device copy: the reference reading for the HBM byte counters."""
+    src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def layer_flops(b, s, h, heads, ffn, t):
@@ -151,6 +163,9 @@ def main():
     ap.add_argument("--vocab-bwd", action="store_true",
                     help="time the vocabulary-parallel cross-entropy backward of rank 0 instead (logits gradient "
                          "+ dX_r + dE_r GEMMs: 3 x 322 GFLOP per call) and print its own JSON line")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time rank 0's twelve layer GEMMs (forward, input and weight gradients) in fp8 E4M3 with "
+                         "per-tensor scales, each operand quantised in the step, and print their own JSON line")
     ap.add_argument("--heads", type=int, default=HEADS,
                     help="attention heads of the layer (the pages' 8.3B head-count sweep uses 16, 24, 32; the "
                          "FLOPs and all other shapes are unchanged, heads per rank = heads / 8)")
@@ -164,6 +179,8 @@ def main():
     import tensor_transformer_layer_amd as tp
     from tensor_transformer_layer_amd.layer import LayerShard, rank_params
 
+    if args.fp8:
+        return bench_fp8(args, tp, torch)
     dev = "cuda:0"
     T = B * S
     Vt = VOCAB_PAD // TP
@@ -215,12 +232,7 @@ def main():
         return bench_vocab_bwd(args, tp, torch, T, Vt, Xv, E0, tg, peers, stream)
     xev = []
     if args.copy_probe:
-        src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(torch, dev)
 
     step_ev = []
 
@@ -329,6 +341,144 @@ def bench_vocab_bwd(args, tp, torch, T, Vt, Xv, E0, tg, peers, stream):
         "config": {"workload": "rank 0 vocab shard backward: logits gradient + dX_r + dE_r", "tokens": T,
                    "hidden": H, "vocab_padded": VOCAB_PAD, "tp": TP},
         "pct_bf16_peak": round(100 * value * 1e12 / PEAK_BF16, 2)}), flush=True)
+
+
+# The twelve GEMMs of rank 0's layer step (8192 tokens, h = 3072, h/t = 384, 3h/t = 1152, ffn/t = 1536):
+# (name, M, N, K, A operand, B operand, epilogue). An operand "X" is X's codes in row layout (K
+# along X's rows' length), "X^T" its transposed codes (K along X's rows), as tp_gemm_fp8 takes them.
+FP8_GEMMS = [
+    ("qkv_fwd", 8192, 1152, 3072, "Xn", "Wqkv^T", "bias"),
+    ("proj_fwd", 8192, 3072, 384, "O", "Wo^T", "store"),
+    ("mlp1_fwd", 8192, 1536, 3072, "Y", "A^T", "bias_gelu"),
+    ("mlp2_fwd", 8192, 3072, 1536, "Z", "B^T", "store"),
+    ("dZ_dgelu", 8192, 1536, 3072, "G", "B", "dgelu"),
+    ("dB_wgrad", 1536, 3072, 8192, "Z^T", "G^T", "store"),
+    ("dY_dgrad", 8192, 3072, 1536, "dU", "A", "store"),
+    ("dA_wgrad", 3072, 1536, 8192, "Y^T", "dU^T", "store"),
+    ("dO_dgrad", 8192, 384, 3072, "G2", "Wo", "store"),
+    ("dWo_wgrad", 384, 3072, 8192, "O^T", "G2^T", "store"),
+    ("dXn_dgrad", 8192, 3072, 1152, "dQKV", "Wqkv", "store"),
+    ("dWqkv_wgrad", 3072, 1152, 8192, "Xn^T", "dQKV^T", "store"),
+]
+# bf16 tensors quantised each step: (name, rows, cols, std); weights are stored [in, out] as in the layer
+FP8_TENSORS = [("Xn", 8192, 3072, 1.0), ("O", 8192, 384, 1.0), ("Y", 8192, 3072, 1.0), ("Z", 8192, 1536, 1.0),
+               ("G", 8192, 3072, 1e-3), ("dU", 8192, 1536, 1e-3), ("G2", 8192, 3072, 1e-3),
+               ("dQKV", 8192, 1152, 1e-3), ("Wqkv", 3072, 1152, 0.02), ("Wo", 384, 3072, 0.02),
+               ("A", 3072, 1536, 0.02), ("B", 1536, 3072, 0.02)]
+PEAK_FP8 = 5.0e15   # MI355X dense fp8 MFMA, FLOP/s
+
+
+def bench_fp8(args, tp, torch):
+    """fp8 E4M3 GEMMs of rank 0's layer step, with the per-tensor quantisation of every operand
+    (amax, power-of-two scale, row and transposed codes) inside the step. The weights are
+    quantised in every step too, as they change after every optimizer step."""
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    T = B * S
+    src, codes, codes_t, desc = {}, {}, {}, {}
+    for i, (name, rows, cols, std) in enumerate(FP8_TENSORS):
+        g = np.random.default_rng([9100, i])
+        src[name] = torch.from_numpy((g.standard_normal((rows, cols)) * std).astype(np.float32)).to(
+            torch.bfloat16).to(dev)
+        codes[name] = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        codes_t[name] = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+        desc[name] = torch.empty(4, dtype=torch.float32, device=dev)
+    qws = torch.empty(max(tp.tp_fp8_quantize_workspace(T, H), 256), dtype=torch.uint8, device=dev)
+    bias = {n: torch.full((N,), 0.01, dtype=torch.bfloat16, device=dev) for n, M, N, K, a, b_, e in FP8_GEMMS
+            if e in ("bias", "bias_gelu")}
+    U = torch.randn((T, FFN // TP), device=dev).to(torch.bfloat16)   # saved pre-activation for dGeLU
+    outs = {n: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for n, M, N, K, a, b_, e in FP8_GEMMS}
+    out2 = torch.empty((T, FFN // TP), dtype=torch.bfloat16, device=dev)
+    gws_bytes = max(tp.tp_gemm_fp8_workspace(M, N, K) for n, M, N, K, a, b_, e in FP8_GEMMS)
+    gws = torch.empty(max(gws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def operand(ref):
+        if ref.endswith("^T"):
+            return codes_t[ref[:-2]], desc[ref[:-2]]
+        return codes[ref], desc[ref]
+
+    ev = {}
+
+    def timed(key, record, fn):
+        if record:
+            a = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+        fn()
+        if record:
+            b_ = torch.cuda.Event(enable_timing=True)
+            b_.record(stream)
+            ev.setdefault(key, []).append((a, b_))
+
+    def step(record):
+        for name, rows, cols, std in FP8_TENSORS:
+            timed("quantize", record, lambda: tp.tp_fp8_quantize(
+                rows, cols, tp.TP_BF16, src[name], cols, codes[name], cols, codes_t[name], rows, None, desc[name],
+                qws, qws.numel()))
+        for name, M, N, K, a, b_, e in FP8_GEMMS:
+            (ca, da), (cb, db) = operand(a), operand(b_)
+            epi = {"store": tp.TP_EPI_STORE, "bias": tp.TP_EPI_STORE, "bias_gelu": tp.TP_EPI_BIAS_GELU,
+                   "dgelu": tp.TP_EPI_DGELU}[e]
+            timed(name, record, lambda: tp.tp_gemm_fp8(
+                M, N, K, ca, K, da, cb, K, db, epi, outs[name], out2 if e == "bias_gelu" else None, N,
+                bias.get(name), U if e == "dgelu" else None, 0, gws, gws.numel()))
+
+    if args.copy_probe:
+        copy_probe(torch, dev)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    per = {k: float(np.mean([a.elapsed_time(b_) for a, b_ in v])) * (len(v) / args.steps) for k, v in ev.items()}
+    gemm_fl = {n: 2.0 * M * N * K for n, M, N, K, a, b_, e in FP8_GEMMS}
+    total_fl = sum(gemm_fl.values())
+    value = total_fl / (ms * 1e-3) / 1e12
+    gemm_ms = sum(per[n] for n in gemm_fl)
+    # roofline kernel: the row-parallel second MLP GEMM (8192 x 3072 x 1536, one launch, no K split)
+    dom = "mlp2_fwd"
+    dom_tf = gemm_fl[dom] / (per[dom] * 1e-3) / 1e12
+    # the same twelve products in bf16 through the vendor library (torch.matmul), for context
+    mm = []
+    for n, M, N, K, a, b_, e in FP8_GEMMS:
+        mm.append((torch.randn((M, K), device=dev).to(torch.bfloat16), torch.randn((K, N), device=dev).to(torch.bfloat16)))
+    for _ in range(2):
+        for x_, w_ in mm:
+            torch.matmul(x_, w_)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        for x_, w_ in mm:
+            torch.matmul(x_, w_)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    lib_ms = t0.elapsed_time(t1) / args.steps
+    print(json.dumps({
+        "metric": "layer-shard GEMM TFLOP/s in fp8 E4M3 (fwd + dgrad + wgrad, quantisation included), "
+                  "8.3B shape t=8, 1 GPU",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3", "data": "synthetic (seeded N(0,1) activations, N(0,1e-3^2) gradients, "
+                                     "N(0,0.02^2) weights)",
+        "config": {"workload": "rank 0's 12 layer GEMMs in fp8 with 12 per-tensor quantisations (row + transposed "
+                               "codes) per step", "tokens": T, "hidden": H, "ffn": FFN, "tp": TP},
+        "pct_fp8_peak": round(100 * value * 1e12 / PEAK_FP8, 2),
+        "breakdown": {"gemm_gflop": round(total_fl / 1e9, 2), "gemm_ms": round(gemm_ms, 4),
+                      "quantize_ms": round(per["quantize"], 4),
+                      "gemm_tflops": round(total_fl / (gemm_ms * 1e-3) / 1e12, 2),
+                      "per_gemm_us": {n: round(per[n] * 1e3, 1) for n in gemm_fl},
+                      "bf16_vendor_matmul_ms_same_shapes": round(lib_ms, 4)},
+        "roofline": {"bound": "mfma", "kernel": "gemm_fp8_kernel<256x192, EpiStore> of mlp2_fwd (8192 x 3072 x 1536)",
+                     "achieved": round(dom_tf, 2), "peak": PEAK_FP8 / 1e12, "unit": "TFLOP/s",
+                     "frac": round(dom_tf * 1e12 / PEAK_FP8, 4),
+                     "traffic": measured_traffic(FP8_TRAFFIC_FILE, FP8_KERNEL_SOURCES),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"}}),
+          flush=True)
 
 
 if __name__ == "__main__":

@@ -65,8 +65,9 @@ def check_quant(x, dtype, got):
 def all_bf16_in_range():
     """Every bf16 value with magnitude <= 448, as float64 (31,618 values incl. +-0)."""
     u = np.arange(65536, dtype=np.uint32) << np.uint32(16)
-    v = u.view(np.float32).astype(np.float64)
-    return v[np.isfinite(v) & (np.abs(v) <= 448)]
+    v = u.view(np.float32)
+    v = v[np.isfinite(v)].astype(np.float64)
+    return v[np.abs(v) <= 448]
 
 
 @pytest.mark.parametrize("shift", [0, 5, -7])
