@@ -6,7 +6,8 @@ routes through it, and it shares no code with the GPU library: it imports nothin
 ``tensor_transformer_layer_amd`` and reads no file that the library writes.
 
 Every function is a plain, unfused, float64 definition written from the pages (``fp8`` holds
-the library's own 8-bit scheme, which the pages do not define; its header says so):
+the library's own 8-bit scheme, which the pages do not define, and ``rng`` the counter-based
+generator behind dropout, which they do not name; their headers say so):
 
 * "Megatron-LM: Training Multi-Billion Parameter Language Models Using Model Parallelism"
   (paper digest), §3.4 Detailed, Sentence-Based Technical Breakdown;
@@ -34,7 +35,7 @@ from .layernorm import layernorm_fwd, layernorm_bwd
 from .layer import layer_fwd, layer_bwd, layer_split_fwd, layer_split_bwd
 from .xent import (xent_full, xent_shard_stats, xent_combine, xent_two_round, vocab_shard,
                    pad_vocab, xent_full_grad, xent_shard_grad, xent_merged_stats)
-from . import fp8
+from . import fp8, rng, embedding
 
 __all__ = [
     "gelu", "gelu_grad", "gelu_scalar",
@@ -45,5 +46,5 @@ __all__ = [
     "layernorm_fwd", "layernorm_bwd",
     "layer_fwd", "layer_bwd", "layer_split_fwd", "layer_split_bwd",
     "xent_full", "xent_shard_stats", "xent_combine", "xent_two_round", "vocab_shard", "pad_vocab",
-    "xent_full_grad", "xent_shard_grad", "xent_merged_stats", "fp8",
+    "xent_full_grad", "xent_shard_grad", "xent_merged_stats", "fp8", "rng", "embedding",
 ]

@@ -53,8 +53,11 @@ def wo_shard(Wo, heads, t, r):
     return Wo[lo:hi]
 
 
-def attn_core_fwd(Q, K, V, causal):
-    """One (sequence, head): S = QK^T/sqrt(d), masked, P = softmax(S), O = PV, lse per row."""
+def attn_core_fwd(Q, K, V, causal, keep=None, scale=1.0):
+    """One (sequence, head): S = QK^T/sqrt(d), masked, P = softmax(S), O = PV, lse per row.
+
+    With a dropout keep mask (the paper digest's "dropout within attention", §3.4, applied to the
+    attention weights): O = (P * keep * scale) V; P and lse stay those of the undropped softmax."""
     s, d = Q.shape
     S = (Q @ K.T) / math.sqrt(d)
     if causal:
@@ -63,15 +66,20 @@ def attn_core_fwd(Q, K, V, causal):
     E = np.exp(S - m)
     denom = E.sum(axis=1, keepdims=True)
     P = E / denom
-    return {"O": P @ V, "P": P, "lse": (m + np.log(denom))[:, 0]}
+    Pd = P if keep is None else np.where(keep, P * scale, 0.0)
+    return {"O": Pd @ V, "P": P, "lse": (m + np.log(denom))[:, 0]}
 
 
-def attn_core_bwd(Q, K, V, P, dO):
-    """Textbook backward of one (sequence, head) given the forward's P."""
+def attn_core_bwd(Q, K, V, P, dO, keep=None, scale=1.0):
+    """Textbook backward of one (sequence, head) given the forward's P (and its dropout mask:
+    with Pd = P * keep * scale, dV = Pd^T dO and dP = (dO V^T) * keep * scale)."""
     d = Q.shape[1]
     c = 1.0 / math.sqrt(d)
-    dV = P.T @ dO
+    Pd = P if keep is None else np.where(keep, P * scale, 0.0)
+    dV = Pd.T @ dO
     dP = dO @ V.T
+    if keep is not None:
+        dP = np.where(keep, dP * scale, 0.0)
     dS = P * (dP - (dP * P).sum(axis=1, keepdims=True))
     return {"dQ": c * (dS @ K), "dK": c * (dS.T @ Q), "dV": dV}
 
@@ -81,7 +89,16 @@ def _split_qkv(QKV, nh, d):
     return QKV[:, :w], QKV[:, w:2 * w], QKV[:, 2 * w:3 * w]
 
 
-def _heads_fwd(QKV, b, s, nh, d, causal):
+def _keep_masks(drop, b, s, nh):
+    """Dropout keep masks of a rank's heads: drop = {p, seed, stream, heads (all ranks), head0}."""
+    if drop is None or drop["p"] == 0.0:
+        return None
+    from .rng import attn_keep
+    return {(bi, j): attn_keep(bi, drop["head0"] + j, s, drop["heads"], drop["p"], drop["seed"], drop["stream"])
+            for bi in range(b) for j in range(nh)}
+
+
+def _heads_fwd(QKV, b, s, nh, d, causal, keep=None, scale=1.0):
     Q, K, V = _split_qkv(QKV, nh, d)
     T = b * s
     O = np.zeros((T, nh * d))
@@ -91,14 +108,15 @@ def _heads_fwd(QKV, b, s, nh, d, causal):
         rows = slice(bi * s, (bi + 1) * s)
         for j in range(nh):
             cols = slice(j * d, (j + 1) * d)
-            out = attn_core_fwd(Q[rows, cols], K[rows, cols], V[rows, cols], causal)
+            out = attn_core_fwd(Q[rows, cols], K[rows, cols], V[rows, cols], causal,
+                                None if keep is None else keep[bi, j], scale)
             O[rows, cols] = out["O"]
             lse[bi, j] = out["lse"]
             P[bi, j] = out["P"]
     return O, lse, P
 
 
-def _heads_bwd(QKV, P, dO, b, s, nh, d):
+def _heads_bwd(QKV, P, dO, b, s, nh, d, keep=None, scale=1.0):
     Q, K, V = _split_qkv(QKV, nh, d)
     dQKV = np.zeros_like(QKV)
     w = nh * d
@@ -106,19 +124,26 @@ def _heads_bwd(QKV, P, dO, b, s, nh, d):
         rows = slice(bi * s, (bi + 1) * s)
         for j in range(nh):
             cols = slice(j * d, (j + 1) * d)
-            g = attn_core_bwd(Q[rows, cols], K[rows, cols], V[rows, cols], P[bi, j], dO[rows, cols])
+            g = attn_core_bwd(Q[rows, cols], K[rows, cols], V[rows, cols], P[bi, j], dO[rows, cols],
+                              None if keep is None else keep[bi, j], scale)
             dQKV[rows, j * d:(j + 1) * d] = g["dQ"]
             dQKV[rows, w + j * d:w + (j + 1) * d] = g["dK"]
             dQKV[rows, 2 * w + j * d:2 * w + (j + 1) * d] = g["dV"]
     return dQKV
 
 
-def attn_shard_fwd(Xn, Wqkv_r, bqkv_r, Wo_r, b, s, heads_t, causal=True):
-    """One rank: QKV_r = Xn Wqkv_r + bqkv_r; attention for its heads; Z_r = O_r Wo_r (no bo)."""
+def attn_shard_fwd(Xn, Wqkv_r, bqkv_r, Wo_r, b, s, heads_t, causal=True, drop=None):
+    """One rank: QKV_r = Xn Wqkv_r + bqkv_r; attention for its heads; Z_r = O_r Wo_r (no bo).
+    drop: attention dropout {p, seed, stream, heads, head0} (oracle.rng's mapping), or None."""
     d = Wo_r.shape[0] // heads_t
     QKV = Xn @ Wqkv_r + bqkv_r
-    O, lse, P = _heads_fwd(QKV, b, s, heads_t, d, causal)
-    return {"QKV": QKV, "O": O, "lse": lse, "P": P, "Z": O @ Wo_r}
+    keep = _keep_masks(drop, b, s, heads_t)
+    scale = 1.0
+    if keep is not None:
+        from .rng import drop_scale
+        scale = drop_scale(drop["p"])
+    O, lse, P = _heads_fwd(QKV, b, s, heads_t, d, causal, keep, scale)
+    return {"QKV": QKV, "O": O, "lse": lse, "P": P, "Z": O @ Wo_r, "keep": keep, "scale": scale}
 
 
 def attn_shard_bwd(Xn, Wqkv_r, Wo_r, fwd_r, G, b, s, heads_t):
@@ -126,7 +151,7 @@ def attn_shard_bwd(Xn, Wqkv_r, Wo_r, fwd_r, G, b, s, heads_t):
     the partial dXn_r (f sums the ranks' partials)."""
     d = Wo_r.shape[0] // heads_t
     dO = G @ Wo_r.T
-    dQKV = _heads_bwd(fwd_r["QKV"], fwd_r["P"], dO, b, s, heads_t, d)
+    dQKV = _heads_bwd(fwd_r["QKV"], fwd_r["P"], dO, b, s, heads_t, d, fwd_r.get("keep"), fwd_r.get("scale", 1.0))
     return {
         "dO": dO,
         "dQKV": dQKV,
@@ -161,10 +186,16 @@ def attn_bwd(Xn, Wqkv, Wo, fwd, G, b, s, heads):
     }
 
 
-def attn_split_fwd(Xn, Wqkv, bqkv, Wo, bo, b, s, heads, t, causal=True):
-    """All t ranks, then the g sum: Z = sum_r Z_r + bo."""
+def attn_split_fwd(Xn, Wqkv, bqkv, Wo, bo, b, s, heads, t, causal=True, drop=None):
+    """All t ranks, then the g sum: Z = sum_r Z_r + bo. drop: {p, seed, streams[t]} (rank r's
+    attention dropout uses streams[r]) or None."""
+    def rank_drop(r):
+        if drop is None:
+            return None
+        return {"p": drop["p"], "seed": drop["seed"], "stream": drop["streams"][r], "heads": heads,
+                "head0": r * (heads // t)}
     ranks = [attn_shard_fwd(Xn, qkv_shard(Wqkv, heads, t, r), qkv_shard(bqkv, heads, t, r),
-                            wo_shard(Wo, heads, t, r), b, s, heads // t, causal)
+                            wo_shard(Wo, heads, t, r), b, s, heads // t, causal, rank_drop(r))
              for r in range(t)]
     return {"Z": sum(p["Z"] for p in ranks) + bo, "ranks": ranks}
 

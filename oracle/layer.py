@@ -6,7 +6,16 @@ Passages: "Megatron-LM, annotated", §2.2 (each layer is self-attention then a t
 feed-forward network, each wrapped in a norm and a residual connection; GPT-2 normalises at
 the start of each block) and §3.5 Duplicate the cheap parts; "Megatron-LM: Training ...
 Model Parallelism" (paper digest), §3.4, f and g operators and "Duplicate Computation vs.
-Communication" (norm, dropout and residual are replicated). Dropout probability is 0 here.
+Communication" (norm, dropout and residual are replicated), and "Random Number Generation
+Handling" (residual dropout after g draws one pattern shared by all ranks; attention dropout
+draws a per-rank pattern). The unsplit functions run without dropout; the split ones take an
+optional drop = {p, seed, resid_streams (site 1, site 2), attn_streams[t]} with oracle.rng's
+generator and element mapping:
+
+    x1 = x  + D1(sum_r Attn_r(LN1(x)) + bo)      x2 = x1 + D2(sum_r MLP_r(LN2(x1)) + b2)
+
+and backward dm = D2(G), dx1 = G + LN2^T(sum_r dXn2_r), da = D1(dx1), dx = dx1 + LN1^T(...),
+where D(v) = v * keep * scale with the site's mask.
 
     x1 = x  + Attn(LN1(x))           (g sums the attention partials, then bo, then residual)
     x2 = x1 + MLP(LN2(x1))           (g sums the MLP partials, then b2, then residual)
@@ -38,27 +47,46 @@ def layer_bwd(x, p, fwd, G, b, s, heads):
     dx1 = G + l2["dx"]
     ag = attn_bwd(fwd["ln1"]["y"], p["Wqkv"], p["Wo"], fwd["attn"], dx1, b, s, heads)
     l1 = layernorm_bwd(x, p["ln1_g"], fwd["ln1"]["mean"], fwd["ln1"]["rstd"], ag["dXn"])
-    return {"dx": dx1 + l1["dx"], "dx1": dx1, "mlp": mg, "attn": ag,
+    return {"dx": dx1 + l1["dx"], "dx1": dx1, "dm": dm, "da": da, "mlp": mg, "attn": ag,
             "dln1_g": l1["dgamma"], "dln1_b": l1["dbeta"],
             "dln2_g": l2["dgamma"], "dln2_b": l2["dbeta"]}
 
 
-def layer_split_fwd(x, p, b, s, heads, t, causal=True):
+def _resid(v, keep, pdrop):
+    if keep is None:
+        return v
+    from .rng import dropout_apply
+    return dropout_apply(v, keep, pdrop)
+
+
+def layer_split_fwd(x, p, b, s, heads, t, causal=True, drop=None):
+    k1 = k2 = None
+    pd = 0.0
+    if drop is not None and drop["p"] > 0.0:
+        from .rng import residual_keep
+        pd = drop["p"]
+        k1 = residual_keep(x.shape[0], x.shape[1], pd, drop["seed"], drop["resid_streams"][0])
+        k2 = residual_keep(x.shape[0], x.shape[1], pd, drop["seed"], drop["resid_streams"][1])
     ln1 = layernorm_fwd(x, p["ln1_g"], p["ln1_b"])
-    at = attn_split_fwd(ln1["y"], p["Wqkv"], p["bqkv"], p["Wo"], p["bo"], b, s, heads, t, causal)
-    x1 = x + at["Z"]
+    adrop = None if k1 is None else {"p": pd, "seed": drop["seed"], "streams": drop["attn_streams"]}
+    at = attn_split_fwd(ln1["y"], p["Wqkv"], p["bqkv"], p["Wo"], p["bo"], b, s, heads, t, causal, adrop)
+    x1 = x + _resid(at["Z"], k1, pd)
     ln2 = layernorm_fwd(x1, p["ln2_g"], p["ln2_b"])
     ml = mlp_split_fwd(ln2["y"], p["A"], p["b1"], p["B"], p["b2"], t)
-    return {"ln1": ln1, "attn": at, "x1": x1, "ln2": ln2, "mlp": ml, "x2": x1 + ml["Z"]}
+    return {"ln1": ln1, "attn": at, "x1": x1, "ln2": ln2, "mlp": ml, "x2": x1 + _resid(ml["Z"], k2, pd),
+            "keep1": k1, "keep2": k2, "p_drop": pd}
 
 
 def layer_split_bwd(x, p, fwd, G, b, s, heads, t):
-    mg = mlp_split_bwd(fwd["ln2"]["y"], p["A"], p["B"], fwd["mlp"]["ranks"], G, t)
+    pd = fwd.get("p_drop", 0.0)
+    dm = _resid(G, fwd.get("keep2"), pd)
+    mg = mlp_split_bwd(fwd["ln2"]["y"], p["A"], p["B"], fwd["mlp"]["ranks"], dm, t)
     l2 = layernorm_bwd(fwd["x1"], p["ln2_g"], fwd["ln2"]["mean"], fwd["ln2"]["rstd"], mg["dX"])
     dx1 = G + l2["dx"]
-    ag = attn_split_bwd(fwd["ln1"]["y"], p["Wqkv"], p["Wo"], fwd["attn"]["ranks"], dx1, b, s,
+    da = _resid(dx1, fwd.get("keep1"), pd)
+    ag = attn_split_bwd(fwd["ln1"]["y"], p["Wqkv"], p["Wo"], fwd["attn"]["ranks"], da, b, s,
                         heads, t)
     l1 = layernorm_bwd(x, p["ln1_g"], fwd["ln1"]["mean"], fwd["ln1"]["rstd"], ag["dXn"])
-    return {"dx": dx1 + l1["dx"], "dx1": dx1, "mlp": mg, "attn": ag,
+    return {"dx": dx1 + l1["dx"], "dx1": dx1, "dm": dm, "da": da, "mlp": mg, "attn": ag,
             "dln1_g": l1["dgamma"], "dln1_b": l1["dbeta"],
             "dln2_g": l2["dgamma"], "dln2_b": l2["dbeta"]}
