@@ -47,7 +47,7 @@ def layer_bwd(x, p, fwd, G, b, s, heads):
     dx1 = G + l2["dx"]
     ag = attn_bwd(fwd["ln1"]["y"], p["Wqkv"], p["Wo"], fwd["attn"], dx1, b, s, heads)
     l1 = layernorm_bwd(x, p["ln1_g"], fwd["ln1"]["mean"], fwd["ln1"]["rstd"], ag["dXn"])
-    return {"dx": dx1 + l1["dx"], "dx1": dx1, "dm": dm, "da": da, "mlp": mg, "attn": ag,
+    return {"dx": dx1 + l1["dx"], "dx1": dx1, "mlp": mg, "attn": ag,
             "dln1_g": l1["dgamma"], "dln1_b": l1["dbeta"],
             "dln2_g": l2["dgamma"], "dln2_b": l2["dbeta"]}
 
