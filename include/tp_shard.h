@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 1
+#define TP_ABI_VERSION 2
 
 typedef enum tp_status {
     TP_OK = 0,
@@ -54,6 +54,25 @@ typedef enum tp_status {
 } tp_status;
 
 typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* Dropout of one site. Passage: "Megatron-LM ..." digest §3.4, "Random Number Generation
+ * Handling": residual dropout after g must draw the same pattern on every rank (pass the same seed
+ * and stream on all ranks), attention dropout a different one per rank (pass a per-rank stream).
+ * Generator (the pages name none): Philox4x32-10 (Salmon et al., SC 2011) with key = seed
+ * (low word first) and counter = (call low, call high, 0, stream). One call gives eight 16-bit
+ * uniforms u[j] = 16-bit half j%2 (low first) of word j/2; an element is kept iff u >= thr with
+ * thr = round(p * 65536), and kept values are scaled by 65536 / (65536 - thr).
+ * Residual sites over a [rows, n] tensor: element (row, c) is slot c % 8 of call row * n/8 + c/8.
+ * Attention: element (sequence b, global head hg, query q, key k), with `heads` heads in all and
+ * n32 = ceil(s / 32), is slot ((k % 16) / 8) * 4 + k % 4 of call
+ * ((((b * heads + hg) * s + q) * n32 + k / 32) * 2 + (k % 8) / 4) * 2 + (k % 32) / 16.
+ * A NULL tp_dropout pointer, or p = 0, means no dropout. */
+typedef struct tp_dropout {
+    float p;            /* drop probability, [0, 1) */
+    uint32_t stream;    /* counter word 3 */
+    uint64_t seed;      /* Philox key */
+    uint16_t* mask;     /* attention only: keep bits, written by the forward, read by the backward */
+} tp_dropout;
 
 /* Version of this header's ABI (TP_ABI_VERSION). */
 int tp_abi_version(void);
@@ -191,24 +210,52 @@ tp_status tp_vocab_xent_shard_bwd(int N, int h, int Vpad, int Vreal, int t, int 
  * Computation vs. Communication": norm, dropout and residual are computed by every rank).
  * ------------------------------------------------------------------------------------------- */
 
-/* out = sum_{r=0}^{t-1} parts[r] + bias (broadcast over rows) + residual, summed in fp32 in rank
- * order. parts is a HOST array of t device pointers to [rows, cols] tensors of in_dt; bias
- * [cols] and residual [rows, cols] are in out_dt and may be NULL. Stands in for g (forward) and
- * f (backward) on one device. */
+/* out = residual + D(sum_{r=0}^{t-1} parts[r] + bias (broadcast over rows)), summed in fp32 in
+ * rank order; D is the residual dropout of `drop` (a residual site over [rows, cols]) or the
+ * identity when drop is NULL. parts is a HOST array of t device pointers to [rows, cols] tensors
+ * of in_dt; bias [cols] and residual [rows, cols] are in out_dt and may be NULL. Stands in for g
+ * (forward) and f (backward) on one device. */
 tp_status tp_sum_partials(int rows, int cols, int t, tp_dtype in_dt, const void* const* parts,
                           const void* bias, const void* residual, void* out, tp_dtype out_dt,
-                          hipStream_t stream);
+                          const tp_dropout* drop, hipStream_t stream);
 
 /* Fused consumer of the forward g in a pre-LN block ("Megatron-LM, annotated", §2.2; the layer
- * norm is replicated on every rank): out = sum_{r=0}^{t-1} parts[r] + bias + residual, summed in
- * fp32 in rank order and stored in dt, then y = LayerNorm(out) exactly as tp_layernorm_fwd would
- * compute it from the stored out. parts is a HOST array of t device pointers to [T, h] tensors;
- * every tensor (parts, bias [h], residual [T, h], out, gamma, beta, y) is in dt; bias and residual
- * may be NULL; mean, rstd [T] fp32 may be NULL. h <= 8192. */
+ * norm is replicated on every rank): out = residual + D(sum_{r=0}^{t-1} parts[r] + bias), summed
+ * in fp32 in rank order and stored in dt (D: the residual dropout of `drop`, a residual site over
+ * [T, h], or the identity when drop is NULL), then y = LayerNorm(out) exactly as tp_layernorm_fwd
+ * would compute it from the stored out. parts is a HOST array of t device pointers to [T, h]
+ * tensors; every tensor (parts, bias [h], residual [T, h], out, gamma, beta, y) is in dt; bias and
+ * residual may be NULL; mean, rstd [T] fp32 may be NULL. h <= 8192. */
 tp_status tp_sum_partials_layernorm(int T, int h, int t, tp_dtype dt, const void* const* parts,
                                     const void* bias, const void* residual, void* out, float eps,
                                     const void* gamma, const void* beta, void* y, float* mean,
-                                    float* rstd, hipStream_t stream);
+                                    float* rstd, const tp_dropout* drop, hipStream_t stream);
+
+/* y = D(x) for a residual dropout site over x, y [rows, cols] in dt (in place allowed): the
+ * backward of the forward's dropout is the same mask and scale applied to the gradient.
+ * drop must not be NULL (p = 0 copies). */
+tp_status tp_dropout_apply(int rows, int cols, tp_dtype dt, const void* x, void* y,
+                           const tp_dropout* drop, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Vocabulary-parallel input embedding. Passage: "Megatron-LM ..." digest §3.4, "Input Embedding
+ * Parallelism": the table E [Vpad, h] is split over vocabulary entries; rank r holds
+ * E_r = rows r*Vpad/t .. (r+1)*Vpad/t - 1 and returns, for each token, its row when the id falls
+ * in that range and a zero row otherwise; g sums the ranks' partials into E[ids] on every rank.
+ * ids: int32 [N] (ids outside [0, Vpad) give zero rows on every rank; the host does not read ids).
+ * ------------------------------------------------------------------------------------------- */
+tp_status tp_embedding_shard_fwd(int N, int h, int Vpad, int t, int r, tp_dtype dt,
+                                 const int32_t* ids, const void* E_r, void* out, hipStream_t stream);
+
+/* Backward of the lookup (the derivative of a gather; not on the pages): dE_r[v] (+)= sum of dX[i]
+ * over the tokens i with ids[i] = r*Vpad/t + v, in increasing token order (a stable counting sort
+ * in the workspace, then ordered fp32 sums: deterministic). dX [N, h] is the replicated gradient
+ * of the summed embedding output. accumulate = 0 overwrites dE_r (rows without tokens become 0);
+ * 1 adds into it (e.g. onto the output-embedding gradient of a tied table). */
+size_t tp_embedding_shard_bwd_workspace(int N, int Vpad, int t);
+tp_status tp_embedding_shard_bwd(int N, int h, int Vpad, int t, int r, tp_dtype dt,
+                                 const int32_t* ids, const void* dX, void* dE_r, int accumulate,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* LayerNorm over the last dimension: y = (x - mean) / sqrt(var + eps) * gamma + beta with the
  * biased variance. x, y [T, h] and gamma, beta [h] in dt; mean, rstd [T] fp32 (may be NULL). */

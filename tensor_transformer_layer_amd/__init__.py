@@ -26,6 +26,21 @@ STATUS_NAMES = {0: "TP_OK", 1: "TP_ERR_ARG", 2: "TP_ERR_SHAPE", 3: "TP_ERR_DTYPE
                 5: "TP_ERR_HIP", 6: "TP_ERR_UNSUPPORTED"}
 
 
+class tp_dropout(C.Structure):
+    """struct tp_dropout of the header: p, stream, seed, mask (device pointer or None)."""
+    _fields_ = [("p", C.c_float), ("stream", C.c_uint32), ("seed", C.c_uint64), ("mask", C.c_void_p)]
+
+
+def dropout(p, seed, stream, mask=None):
+    """A tp_dropout for the calls that take one (mask: a device tensor for attention sites)."""
+    return tp_dropout(float(p), int(stream) & 0xFFFFFFFF, int(seed) & 0xFFFFFFFFFFFFFFFF,
+                      None if mask is None else _ptr(mask))
+
+
+def _drop(d):
+    return None if d is None else C.byref(d)
+
+
 class TPError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
@@ -56,8 +71,12 @@ SIGNATURES = {
     "tp_vocab_xent_combine": (_i, [_i, _i, _pp, _pp, _pp, _p, _p, _p, _p, _p]),
     "tp_vocab_xent_shard_bwd_workspace": (_z, [_i, _i, _i, _i, _i]),
     "tp_vocab_xent_shard_bwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
-    "tp_sum_partials": (_i, [_i, _i, _i, _i, _pp, _p, _p, _p, _i, _p]),
-    "tp_sum_partials_layernorm": (_i, [_i, _i, _i, _i, _pp, _p, _p, _p, _f, _p, _p, _p, _p, _p, _p]),
+    "tp_sum_partials": (_i, [_i, _i, _i, _i, _pp, _p, _p, _p, _i, _p, _p]),
+    "tp_sum_partials_layernorm": (_i, [_i, _i, _i, _i, _pp, _p, _p, _p, _f, _p, _p, _p, _p, _p, _p, _p]),
+    "tp_dropout_apply": (_i, [_i, _i, _i, _p, _p, _p, _p]),
+    "tp_embedding_shard_fwd": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p]),
+    "tp_embedding_shard_bwd_workspace": (_z, [_i, _i, _i]),
+    "tp_embedding_shard_bwd": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _z, _p]),
     "tp_layernorm_fwd": (_i, [_i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p]),
     "tp_layernorm_bwd_workspace": (_z, [_i, _i, _i]),
     "tp_layernorm_bwd": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
@@ -188,16 +207,34 @@ def tp_vocab_xent_shard_bwd(N, h, Vpad, Vreal, t, r, dt, mask_padding, X, E_r, t
                                        _ptr(dE_r), accumulate, _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def tp_sum_partials(rows, cols, t, in_dt, parts, bias, residual, out, out_dt, stream=None):
+def tp_sum_partials(rows, cols, t, in_dt, parts, bias, residual, out, out_dt, drop=None, stream=None):
     pp, _keep = _ptr_array(parts)
     _check(lib.tp_sum_partials(rows, cols, t, _dt(in_dt), pp, _ptr(bias), _ptr(residual), _ptr(out), _dt(out_dt),
-                               _stream(stream)))
+                               _drop(drop), _stream(stream)))
 
 
-def tp_sum_partials_layernorm(T, h, t, dt, parts, bias, residual, out, eps, gamma, beta, y, mean, rstd, stream=None):
+def tp_sum_partials_layernorm(T, h, t, dt, parts, bias, residual, out, eps, gamma, beta, y, mean, rstd, drop=None,
+                              stream=None):
     pp, _keep = _ptr_array(parts)
     _check(lib.tp_sum_partials_layernorm(T, h, t, _dt(dt), pp, _ptr(bias), _ptr(residual), _ptr(out), eps, _ptr(gamma),
-                                         _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), _stream(stream)))
+                                         _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), _drop(drop), _stream(stream)))
+
+
+def tp_dropout_apply(rows, cols, dt, x, y, drop, stream=None):
+    _check(lib.tp_dropout_apply(rows, cols, _dt(dt), _ptr(x), _ptr(y), _drop(drop), _stream(stream)))
+
+
+def tp_embedding_shard_fwd(N, h, Vpad, t, r, dt, ids, E_r, out, stream=None):
+    _check(lib.tp_embedding_shard_fwd(N, h, Vpad, t, r, _dt(dt), _ptr(ids), _ptr(E_r), _ptr(out), _stream(stream)))
+
+
+def tp_embedding_shard_bwd_workspace(N, Vpad, t):
+    return lib.tp_embedding_shard_bwd_workspace(N, Vpad, t)
+
+
+def tp_embedding_shard_bwd(N, h, Vpad, t, r, dt, ids, dX, dE_r, accumulate, ws, ws_bytes, stream=None):
+    _check(lib.tp_embedding_shard_bwd(N, h, Vpad, t, r, _dt(dt), _ptr(ids), _ptr(dX), _ptr(dE_r), accumulate, _ptr(ws),
+                                      ws_bytes, _stream(stream)))
 
 
 def tp_layernorm_fwd(T, h, dt, eps, x, gamma, beta, y, mean, rstd, stream=None):

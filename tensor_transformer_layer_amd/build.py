@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "gemm_plan.cpp", "gemm_nn.hip", "gemm_nt.hip", "gemm_tn.hip", "gemm_f32.hip",
-           "gemm_fp8.hip", "fp8.hip", "attention.hip", "xent.hip", "norm.hip"]
+           "gemm_fp8.hip", "fp8.hip", "embedding.hip", "attention.hip", "xent.hip", "norm.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

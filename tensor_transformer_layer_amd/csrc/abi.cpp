@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 
 #include "launch.h"
@@ -70,6 +71,24 @@ tp_status check_mult8(const char* fn, const char* what, long v) {
 }
 
 size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+
+// tp_dropout -> kernel parameters: thr = round(p * 65536), scale = 65536 / (65536 - thr). NULL or
+// p = 0 gives thr = 0 (no dropout).
+tp_status make_drop(const char* fn, const tp_dropout* d, DropParams& out) {
+    memset(&out, 0, sizeof(out));
+    out.scale = 1.0f;
+    if (!d) return TP_OK;
+    if (!(d->p >= 0.0f && d->p < 1.0f)) return fail(TP_ERR_ARG, "%s: dropout p=%g must be in [0, 1)", fn, (double)d->p);
+    const uint32_t thr = (uint32_t)std::floor((double)d->p * 65536.0 + 0.5);
+    if (thr >= 65536u) return fail(TP_ERR_ARG, "%s: dropout p=%g rounds to 1", fn, (double)d->p);
+    out.thr = thr;
+    out.scale = (float)(65536.0 / (65536.0 - thr));
+    out.seed_lo = (uint32_t)d->seed;
+    out.seed_hi = (uint32_t)(d->seed >> 32);
+    out.stream = d->stream;
+    out.mask = d->mask;
+    return TP_OK;
+}
 size_t esize(tp_dtype dt) { return dt == TP_BF16 ? 2 : 4; }
 
 GemmReq req(int M, int N, int K, const void* A, int lda, int a_mn, const void* B, int ldb, int b_mn, int epi,
@@ -417,7 +436,8 @@ tp_status tp_vocab_xent_combine(int N, int t, const float* const* max_r, const f
 
 // ------------------------------------------------------------------------------------------------
 tp_status tp_sum_partials(int rows, int cols, int t, tp_dtype in_dt, const void* const* parts, const void* bias,
-                          const void* residual, void* out, tp_dtype out_dt, hipStream_t stream) {
+                          const void* residual, void* out, tp_dtype out_dt, const tp_dropout* drop,
+                          hipStream_t stream) {
     const char* fn = "tp_sum_partials";
     tp_status s;
     if ((s = check_dt(fn, in_dt)) != TP_OK || (s = check_dt(fn, out_dt)) != TP_OK) return s;
@@ -430,14 +450,17 @@ tp_status tp_sum_partials(int rows, int cols, int t, tp_dtype in_dt, const void*
         if (!aligned16(parts[i])) return fail(TP_ERR_ARG, "%s: parts[%d] is not 16-byte aligned", fn, i);
     }
     NEED(out); OPT(bias); OPT(residual);
-    HIP_TRY(sum_partials(in_dt == TP_BF16, out_dt == TP_BF16, (size_t)rows, cols, t, parts, bias, residual, out, stream),
+    DropParams dp;
+    if ((s = make_drop(fn, drop, dp)) != TP_OK) return s;
+    HIP_TRY(sum_partials(in_dt == TP_BF16, out_dt == TP_BF16, (size_t)rows, cols, t, parts, bias, residual, out, dp,
+                         stream),
             "tp_sum_partials");
     return ok();
 }
 
 tp_status tp_sum_partials_layernorm(int T, int h, int t, tp_dtype dt, const void* const* parts, const void* bias,
                                     const void* residual, void* out, float eps, const void* gamma, const void* beta,
-                                    void* y, float* mean, float* rstd, hipStream_t stream) {
+                                    void* y, float* mean, float* rstd, const tp_dropout* drop, hipStream_t stream) {
     const char* fn = "tp_sum_partials_layernorm";
     tp_status s;
     if ((s = check_dt(fn, dt)) != TP_OK) return s;
@@ -452,8 +475,10 @@ tp_status tp_sum_partials_layernorm(int T, int h, int t, tp_dtype dt, const void
         if (!aligned16(parts[i])) return fail(TP_ERR_ARG, "%s: parts[%d] is not 16-byte aligned", fn, i);
     }
     NEED(out); OPT(bias); OPT(residual); NEED(gamma); NEED(beta); NEED(y); OPT(mean); OPT(rstd);
+    DropParams dp;
+    if ((s = make_drop(fn, drop, dp)) != TP_OK) return s;
     HIP_TRY(sum_partials_layernorm(dt == TP_BF16, T, h, t, parts, bias, residual, out, eps, gamma, beta, y, mean, rstd,
-                                   stream), fn);
+                                   dp, stream), fn);
     return ok();
 }
 
@@ -520,6 +545,69 @@ tp_status tp_colsum(int T, int n, tp_dtype dt, const void* G, void* out, int acc
     if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
     if (need > 0) NEED(ws);
     HIP_TRY(colsum(dt == TP_BF16, T, n, G, out, accumulate, (float*)ws, stream), fn);
+    return ok();
+}
+
+/* ---- dropout and the vocabulary-parallel embedding ---- */
+
+tp_status tp_dropout_apply(int rows, int cols, tp_dtype dt, const void* x, void* y, const tp_dropout* drop,
+                           hipStream_t stream) {
+    const char* fn = "tp_dropout_apply";
+    tp_status s;
+    if ((s = check_dt(fn, dt)) != TP_OK) return s;
+    if (rows < 0) return fail(TP_ERR_SHAPE, "%s: rows=%d is negative", fn, rows);
+    if ((s = check_mult8(fn, "cols", cols)) != TP_OK) return s;
+    if (!drop) return fail(TP_ERR_ARG, "%s: drop is NULL", fn);
+    NEED(x); NEED(y);
+    DropParams dp;
+    if ((s = make_drop(fn, drop, dp)) != TP_OK) return s;
+    const size_t n = (size_t)rows * cols;
+    if (dp.thr == 0) {
+        if (x != y) HIP_TRY(hipMemcpyAsync(y, x, n * esize(dt), hipMemcpyDeviceToDevice, stream), fn);
+        return ok();
+    }
+    HIP_TRY(dropout(dt == TP_BF16, n, x, y, dp, stream), fn);
+    return ok();
+}
+
+tp_status tp_embedding_shard_fwd(int N, int h, int Vpad, int t, int r, tp_dtype dt, const int32_t* ids,
+                                 const void* E_r, void* out, hipStream_t stream) {
+    const char* fn = "tp_embedding_shard_fwd";
+    tp_status s;
+    if ((s = check_dt(fn, dt)) != TP_OK || (s = check_rank(fn, t, r)) != TP_OK) return s;
+    if (N < 0) return fail(TP_ERR_SHAPE, "%s: N=%d is negative", fn, N);
+    if ((s = check_mult8(fn, "h", h)) != TP_OK) return s;
+    if (Vpad <= 0 || Vpad % t != 0) return fail(TP_ERR_SHAPE, "%s: Vpad=%d must be a positive multiple of t", fn, Vpad);
+    if ((long)N * h >= (1L << 31)) return fail(TP_ERR_SHAPE, "%s: N*h too large", fn);
+    if (!ids) return fail(TP_ERR_ARG, "%s: ids is NULL", fn);
+    NEED(E_r); NEED(out);
+    HIP_TRY(embedding_fwd(dt == TP_BF16, N, h, Vpad / t, r, ids, E_r, out, stream), fn);
+    return ok();
+}
+
+size_t tp_embedding_shard_bwd_workspace(int N, int Vpad, int t) {
+    if (N < 0 || t < 1 || Vpad <= 0 || Vpad % t) return 0;
+    return al256(embedding_bwd_ws_bytes(N, Vpad / t));
+}
+
+tp_status tp_embedding_shard_bwd(int N, int h, int Vpad, int t, int r, tp_dtype dt, const int32_t* ids,
+                                 const void* dX, void* dE_r, int accumulate, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+    const char* fn = "tp_embedding_shard_bwd";
+    tp_status s;
+    if ((s = check_dt(fn, dt)) != TP_OK || (s = check_rank(fn, t, r)) != TP_OK) return s;
+    if (N < 0) return fail(TP_ERR_SHAPE, "%s: N=%d is negative", fn, N);
+    if ((s = check_mult8(fn, "h", h)) != TP_OK) return s;
+    if (Vpad <= 0 || Vpad % t != 0) return fail(TP_ERR_SHAPE, "%s: Vpad=%d must be a positive multiple of t", fn, Vpad);
+    if ((long)N * h >= (1L << 31)) return fail(TP_ERR_SHAPE, "%s: N*h too large", fn);
+    if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_ARG, "%s: accumulate=%d must be 0 or 1", fn, accumulate);
+    if (!ids && N > 0) return fail(TP_ERR_ARG, "%s: ids is NULL", fn);
+    if (N > 0) NEED(dX);
+    NEED(dE_r);
+    size_t need = tp_embedding_shard_bwd_workspace(N, Vpad, t);
+    if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    NEED(ws);
+    HIP_TRY(embedding_bwd(dt == TP_BF16, N, h, Vpad / t, r, ids, dX, dE_r, accumulate, ws, stream), fn);
     return ok();
 }
 

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "rng.h"
+
 namespace tp {
 
 enum EpiKind {
@@ -82,10 +84,11 @@ hipError_t xent_combine(int N, int t, const float* const* mx, const float* const
 int ln_bwd_blocks(int rows);
 hipError_t layernorm_fwd(int dt, int rows, int h, float eps, const void* x, const void* g, const void* b, void* y,
                          float* mean, float* rstd, hipStream_t st);
-// out = sum_r parts[r] + bias + residual (all dt), then y = LayerNorm(out as stored)
+// out = residual + D(sum_r parts[r] + bias) (all dt; D = residual dropout, identity when
+// drop.thr = 0), then y = LayerNorm(out as stored)
 hipError_t sum_partials_layernorm(int dt, int rows, int h, int t, const void* const* parts, const void* bias,
                                   const void* residual, void* out, float eps, const void* g, const void* b, void* y,
-                                  float* mean, float* rstd, hipStream_t st);
+                                  float* mean, float* rstd, const DropParams& drop, hipStream_t st);
 // dres_sum / dx_sum: optional column sums of dres and of dx (the bias gradients of the row-parallel
 // layers on either side of the residual branch)
 hipError_t layernorm_bwd(int dt, int rows, int h, const void* x, const void* g, const float* mean,
@@ -94,6 +97,15 @@ hipError_t layernorm_bwd(int dt, int rows, int h, const void* x, const void* g, 
 int colsum_row_blocks(int rows);
 hipError_t colsum(int dt, int rows, int n, const void* G, void* out, int accumulate, float* ws, hipStream_t st);
 hipError_t sum_partials(int in_dt, int out_dt, size_t rows, int cols, int t, const void* const* parts,
-                        const void* bias, const void* residual, void* out, hipStream_t st);
+                        const void* bias, const void* residual, void* out, const DropParams& drop, hipStream_t st);
+// y = D(x) over n contiguous elements of a tensor whose row length is a multiple of 8
+hipError_t dropout(int dt, size_t n, const void* x, void* y, const DropParams& drop, hipStream_t st);
+
+// Vocabulary-parallel embedding (embedding.hip)
+hipError_t embedding_fwd(int dt, int N, int h, int Vt, int r, const int32_t* ids, const void* E_r, void* out,
+                         hipStream_t st);
+size_t embedding_bwd_ws_bytes(int N, int Vt);
+hipError_t embedding_bwd(int dt, int N, int h, int Vt, int r, const int32_t* ids, const void* dX, void* dE_r,
+                         int accumulate, void* ws, hipStream_t st);
 
 }  // namespace tp

@@ -3,6 +3,7 @@
 // fixed order (wave butterflies, then block partials reduced in block order): no atomics.
 #pragma once
 #include "common.h"
+#include "rng.h"
 
 namespace tp {
 
@@ -114,7 +115,8 @@ __global__ __launch_bounds__(256) void add_ln_fwd_kernel(int rows, int h, int t,
                                                          const T* __restrict__ bias, const T* __restrict__ residual,
                                                          T* __restrict__ out, float eps, const T* __restrict__ gamma,
                                                          const T* __restrict__ beta, T* __restrict__ y,
-                                                         float* __restrict__ mean, float* __restrict__ rstd) {
+                                                         float* __restrict__ mean, float* __restrict__ rstd,
+                                                         DropParams drop) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
@@ -139,6 +141,8 @@ __global__ __launch_bounds__(256) void add_ln_fwd_kernel(int rows, int h, int t,
 #pragma unroll
                 for (int e = 0; e < 8; ++e) a[e] += b[e];
             }
+            // residual dropout of the summed branch: element (row, c..c+7) is one call
+            if (drop.thr) apply_keep8(a, keep8((uint64_t)row * (h >> 3) + (c >> 3), drop), drop.scale);
             if (residual) {
                 float b[8];
                 load8(residual + ro + c, b);
@@ -341,7 +345,9 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(int rows, int n, in
 }
 
 // ---------------------------------------------------------------------------------------------
-// out = sum_r parts[r] + bias + residual (fp32 sum in rank order), 8 elements per thread.
+// out = residual + D(sum_r parts[r] + bias) (fp32 sum in rank order; D = residual dropout or the
+// identity), 8 elements per thread. With cols % 8 == 0, flat index i / 8 is the dropout call of
+// the thread's 8 elements.
 // ---------------------------------------------------------------------------------------------
 constexpr int SUM_MAX_T = 64;
 struct PartPtrs { const void* p[SUM_MAX_T]; };
@@ -349,7 +355,8 @@ struct PartPtrs { const void* p[SUM_MAX_T]; };
 template <typename TI, typename TO>
 __global__ __launch_bounds__(256) void sum_partials_kernel(size_t n_elems, int cols, int t, PartPtrs parts,
                                                            const TO* __restrict__ bias,
-                                                           const TO* __restrict__ residual, TO* __restrict__ out) {
+                                                           const TO* __restrict__ residual, TO* __restrict__ out,
+                                                           DropParams drop) {
     size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (i >= n_elems) return;
     float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -365,6 +372,7 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(size_t n_elems, int c
 #pragma unroll
         for (int e = 0; e < 8; ++e) a[e] += b[e];
     }
+    if (drop.thr) apply_keep8(a, keep8(i >> 3, drop), drop.scale);
     if (residual) {
         float rr[8];
         load8(residual + i, rr);
@@ -372,6 +380,18 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(size_t n_elems, int c
         for (int e = 0; e < 8; ++e) a[e] += rr[e];
     }
     store8(out + i, a);
+}
+
+// y = D(x) over a contiguous [rows, cols] tensor (cols % 8 == 0): the residual-site mapping,
+// 8 elements (one call) per thread. In place is allowed.
+template <typename T>
+__global__ __launch_bounds__(256) void dropout_kernel(size_t n_elems, const T* x, T* y, DropParams drop) {
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i >= n_elems) return;
+    float v[8];
+    load8(x + i, v);
+    apply_keep8(v, keep8(i >> 3, drop), drop.scale);
+    store8(y + i, v);
 }
 
 }  // namespace tp

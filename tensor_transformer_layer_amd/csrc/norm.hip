@@ -43,14 +43,14 @@ hipError_t layernorm_fwd(int dt, int rows, int h, float eps, const void* x, cons
 
 hipError_t sum_partials_layernorm(int dt, int rows, int h, int t, const void* const* parts, const void* bias,
                                   const void* residual, void* out, float eps, const void* g, const void* b, void* y,
-                                  float* mean, float* rstd, hipStream_t st) {
+                                  float* mean, float* rstd, const DropParams& drop, hipStream_t st) {
     if (rows == 0) return hipSuccess;
     if (t < 1 || t > ADDLN_MAX_T) return hipErrorInvalidValue;
     AddLnParts pp;
     for (int r = 0; r < t; ++r) pp.p[r] = parts[r];
     dim3 grid((rows + 3) / 4);
 #define ADDLN(TT, C) hipLaunchKernelGGL((add_ln_fwd_kernel<TT, C>), grid, dim3(256), 0, st, rows, h, t, pp, (const TT*)bias, \
-                                        (const TT*)residual, (TT*)out, eps, (const TT*)g, (const TT*)b, (TT*)y, mean, rstd)
+                                        (const TT*)residual, (TT*)out, eps, (const TT*)g, (const TT*)b, (TT*)y, mean, rstd, drop)
 #define ADDLN_T(TT)                        \
     switch (ln_chunks(h)) {                \
         case 1: ADDLN(TT, 1); break;       \
@@ -149,7 +149,7 @@ hipError_t colsum(int dt, int rows, int n, const void* G, void* out, int accumul
 }
 
 hipError_t sum_partials(int in_dt, int out_dt, size_t rows, int cols, int t, const void* const* parts,
-                        const void* bias, const void* residual, void* out, hipStream_t st) {
+                        const void* bias, const void* residual, void* out, const DropParams& drop, hipStream_t st) {
     size_t n = rows * (size_t)cols;
     if (n == 0) return hipSuccess;
     PartPtrs pp;
@@ -157,16 +157,26 @@ hipError_t sum_partials(int in_dt, int out_dt, size_t rows, int cols, int t, con
     dim3 grid((unsigned)((n / 8 + 255) / 256));
     if (in_dt == 1 && out_dt == 1)
         hipLaunchKernelGGL((sum_partials_kernel<bf16, bf16>), grid, dim3(256), 0, st, n, cols, t, pp,
-                           (const bf16*)bias, (const bf16*)residual, (bf16*)out);
+                           (const bf16*)bias, (const bf16*)residual, (bf16*)out, drop);
     else if (in_dt == 1 && out_dt == 0)
         hipLaunchKernelGGL((sum_partials_kernel<bf16, float>), grid, dim3(256), 0, st, n, cols, t, pp,
-                           (const float*)bias, (const float*)residual, (float*)out);
+                           (const float*)bias, (const float*)residual, (float*)out, drop);
     else if (in_dt == 0 && out_dt == 1)
         hipLaunchKernelGGL((sum_partials_kernel<float, bf16>), grid, dim3(256), 0, st, n, cols, t, pp,
-                           (const bf16*)bias, (const bf16*)residual, (bf16*)out);
+                           (const bf16*)bias, (const bf16*)residual, (bf16*)out, drop);
     else
         hipLaunchKernelGGL((sum_partials_kernel<float, float>), grid, dim3(256), 0, st, n, cols, t, pp,
-                           (const float*)bias, (const float*)residual, (float*)out);
+                           (const float*)bias, (const float*)residual, (float*)out, drop);
+    return hipGetLastError();
+}
+
+hipError_t dropout(int dt, size_t n, const void* x, void* y, const DropParams& drop, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    dim3 grid((unsigned)((n / 8 + 255) / 256));
+    if (dt == 1)
+        hipLaunchKernelGGL(dropout_kernel<bf16>, grid, dim3(256), 0, st, n, (const bf16*)x, (bf16*)y, drop);
+    else
+        hipLaunchKernelGGL(dropout_kernel<float>, grid, dim3(256), 0, st, n, (const float*)x, (float*)y, drop);
     return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version_and_error_text():
-    assert tp.tp_abi_version() == 1
+    assert tp.tp_abi_version() == 2
     st = tp.lib.tp_mlp_shard_fwd(8, 64, 256, 0, 0, tp.TP_BF16, *([FAKE] * 7), None)
     assert st == tp.TP_ERR_ARG
     assert "t=0" in tp.tp_last_error()
@@ -88,10 +88,10 @@ def test_vocab_argument_errors():
 
 def test_sum_partials_argument_errors():
     arr, _keep = tp._ptr_array([FAKE, None])
-    assert tp.lib.tp_sum_partials(4, 64, 2, tp.TP_BF16, arr, None, None, FAKE, tp.TP_F32, None) == tp.TP_ERR_ARG
+    assert tp.lib.tp_sum_partials(4, 64, 2, tp.TP_BF16, arr, None, None, FAKE, tp.TP_F32, None, None) == tp.TP_ERR_ARG
     arr, _keep = tp._ptr_array([FAKE])
-    assert tp.lib.tp_sum_partials(4, 60, 1, tp.TP_BF16, arr, None, None, FAKE, tp.TP_F32, None) == tp.TP_ERR_SHAPE
-    assert tp.lib.tp_sum_partials(4, 64, 0, tp.TP_BF16, arr, None, None, FAKE, tp.TP_F32, None) == tp.TP_ERR_ARG
+    assert tp.lib.tp_sum_partials(4, 60, 1, tp.TP_BF16, arr, None, None, FAKE, tp.TP_F32, None, None) == tp.TP_ERR_SHAPE
+    assert tp.lib.tp_sum_partials(4, 64, 0, tp.TP_BF16, arr, None, None, FAKE, tp.TP_F32, None, None) == tp.TP_ERR_ARG
 
 
 def test_layernorm_argument_errors():
@@ -116,7 +116,8 @@ def test_sum_partials_layernorm_argument_errors():
 
     def call(T=4, h=64, t=2, dt=tp.TP_BF16, parts=arr, eps=1e-5, **kw):
         a = {**ok, **kw}
-        return f(T, h, t, dt, parts, None, None, a["out"], eps, a["gamma"], a["beta"], a["y"], None, None, None)
+        return f(T, h, t, dt, parts, None, None, a["out"], eps, a["gamma"], a["beta"], a["y"], None, None,
+                 a.get("drop"), None)
 
     assert call(t=0) == tp.TP_ERR_ARG
     assert call(h=60) == tp.TP_ERR_SHAPE
@@ -125,6 +126,10 @@ def test_sum_partials_layernorm_argument_errors():
     assert call(y=None) == tp.TP_ERR_ARG
     bad, _k2 = tp._ptr_array([FAKE, None])
     assert call(parts=bad) == tp.TP_ERR_ARG
+    d = tp.dropout(1.0, 1, 0)
+    assert call(drop=tp._drop(d)) == tp.TP_ERR_ARG             # p must be < 1
+    d = tp.dropout(0.999995, 1, 0)
+    assert call(drop=tp._drop(d)) == tp.TP_ERR_ARG             # rounds to 1
 
 
 def test_vocab_bwd_argument_errors():
@@ -191,3 +196,22 @@ def test_gemm_fp8_argument_errors():
     assert call(A=FAKE + 8) == tp.TP_ERR_ARG                   # misaligned operand
     assert call(M=-1) == tp.TP_ERR_SHAPE
     assert "tp_gemm_fp8" in tp.tp_last_error()
+
+
+def test_dropout_and_embedding_argument_errors():
+    d = tp.dropout(0.1, 7, 3)
+    f = tp.lib.tp_dropout_apply
+    assert f(4, 60, tp.TP_BF16, FAKE, FAKE, tp._drop(d), None) == tp.TP_ERR_SHAPE
+    assert f(4, 64, tp.TP_BF16, FAKE, FAKE, None, None) == tp.TP_ERR_ARG
+    assert f(4, 64, tp.TP_BF16, FAKE, FAKE, tp._drop(tp.dropout(-0.1, 1, 1)), None) == tp.TP_ERR_ARG
+    g = tp.lib.tp_embedding_shard_fwd
+    assert g(8, 64, 100, 8, 0, tp.TP_BF16, FAKE, FAKE, FAKE, None) == tp.TP_ERR_SHAPE    # Vpad % t
+    assert g(8, 60, 128, 8, 0, tp.TP_BF16, FAKE, FAKE, FAKE, None) == tp.TP_ERR_SHAPE    # h % 8
+    assert g(8, 64, 128, 8, 8, tp.TP_BF16, FAKE, FAKE, FAKE, None) == tp.TP_ERR_ARG      # r >= t
+    assert g(8, 64, 128, 8, 0, tp.TP_BF16, None, FAKE, FAKE, None) == tp.TP_ERR_ARG      # ids NULL
+    b = tp.lib.tp_embedding_shard_bwd
+    nb = tp.lib.tp_embedding_shard_bwd_workspace(1000, 128, 8)
+    assert nb >= (4 * 16 + 2 * 1000 + 17) * 4
+    assert b(1000, 64, 128, 8, 1, tp.TP_BF16, FAKE, FAKE, FAKE, 0, FAKE, nb - 256, None) == tp.TP_ERR_WORKSPACE
+    assert b(1000, 64, 128, 8, 1, tp.TP_BF16, FAKE, FAKE, FAKE, 2, FAKE, nb, None) == tp.TP_ERR_ARG
+    assert "tp_embedding_shard_bwd" in tp.tp_last_error()
