@@ -66,12 +66,15 @@ typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
  * Attention: element (sequence b, global head hg, query q, key k), with `heads` heads in all and
  * n32 = ceil(s / 32), is slot ((k % 16) / 8) * 4 + k % 4 of call
  * ((((b * heads + hg) * s + q) * n32 + k / 32) * 2 + (k % 8) / 4) * 2 + (k % 32) / 16.
- * A NULL tp_dropout pointer, or p = 0, means no dropout. */
+ * A NULL tp_dropout pointer, or p = 0, means no dropout.
+ * Attention sites also need `mask`: device memory of tp_attn_dropout_mask_bytes() bytes, laid out
+ * as [b][heads/t][s][ceil(s/32)] 32-bit words whose bit j keeps key 32*kt + j of word (.., q, kt).
+ * tp_attn_shard_fwd writes it; tp_attn_shard_bwd reads it (same p; seed and stream unused). */
 typedef struct tp_dropout {
     float p;            /* drop probability, [0, 1) */
     uint32_t stream;    /* counter word 3 */
     uint64_t seed;      /* Philox key */
-    uint16_t* mask;     /* attention only: keep bits, written by the forward, read by the backward */
+    uint32_t* mask;     /* attention only: keep bits, written by the forward, read by the backward */
 } tp_dropout;
 
 /* Version of this header's ABI (TP_ABI_VERSION). */
@@ -135,19 +138,27 @@ tp_status tp_mlp_shard_bwd(int T, int h, int ffn, int t, int r, tp_dtype dt,
  * causal = 1: query i sees keys j <= i of its own sequence; 0: all keys of the sequence. */
 tp_status tp_attn_shard_fwd(int b, int s, int h, int heads, int t, int r, tp_dtype dt, int causal,
                             const void* Xn, const void* Wqkv_r, const void* bqkv_r, const void* Wo_r,
-                            void* QKV_r, void* O_r, float* lse_r, void* Z_r, hipStream_t stream);
+                            void* QKV_r, void* O_r, float* lse_r, void* Z_r, const tp_dropout* drop,
+                            hipStream_t stream);
+
+/* Bytes of the keep-bit mask of one attention dropout site (tp_dropout.mask), for rank shapes
+ * b, s and heads/t heads. */
+size_t tp_attn_dropout_mask_bytes(int b, int s, int heads, int t);
 
 /* Backward of the attention shard for G [b*s, h] = dL/dZ (replicated). The attention chain is the
  * textbook one (not on the pages): dO = G Wo_r^T; D = rowsum(dO * O); P recomputed from lse;
  * dV = P^T dO; dS = P * (dO V^T - D); dQ = dS K / sqrt(d); dK = dS^T Q / sqrt(d).
  * Outputs: dXn_r [b*s, h] partial (f sums them); dWqkv_r [h, 3h_t]; dbqkv_r [3h_t] (may be NULL);
- * dWo_r [h_t, h]. accumulate as in tp_mlp_shard_bwd (dXn_r always overwritten). */
+ * dWo_r [h_t, h]. accumulate as in tp_mlp_shard_bwd (dXn_r always overwritten).
+ * With the forward's attention dropout (drop with the same p and the mask it wrote): dV = P~^T dO
+ * and dS = P * ((dO V^T) * keep * scale - D), P~ = P * keep * scale; D = rowsum(dO * O) holds as
+ * is because O = P~ V. */
 size_t tp_attn_shard_bwd_workspace(int b, int s, int h, int heads, int t, tp_dtype dt);
 tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dtype dt, int causal,
                             const void* Xn, const void* Wqkv_r, const void* Wo_r, const void* QKV_r,
                             const void* O_r, const float* lse_r, const void* G, void* dXn_r,
                             void* dWqkv_r, void* dbqkv_r, void* dWo_r, int accumulate,
-                            void* ws, size_t ws_bytes, hipStream_t stream);
+                            const tp_dropout* drop, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Vocabulary-parallel fused logits GEMM + cross-entropy statistics. Passage: "Megatron-LM ..."

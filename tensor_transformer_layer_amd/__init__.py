@@ -61,9 +61,10 @@ SIGNATURES = {
     "tp_mlp_shard_fwd": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
     "tp_mlp_shard_bwd_workspace": (_z, [_i, _i, _i, _i, _i]),
     "tp_mlp_shard_bwd": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
-    "tp_attn_shard_fwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "tp_attn_shard_fwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "tp_attn_dropout_mask_bytes": (_z, [_i, _i, _i, _i]),
     "tp_attn_shard_bwd_workspace": (_z, [_i, _i, _i, _i, _i, _i]),
-    "tp_attn_shard_bwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i,
+    "tp_attn_shard_bwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p,
                                _p, _z, _p]),
     "tp_vocab_xent_shard_fwd_workspace": (_z, [_i, _i, _i, _i, _i]),
     "tp_vocab_xent_shard_fwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _z, _p]),
@@ -156,9 +157,14 @@ def tp_mlp_shard_bwd(T, h, ffn, t, r, dt, X, A_r, B_r, U_r, Y_r, G, dX_r, dA_r, 
 
 
 def tp_attn_shard_fwd(b, s, h, heads, t, r, dt, causal, Xn, Wqkv_r, bqkv_r, Wo_r, QKV_r, O_r, lse_r, Z_r,
-                      stream=None):
+                      drop=None, stream=None):
     _check(lib.tp_attn_shard_fwd(b, s, h, heads, t, r, _dt(dt), causal, _ptr(Xn), _ptr(Wqkv_r), _ptr(bqkv_r),
-                                 _ptr(Wo_r), _ptr(QKV_r), _ptr(O_r), _ptr(lse_r), _ptr(Z_r), _stream(stream)))
+                                 _ptr(Wo_r), _ptr(QKV_r), _ptr(O_r), _ptr(lse_r), _ptr(Z_r), _drop(drop),
+                                 _stream(stream)))
+
+
+def tp_attn_dropout_mask_bytes(b, s, heads, t):
+    return lib.tp_attn_dropout_mask_bytes(b, s, heads, t)
 
 
 def tp_attn_shard_bwd_workspace(b, s, h, heads, t, dt):
@@ -166,10 +172,11 @@ def tp_attn_shard_bwd_workspace(b, s, h, heads, t, dt):
 
 
 def tp_attn_shard_bwd(b, s, h, heads, t, r, dt, causal, Xn, Wqkv_r, Wo_r, QKV_r, O_r, lse_r, G, dXn_r, dWqkv_r,
-                      dbqkv_r, dWo_r, accumulate, ws, ws_bytes, stream=None):
+                      dbqkv_r, dWo_r, accumulate, ws, ws_bytes, drop=None, stream=None):
     _check(lib.tp_attn_shard_bwd(b, s, h, heads, t, r, _dt(dt), causal, _ptr(Xn), _ptr(Wqkv_r), _ptr(Wo_r),
                                  _ptr(QKV_r), _ptr(O_r), _ptr(lse_r), _ptr(G), _ptr(dXn_r), _ptr(dWqkv_r),
-                                 _ptr(dbqkv_r), _ptr(dWo_r), accumulate, _ptr(ws), ws_bytes, _stream(stream)))
+                                 _ptr(dbqkv_r), _ptr(dWo_r), accumulate, _drop(drop), _ptr(ws), ws_bytes,
+                                 _stream(stream)))
 
 
 def tp_vocab_xent_shard_fwd_workspace(N, h, Vpad, t, dt):

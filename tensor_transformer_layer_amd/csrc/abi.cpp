@@ -89,6 +89,17 @@ tp_status make_drop(const char* fn, const tp_dropout* d, DropParams& out) {
     out.mask = d->mask;
     return TP_OK;
 }
+
+// attention site: also the rank's head offset and the mask buffer
+tp_status attn_drop(const char* fn, const tp_dropout* d, int heads, int heads_t, int r, DropParams& out) {
+    tp_status s = make_drop(fn, d, out);
+    if (s != TP_OK) return s;
+    out.head0 = r * heads_t;
+    out.heads = heads;
+    if (out.thr && (!out.mask || ((uintptr_t)out.mask & 3u)))
+        return fail(TP_ERR_ARG, "%s: attention dropout needs a 4-byte aligned mask buffer", fn);
+    return TP_OK;
+}
 size_t esize(tp_dtype dt) { return dt == TP_BF16 ? 2 : 4; }
 
 GemmReq req(int M, int N, int K, const void* A, int lda, int a_mn, const void* B, int ldb, int b_mn, int epi,
@@ -255,21 +266,28 @@ tp_status tp_mlp_shard_bwd(int T, int h, int ffn, int t, int r, tp_dtype dt, con
 // ------------------------------------------------------------------------------------------------
 tp_status tp_attn_shard_fwd(int b, int s, int h, int heads, int t, int r, tp_dtype dt, int causal, const void* Xn,
                             const void* Wqkv_r, const void* bqkv_r, const void* Wo_r, void* QKV_r, void* O_r,
-                            float* lse_r, void* Z_r, hipStream_t stream) {
+                            float* lse_r, void* Z_r, const tp_dropout* drop, hipStream_t stream) {
     const char* fn = "tp_attn_shard_fwd";
     tp_status st = check_attn(fn, b, s, h, heads, t, r, dt, causal);
     if (st != TP_OK) return st;
     NEED(Xn); NEED(Wqkv_r); NEED(Wo_r); NEED(QKV_r); NEED(O_r); NEED(lse_r); NEED(Z_r); OPT(bqkv_r);
+    const int heads_t = heads / t, d = h / heads, h_t = heads_t * d;
+    DropParams dp;
+    if ((st = attn_drop(fn, drop, heads, heads_t, r, dp)) != TP_OK) return st;
     const int T = b * s;
     if (T == 0) return ok();
-    const int heads_t = heads / t, d = h / heads, h_t = heads_t * d;
     GemmReq g = req(T, 3 * h_t, h, Xn, h, 0, Wqkv_r, 3 * h_t, 1, EPI_STORE, QKV_r, 3 * h_t);
     g.bias = bqkv_r;
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_fwd: QKV GEMM");
-    HIP_TRY(attn_fwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, stream), "tp_attn_shard_fwd: attention");
+    HIP_TRY(attn_fwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, dp, stream), "tp_attn_shard_fwd: attention");
     g = req(T, h, h_t, O_r, h_t, 0, Wo_r, h, 1, EPI_STORE, Z_r, h);
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_fwd: output projection");
     return ok();
+}
+
+size_t tp_attn_dropout_mask_bytes(int b, int s, int heads, int t) {
+    if (b < 0 || s < 0 || heads <= 0 || t < 1 || heads % t) return 0;
+    return (size_t)b * (heads / t) * s * ((s + 31) / 32) * sizeof(uint32_t);
 }
 
 size_t tp_attn_shard_bwd_workspace(int b, int s, int h, int heads, int t, tp_dtype dt) {
@@ -282,7 +300,8 @@ size_t tp_attn_shard_bwd_workspace(int b, int s, int h, int heads, int t, tp_dty
 tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dtype dt, int causal, const void* Xn,
                             const void* Wqkv_r, const void* Wo_r, const void* QKV_r, const void* O_r,
                             const float* lse_r, const void* G, void* dXn_r, void* dWqkv_r, void* dbqkv_r,
-                            void* dWo_r, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
+                            void* dWo_r, int accumulate, const tp_dropout* drop, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
     const char* fn = "tp_attn_shard_bwd";
     tp_status st = check_attn(fn, b, s, h, heads, t, r, dt, causal);
     if (st != TP_OK) return st;
@@ -291,6 +310,8 @@ tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dty
     NEED(dWo_r); OPT(dbqkv_r);
     const int T = b * s;
     const int heads_t = heads / t, d = h / heads, h_t = heads_t * d;
+    DropParams dp;
+    if ((st = attn_drop(fn, drop, heads, heads_t, r, dp)) != TP_OK) return st;
     AttnWs w = attn_ws(b, s, h, heads_t, h_t);
     if (ws_bytes < w.total) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, w.total);
     if (w.total > 0) NEED(ws);
@@ -307,7 +328,7 @@ tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dty
     g.accumulate = accumulate;
     HIP_TRY(run_gemm(dt, g, true, scratch, stream), "tp_attn_shard_bwd: dWo GEMM");
     if (T > 0)
-        HIP_TRY(attn_bwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, dO, Dv, dQKV, stream),
+        HIP_TRY(attn_bwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, dO, Dv, dQKV, dp, stream),
                 "tp_attn_shard_bwd: attention backward");
     // dWqkv_r = Xn^T dQKV
     g = req(h, 3 * h_t, T, Xn, h, 1, dQKV, 3 * h_t, 1, EPI_STORE, dWqkv_r, 3 * h_t);

@@ -27,8 +27,18 @@
 // Backward: D = rowsum(dO * O); the dK/dV kernel owns 64 keys per block and loops over query
 // tiles; the dQ kernel owns 64 queries per block and loops over key tiles. Both recompute P from
 // lse. No atomics: every output element is written by exactly one lane.
+//
+// Dropout on the attention weights (DROP = true; "Megatron-LM ..." paper digest, §3.4: drawn per
+// rank): the forward draws each lane's keep bits with Philox (rng.h; the element mapping puts a
+// lane's 16 keys of a 32-key tile in two calls), applies P~ = P * keep * scale before P V while
+// the row sums l use the undropped P, and stores the bits as a query-major bitmap, one 32-bit word
+// per (query, 32-key tile). The backward reads the bits instead of drawing again: dV = P~^T dO,
+// dP = (dO V^T) * keep * scale, dS = P (dP - D) with D = rowsum(dO * O) unchanged. The dQ kernel
+// has the forward's lane layout and reads one word per tile; the dK/dV kernel (one key and 16
+// queries per lane) stages the query tile's words in LDS with lse and D.
 #pragma once
 #include "common.h"
+#include "rng.h"
 
 namespace tp {
 
@@ -151,10 +161,10 @@ __device__ __forceinline__ float xch_get(const float* xch, int group, int j, int
 // Forward. grid = (b * heads_t, query tiles), query tile qt = last - blockIdx.y (heavy first).
 // Wave w: row group g = w & 1 (queries qt*64 + 32g ..), key-tile parity kp = w >> 1.
 // ---------------------------------------------------------------------------------------------
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(D <= 96 ? 2 : 1)))
 void attn_fwd_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int heads_t, float scale_log2,
-                     int causal, bf16* __restrict__ O, int ldo, float* __restrict__ lse) {
+                     int causal, bf16* __restrict__ O, int ldo, float* __restrict__ lse, DropParams dp) {
     __shared__ __attribute__((aligned(16))) bf16 smem[4 * ATT_B * D];   // K tiles [2] | V tiles [2]
     __shared__ __attribute__((aligned(16))) bf16 Qs[ATT_B * D];          // the block's queries
     bf16* Kb = smem;
@@ -238,6 +248,25 @@ void attn_fwd_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int h
             rs += __shfl_xor(rs, 32);
             l_i = l_i * alpha + rs;
             m_i = m_new;
+            if constexpr (DROP) {
+                const int n32 = (s + 31) >> 5;
+                const uint64_t row = ((uint64_t)bi * dp.heads + dp.head0 + head) * s + myq;
+#pragma unroll
+                for (int sub = 0; sub < 2; ++sub) {
+                    const int kt32 = (k0 >> 5) + sub;
+                    const uint64_t call = ((row * n32 + kt32) * 2 + h) * 2;
+                    const uint32_t bits = keep8(call, dp) | (keep8(call + 1, dp) << 8);
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const uint32_t kb = (bits >> v) & 1u;
+                        st[sub][v] = kb ? st[sub][v] * dp.scale : 0.0f;
+                        w |= kb << (8 * (v >> 2) + 4 * h + (v & 3));
+                    }
+                    w |= __shfl_xor(w, 32);
+                    if (h == 0 && myq < s && kt32 < n32) dp.mask[((size_t)(bi * heads_t + head) * s + myq) * n32 + kt32] = w;
+                }
+            }
             // rescale only when some lane's running max moved (alpha == 1 leaves o unchanged)
             if (__builtin_amdgcn_read_exec() && __any(alpha != 1.0f)) {
 #pragma unroll
@@ -329,14 +358,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(const bf16* __restric
 //   S = Q K^T, P = exp2(S*c - lse2), dP = dO V^T, dS = P (dP - D)      (query rows x own keys)
 //   dV^T += dO^T P,  dK^T += Q^T dS                                     (transposing reads)
 // ---------------------------------------------------------------------------------------------
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(D <= 96 ? 2 : 1)))
 void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int heads_t,
                           const bf16* __restrict__ dO, int ld_do, const float* __restrict__ lse,
                           const float* __restrict__ Dv, float scale_log2, float scale, int causal,
-                          bf16* __restrict__ dQKV, int ld_dq) {
+                          bf16* __restrict__ dQKV, int ld_dq, DropParams dp) {
     __shared__ __attribute__((aligned(16))) bf16 smem[4 * ATT_B * D];   // Q tile | dO tile | K | V
     __shared__ float lse_s[ATT_B], D_s[ATT_B];
+    __shared__ uint32_t mk_s[ATT_B][2];   // dropout keep words of the query tile x the block's two key groups
     bf16* Qb = smem;
     bf16* Gb = smem + ATT_B * D;
     bf16* KVs = smem + 2 * ATT_B * D;
@@ -366,6 +396,8 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
     AttTileRegs<D, ATT_B> qr, gr;
     const auto qrs = att_rsrc<D>(Qp, ld, s), grs = att_rsrc<D>(dOp, ld_do, s);
     float lse_r = INFINITY, d_r = 0.f;
+    uint32_t mk_r = 0;
+    const int n32 = (s + 31) >> 5;
     auto fetch = [&](int q0) {
         qr.load(qrs, ld, q0, s, tid);
         gr.load(grs, ld_do, q0, s, tid);
@@ -374,11 +406,20 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
             lse_r = (q < s) ? lsep[q] * kLog2e : INFINITY;
             d_r = (q < s) ? Dp[q] : 0.f;
         }
+        if constexpr (DROP) {
+            if (tid < 2 * ATT_B) {
+                const int q = q0 + (tid >> 1), kt32 = 2 * kt + (tid & 1);
+                mk_r = (q < s && kt32 < n32) ? dp.mask[((size_t)(bi * heads_t + head) * s + q) * n32 + kt32] : 0u;
+            }
+        }
     };
     auto stash = [&]() {
         qr.store(Qb, tid);
         gr.store(Gb, tid);
         if (tid < ATT_B) { lse_s[tid] = lse_r; D_s[tid] = d_r; }
+        if constexpr (DROP) {
+            if (tid < 2 * ATT_B) mk_s[tid >> 1][tid & 1] = mk_r;
+        }
     };
     if (qt0 < nqt) { fetch(qt0 * ATT_B); stash(); }
     __syncthreads();
@@ -405,8 +446,14 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
                     int q = q0 + qi;
                     if ((causal && mykey > q) || mykey >= s) pv = 0.f;
                 }
-                sacc[v] = pv;
-                dpacc[v] = pv * (dpacc[v] - D_s[qi]);
+                if constexpr (DROP) {
+                    const bool kb = (mk_s[qi][grp] >> l32) & 1u;
+                    sacc[v] = kb ? pv * dp.scale : 0.0f;
+                    dpacc[v] = pv * ((kb ? dpacc[v] * dp.scale : 0.0f) - D_s[qi]);
+                } else {
+                    sacc[v] = pv;
+                    dpacc[v] = pv * (dpacc[v] - D_s[qi]);
+                }
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -503,12 +550,12 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
 // g = w & 1 (32 queries), key-tile parity kp = w >> 1; K and V tiles two per step.
 //   S^T = K Q^T, P^T = exp2(S^T*c - lse2), dP^T = V dO^T, dS^T = P^T (dP^T - D); dQ^T += K^T dS^T
 // ---------------------------------------------------------------------------------------------
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(D <= 96 ? 2 : 1)))
 void attn_bwd_dq_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int heads_t,
                         const bf16* __restrict__ dO, int ld_do, const float* __restrict__ lse,
                         const float* __restrict__ Dv, float scale_log2, float scale, int causal,
-                        bf16* __restrict__ dQKV, int ld_dq) {
+                        bf16* __restrict__ dQKV, int ld_dq, DropParams dp) {
     __shared__ __attribute__((aligned(16))) bf16 smem[4 * ATT_B * D];   // K tiles [2] | V tiles [2]
     __shared__ __attribute__((aligned(16))) bf16 QGs[2 * ATT_B * D];    // the block's queries | their dO
     bf16* Kb = smem;
@@ -561,6 +608,11 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, in
                 const int ks0 = k0 + sub * 32;
                 if (causal && ks0 > q0w + 31) continue;
                 const bool need_mask = (causal && ks0 + 31 > q0w) || (ks0 + 32 > s);
+                uint32_t keepw = 0;
+                if constexpr (DROP) {
+                    const int n32 = (s + 31) >> 5, kt32 = ks0 >> 5;
+                    if (myq < s && kt32 < n32) keepw = dp.mask[((size_t)(bi * heads_t + head) * s + myq) * n32 + kt32];
+                }
                 f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ++ks) {
@@ -576,7 +628,12 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, in
                         int key = ks0 + 8 * (v >> 2) + 4 * h + (v & 3);
                         if ((causal && key > myq) || key >= s) pv = 0.f;
                     }
-                    dpacc[v] = pv * (dpacc[v] - Dq);
+                    if constexpr (DROP) {
+                        const bool kb = (keepw >> (8 * (v >> 2) + 4 * h + (v & 3))) & 1u;
+                        dpacc[v] = pv * ((kb ? dpacc[v] * dp.scale : 0.0f) - Dq);
+                    } else {
+                        dpacc[v] = pv * (dpacc[v] - Dq);
+                    }
                 }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {

@@ -7,17 +7,22 @@ namespace tp {
 
 template <int D>
 static hipError_t fwd_d(int b, int s, int h_t, int heads_t, int causal, const void* QKV, void* O, float* lse,
-                        hipStream_t st) {
+                        const DropParams& dp, hipStream_t st) {
     dim3 grid(b * heads_t, (s + ATT_B - 1) / ATT_B);
     float scale_log2 = kLog2e / sqrtf((float)D);
-    hipLaunchKernelGGL((attn_fwd_kernel<D>), grid, dim3(ATT_NT), 0, st, (const bf16*)QKV, 3 * h_t, h_t, s, heads_t,
-                       scale_log2, causal, (bf16*)O, h_t, lse);
+    if (dp.thr)
+        hipLaunchKernelGGL((attn_fwd_kernel<D, true>), grid, dim3(ATT_NT), 0, st, (const bf16*)QKV, 3 * h_t, h_t, s,
+                           heads_t, scale_log2, causal, (bf16*)O, h_t, lse, dp);
+    else
+        hipLaunchKernelGGL((attn_fwd_kernel<D, false>), grid, dim3(ATT_NT), 0, st, (const bf16*)QKV, 3 * h_t, h_t, s,
+                           heads_t, scale_log2, causal, (bf16*)O, h_t, lse, dp);
     return hipGetLastError();
 }
 
 template <int D>
 static hipError_t bwd_d(int b, int s, int h_t, int heads_t, int causal, const void* QKV, const void* O,
-                        const float* lse, const void* dO, float* Dws, void* dQKV, hipStream_t st) {
+                        const float* lse, const void* dO, float* Dws, void* dQKV, const DropParams& dp,
+                        hipStream_t st) {
     size_t rows = (size_t)b * s * heads_t;
     hipLaunchKernelGGL((attn_bwd_dot_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
                        (const bf16*)dO, (const bf16*)O, h_t, b, s, heads_t, Dws);
@@ -26,35 +31,38 @@ static hipError_t bwd_d(int b, int s, int h_t, int heads_t, int causal, const vo
     dim3 grid(b * heads_t, (s + ATT_B - 1) / ATT_B);
     float scale = 1.0f / sqrtf((float)D);
     float scale_log2 = kLog2e * scale;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), grid, dim3(ATT_NT), 0, st, (const bf16*)QKV, 3 * h_t, h_t, s,
-                       heads_t, (const bf16*)dO, h_t, lse, (const float*)Dws, scale_log2, scale, causal,
-                       (bf16*)dQKV, 3 * h_t);
+#define TP_ATT_BWD(K, DR)                                                                                     \
+    hipLaunchKernelGGL((K<D, DR>), grid, dim3(ATT_NT), 0, st, (const bf16*)QKV, 3 * h_t, h_t, s, heads_t,      \
+                       (const bf16*)dO, h_t, lse, (const float*)Dws, scale_log2, scale, causal, (bf16*)dQKV,  \
+                       3 * h_t, dp)
+    if (dp.thr) TP_ATT_BWD(attn_bwd_dkdv_kernel, true);
+    else TP_ATT_BWD(attn_bwd_dkdv_kernel, false);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), grid, dim3(ATT_NT), 0, st, (const bf16*)QKV, 3 * h_t, h_t, s,
-                       heads_t, (const bf16*)dO, h_t, lse, (const float*)Dws, scale_log2, scale, causal,
-                       (bf16*)dQKV, 3 * h_t);
+    if (dp.thr) TP_ATT_BWD(attn_bwd_dq_kernel, true);
+    else TP_ATT_BWD(attn_bwd_dq_kernel, false);
+#undef TP_ATT_BWD
     return hipGetLastError();
 }
 
 hipError_t attn_fwd(int b, int s, int h_t, int heads_t, int d, int causal, const void* QKV, void* O, float* lse,
-                    hipStream_t st) {
+                    const DropParams& dp, hipStream_t st) {
     switch (d) {
-        case 64: return fwd_d<64>(b, s, h_t, heads_t, causal, QKV, O, lse, st);
-        case 96: return fwd_d<96>(b, s, h_t, heads_t, causal, QKV, O, lse, st);
-        case 128: return fwd_d<128>(b, s, h_t, heads_t, causal, QKV, O, lse, st);
-        case 192: return fwd_d<192>(b, s, h_t, heads_t, causal, QKV, O, lse, st);
+        case 64: return fwd_d<64>(b, s, h_t, heads_t, causal, QKV, O, lse, dp, st);
+        case 96: return fwd_d<96>(b, s, h_t, heads_t, causal, QKV, O, lse, dp, st);
+        case 128: return fwd_d<128>(b, s, h_t, heads_t, causal, QKV, O, lse, dp, st);
+        case 192: return fwd_d<192>(b, s, h_t, heads_t, causal, QKV, O, lse, dp, st);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t attn_bwd(int b, int s, int h_t, int heads_t, int d, int causal, const void* QKV, const void* O,
-                    const float* lse, const void* dO, float* Dws, void* dQKV, hipStream_t st) {
+                    const float* lse, const void* dO, float* Dws, void* dQKV, const DropParams& dp, hipStream_t st) {
     switch (d) {
-        case 64: return bwd_d<64>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dQKV, st);
-        case 96: return bwd_d<96>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dQKV, st);
-        case 128: return bwd_d<128>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dQKV, st);
-        case 192: return bwd_d<192>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dQKV, st);
+        case 64: return bwd_d<64>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dQKV, dp, st);
+        case 96: return bwd_d<96>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dQKV, dp, st);
+        case 128: return bwd_d<128>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dQKV, dp, st);
+        case 192: return bwd_d<192>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dQKV, dp, st);
     }
     return hipErrorInvalidValue;
 }

@@ -68,10 +68,11 @@ hipError_t gemm_bf16_nt(const GemmReq& r, const GemmPlan& p, void* ws, hipStream
 hipError_t gemm_bf16_tn(const GemmReq& r, const GemmPlan& p, void* ws, hipStream_t st);   // both MN-contig
 
 // Attention (bf16, head width d)
+// dp.thr = 0: no dropout; otherwise attention dropout with dp.mask written by attn_fwd, read by attn_bwd
 hipError_t attn_fwd(int b, int s, int h_t, int heads_t, int d, int causal, const void* QKV, void* O, float* lse,
-                    hipStream_t st);
+                    const DropParams& dp, hipStream_t st);
 hipError_t attn_bwd(int b, int s, int h_t, int heads_t, int d, int causal, const void* QKV, const void* O,
-                    const float* lse, const void* dO, float* Dws, void* dQKV, hipStream_t st);
+                    const float* lse, const void* dO, float* Dws, void* dQKV, const DropParams& dp, hipStream_t st);
 
 // Cross-entropy merge / combine
 size_t xent_tiles_m(int Vt);

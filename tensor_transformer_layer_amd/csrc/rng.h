@@ -7,7 +7,9 @@
 //   keep iff u >= thr, thr = round(p * 65536); kept values are scaled by 65536 / (65536 - thr).
 //   Residual sites over [rows, n]: element (row, c) is slot c % 8 of call row * n/8 + c/8, so the
 //   8 consecutive columns a thread owns are exactly one call.
-//   Attention: see attention.h (one lane's 16 keys of a 32-key tile are two whole calls).
+//   Attention, element (sequence b, global head hg, query q, key k), n32 = ceil(s / 32): slot
+//   ((k % 16) / 8) * 4 + k % 4 of call ((((b heads + hg) s + q) n32 + k / 32) 2 + (k % 8) / 4) 2
+//   + (k % 32) / 16: one lane's 16 keys of a 32-key tile are two whole calls.
 #pragma once
 #include <stdint.h>
 
@@ -21,7 +23,8 @@ struct DropParams {
     uint32_t thr;       // 0 = no dropout
     float scale;        // 65536 / (65536 - thr)
     uint32_t seed_lo, seed_hi, stream;
-    uint16_t* mask;     // attention keep bits (forward writes, backward reads)
+    int head0, heads;   // attention: global index of the rank's first head, heads of all ranks
+    uint32_t* mask;     // attention keep bits [b][heads_t][s][ceil(s/32)]: bit j of word (.., q, kt) keeps key 32 kt + j
 };
 
 // Ten rounds on the counter c with key (k0, k1).

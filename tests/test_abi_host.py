@@ -59,11 +59,14 @@ def test_unaligned_pointer_rejected():
 def test_attention_argument_errors():
     f = tp.lib.tp_attn_shard_fwd
     p = [FAKE] * 8
-    assert f(2, 64, 384, 4, 2, 0, tp.TP_F32, 1, *p, None) == tp.TP_ERR_UNSUPPORTED   # fp32 attention
-    assert f(2, 64, 384, 4, 3, 0, tp.TP_BF16, 1, *p, None) == tp.TP_ERR_SHAPE        # t does not divide heads
-    assert f(2, 64, 384, 5, 1, 0, tp.TP_BF16, 1, *p, None) == tp.TP_ERR_SHAPE        # heads does not divide h
-    assert f(2, 64, 480, 6, 2, 0, tp.TP_BF16, 1, *p, None) == tp.TP_ERR_UNSUPPORTED  # head width 80
-    assert f(2, 64, 384, 4, 2, 0, tp.TP_BF16, 2, *p, None) == tp.TP_ERR_ARG          # causal flag
+    assert f(2, 64, 384, 4, 2, 0, tp.TP_F32, 1, *p, None, None) == tp.TP_ERR_UNSUPPORTED   # fp32 attention
+    assert f(2, 64, 384, 4, 3, 0, tp.TP_BF16, 1, *p, None, None) == tp.TP_ERR_SHAPE        # t does not divide heads
+    assert f(2, 64, 384, 5, 1, 0, tp.TP_BF16, 1, *p, None, None) == tp.TP_ERR_SHAPE        # heads does not divide h
+    assert f(2, 64, 480, 6, 2, 0, tp.TP_BF16, 1, *p, None, None) == tp.TP_ERR_UNSUPPORTED  # head width 80
+    assert f(2, 64, 384, 4, 2, 0, tp.TP_BF16, 2, *p, None, None) == tp.TP_ERR_ARG    # causal flag
+    d = tp.dropout(0.1, 1, 2)                                                          # dropout without a mask
+    assert f(2, 64, 384, 4, 2, 0, tp.TP_BF16, 1, *p, tp._drop(d), None) == tp.TP_ERR_ARG
+    assert tp.tp_attn_dropout_mask_bytes(2, 100, 8, 2) == 2 * 4 * 100 * 4 * 4
 
 
 def test_workspace_too_small():
@@ -72,7 +75,7 @@ def test_workspace_too_small():
     st = tp.lib.tp_mlp_shard_bwd(512, 256, 1024, 2, 0, tp.TP_BF16, *([FAKE] * 10), 0, FAKE, need - 1, None)
     assert st == tp.TP_ERR_WORKSPACE
     need_a = tp.tp_attn_shard_bwd_workspace(2, 128, 384, 4, 2, tp.TP_BF16)
-    st = tp.lib.tp_attn_shard_bwd(2, 128, 384, 4, 2, 0, tp.TP_BF16, 1, *([FAKE] * 11), 0, FAKE, need_a - 1, None)
+    st = tp.lib.tp_attn_shard_bwd(2, 128, 384, 4, 2, 0, tp.TP_BF16, 1, *([FAKE] * 11), 0, None, FAKE, need_a - 1, None)
     assert st == tp.TP_ERR_WORKSPACE
 
 
