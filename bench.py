@@ -166,6 +166,14 @@ def main():
     ap.add_argument("--fp8", action="store_true",
                     help="time rank 0's twelve layer GEMMs (forward, input and weight gradients) in fp8 E4M3 with "
                          "per-tensor scales, each operand quantised in the step, and print their own JSON line")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout probability of every site (residual sites after g with shared streams, "
+                         "attention with per-rank streams); the pages train with 0.1")
+    ap.add_argument("--recompute", action="store_true",
+                    help="activation recompute: the step runs the layer forward again before its backward "
+                         "(the recomputed forward's FLOPs are not counted)")
+    ap.add_argument("--embedding", action="store_true",
+                    help="add rank 0's vocabulary-parallel input-embedding lookup and its backward to the step")
     ap.add_argument("--heads", type=int, default=HEADS,
                     help="attention heads of the layer (the pages' 8.3B head-count sweep uses 16, 24, 32; the "
                          "FLOPs and all other shapes are unchanged, heads per rank = heads / 8)")
@@ -195,12 +203,21 @@ def main():
     if heads % TP or H % heads:
         print(f"--heads {heads}: must be a multiple of t={TP} and divide h={H}", file=sys.stderr)
         sys.exit(2)
-    shards = [LayerShard(B, S, H, heads, FFN, TP, r, rank_params(p, heads, TP, r, dev), dev) for r in range(TP)]
+    if not 0.0 <= args.dropout < 1.0:
+        print("--dropout must be in [0, 1)", file=sys.stderr)
+        sys.exit(2)
+
+    def rank_drop(r):
+        if args.dropout == 0.0:
+            return None
+        return {"p": args.dropout, "seed": 20191004, "resid_streams": (0, 1), "attn_stream": 1000 + r}
+    shards = [LayerShard(B, S, H, heads, FFN, TP, r, rank_params(p, heads, TP, r, dev), dev, rank_drop(r))
+              for r in range(TP)]
     attn_sum = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     mlp_sum, dxn2_sum, dxn1_sum = (torch.empty_like(attn_sum) for _ in range(3))
     shards[0].combine([sh.attn_fwd(x) for sh in shards], None, None, attn_sum)
     x1 = torch.empty_like(attn_sum)
-    shards[0].combine([attn_sum], shards[0].p["bo"], x, x1)
+    shards[0].combine([attn_sum], shards[0].p["bo"], x, x1, shards[0].d_res1)
     shards[0].combine([sh.mlp_fwd(x1) for sh in shards], None, None, mlp_sum)
     shards[0].combine([sh.mlp_bwd(G) for sh in shards], None, None, dxn2_sum)
     dx1 = shards[0].ln2_bwd(dxn2_sum, G)
@@ -226,6 +243,11 @@ def main():
             a.copy_(b_)
     loss = torch.empty(T, dtype=torch.float32, device=dev)
     mean = torch.empty(1, dtype=torch.float32, device=dev)
+    # input embedding of rank 0 (the tied table's shard E0): lookup partial and its backward
+    emb_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    dE0 = torch.empty((Vt, H), dtype=torch.bfloat16, device=dev)
+    emb_ws_bytes = tp.tp_embedding_shard_bwd_workspace(T, VOCAB_PAD, TP)
+    emb_ws = torch.empty(max(emb_ws_bytes, 256), dtype=torch.uint8, device=dev)
 
     stream = torch.cuda.current_stream()
     if args.vocab_bwd:
@@ -240,7 +262,11 @@ def main():
         if record:
             s0 = torch.cuda.Event(enable_timing=True)
             s0.record(stream)
-        rank0.step(x, G, attn_sum, mlp_sum, dxn2_sum, dxn1_sum)
+        if args.embedding:
+            tp.tp_embedding_shard_fwd(T, H, VOCAB_PAD, TP, 0, tp.TP_BF16, tg, E0, emb_out)
+        rank0.step(x, G, attn_sum, mlp_sum, dxn2_sum, dxn1_sum, recompute=args.recompute)
+        if args.embedding:
+            tp.tp_embedding_shard_bwd(T, H, VOCAB_PAD, TP, 0, tp.TP_BF16, tg, rank0.dx, dE0, 0, emb_ws, emb_ws_bytes)
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -285,9 +311,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, uniform targets)",
-        "config": {"workload": "8.3B-shape layer shard t=8 rank 0 fwd+bwd + vocab-parallel xent shard",
+        "config": {"workload": "8.3B-shape layer shard t=8 rank 0 fwd+bwd + vocab-parallel xent shard"
+                               + (" + input-embedding lookup fwd+bwd" if args.embedding else "")
+                               + (f", dropout {args.dropout}" if args.dropout else "")
+                               + (", activation recompute" if args.recompute else ""),
                    "batch": B, "seq_len": S, "hidden": H, "heads": heads, "ffn": FFN, "tp": TP,
-                   "vocab_padded": VOCAB_PAD, "parallelism": "one rank of tp8 (sums pre-staged)"},
+                   "vocab_padded": VOCAB_PAD, "parallelism": "one rank of tp8 (sums pre-staged)",
+                   "dropout": args.dropout, "recompute": args.recompute, "embedding": args.embedding},
         "pct_bf16_peak": round(100 * value * 1e12 / PEAK_BF16, 2),
         "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
         "breakdown": {"layer_gflop": round(fl_layer / 1e9, 2), "xent_gflop": round(fl_xent / 1e9, 2),

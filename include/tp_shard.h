@@ -248,6 +248,14 @@ tp_status tp_sum_partials_layernorm(int T, int h, int t, tp_dtype dt, const void
 tp_status tp_dropout_apply(int rows, int cols, tp_dtype dt, const void* x, void* y,
                            const tp_dropout* drop, hipStream_t stream);
 
+/* tp_dropout_apply fused with the column sums of its result: y = D(x) and colsum_out [cols] (+)=
+ * sum over rows of y (fp32 sums of the values before rounding to dt, fixed order). In the backward
+ * of a residual site this is the branch gradient together with the bias gradient of the
+ * row-parallel layer that feeds the site. Workspace: tp_colsum_workspace(rows, cols, dt). */
+tp_status tp_dropout_colsum(int rows, int cols, tp_dtype dt, const void* x, void* y,
+                            const tp_dropout* drop, void* colsum_out, int accumulate, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Vocabulary-parallel input embedding. Passage: "Megatron-LM ..." digest §3.4, "Input Embedding
  * Parallelism": the table E [Vpad, h] is split over vocabulary entries; rank r holds

@@ -75,6 +75,7 @@ SIGNATURES = {
     "tp_sum_partials": (_i, [_i, _i, _i, _i, _pp, _p, _p, _p, _i, _p, _p]),
     "tp_sum_partials_layernorm": (_i, [_i, _i, _i, _i, _pp, _p, _p, _p, _f, _p, _p, _p, _p, _p, _p, _p]),
     "tp_dropout_apply": (_i, [_i, _i, _i, _p, _p, _p, _p]),
+    "tp_dropout_colsum": (_i, [_i, _i, _i, _p, _p, _p, _p, _i, _p, _z, _p]),
     "tp_embedding_shard_fwd": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p]),
     "tp_embedding_shard_bwd_workspace": (_z, [_i, _i, _i]),
     "tp_embedding_shard_bwd": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _z, _p]),
@@ -229,6 +230,11 @@ def tp_sum_partials_layernorm(T, h, t, dt, parts, bias, residual, out, eps, gamm
 
 def tp_dropout_apply(rows, cols, dt, x, y, drop, stream=None):
     _check(lib.tp_dropout_apply(rows, cols, _dt(dt), _ptr(x), _ptr(y), _drop(drop), _stream(stream)))
+
+
+def tp_dropout_colsum(rows, cols, dt, x, y, drop, colsum_out, accumulate, ws, ws_bytes, stream=None):
+    _check(lib.tp_dropout_colsum(rows, cols, _dt(dt), _ptr(x), _ptr(y), _drop(drop), _ptr(colsum_out), accumulate,
+                                 _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def tp_embedding_shard_fwd(N, h, Vpad, t, r, dt, ids, E_r, out, stream=None):

@@ -591,6 +591,25 @@ tp_status tp_dropout_apply(int rows, int cols, tp_dtype dt, const void* x, void*
     return ok();
 }
 
+tp_status tp_dropout_colsum(int rows, int cols, tp_dtype dt, const void* x, void* y, const tp_dropout* drop,
+                            void* colsum_out, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "tp_dropout_colsum";
+    tp_status s;
+    if ((s = check_dt(fn, dt)) != TP_OK) return s;
+    if (rows < 0) return fail(TP_ERR_SHAPE, "%s: rows=%d is negative", fn, rows);
+    if ((s = check_mult8(fn, "cols", cols)) != TP_OK) return s;
+    if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_ARG, "%s: accumulate=%d must be 0 or 1", fn, accumulate);
+    if (!drop) return fail(TP_ERR_ARG, "%s: drop is NULL", fn);
+    NEED(x); NEED(y); NEED(colsum_out);
+    DropParams dp;
+    if ((s = make_drop(fn, drop, dp)) != TP_OK) return s;
+    const size_t need = tp_colsum_workspace(rows, cols, dt);
+    if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    if (need > 0) NEED(ws);
+    HIP_TRY(dropout_colsum(dt == TP_BF16, rows, cols, x, y, dp, colsum_out, accumulate, (float*)ws, stream), fn);
+    return ok();
+}
+
 tp_status tp_embedding_shard_fwd(int N, int h, int Vpad, int t, int r, tp_dtype dt, const int32_t* ids,
                                  const void* E_r, void* out, hipStream_t stream) {
     const char* fn = "tp_embedding_shard_fwd";

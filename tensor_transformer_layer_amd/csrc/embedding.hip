@@ -4,12 +4,13 @@
 //
 // Forward: one thread per 8 columns of a token row, a 16-byte copy or a 16-byte zero store.
 // Backward, deterministic (no float atomics): dE_r[v] = sum over the tokens i with ids[i] = r*Vt + v
-// of dX[i], in token order. A stable counting sort over chunks of 256 tokens, then ordered sums:
+// of dX[i], in token order. A stable counting sort over chunks of 128 tokens, then ordered sums:
 //   1. emb_rank_kernel (one workgroup per chunk): each owned token's rank among the earlier tokens
 //      of its chunk with the same id, and the chunk's count per table row, written by the last
 //      such token (the chunk histogram H[chunk][v], zero elsewhere).
-//   2. emb_scan_kernel (one workgroup): per table row, the exclusive prefix of H over chunks (in
-//      place), then the exclusive scan of the row totals over rows: segment starts.
+//   2. emb_prefix_kernel (one thread per table row): the exclusive prefix of H over chunks, in
+//      place, and the row totals; emb_scan_kernel (one workgroup): their exclusive scan over rows,
+//      the segment starts.
 //   3. emb_place_kernel: token i goes to start[v] + H[chunk][v] + rank_i.
 //   4. emb_segsum_kernel (one workgroup per table row and 2048-column slice): sums the segment's
 //      dX rows in token order in fp32 and writes (or adds to) dE_r's row; rows without tokens get
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(256) void emb_fwd_kernel(int N, int h, int Vt, int 
     store8(out + (size_t)tok * h + c, f);
 }
 
-constexpr int EMB_CHUNK = 256;
+constexpr int EMB_CHUNK = 128;
 
 // local table row of token i on rank r, or -1
 __device__ __forceinline__ int emb_local(const int32_t* ids, int i, int N, long base, int Vt) {
@@ -68,25 +69,36 @@ __global__ __launch_bounds__(EMB_CHUNK) void emb_rank_kernel(int N, int Vt, int 
     if (after == 0) Hb[l] = before + 1;
 }
 
-// one workgroup of 1024 threads; start has Vt + 1 entries
-__global__ __launch_bounds__(1024) void emb_scan_kernel(int nchunks, int Vt, int* __restrict__ H,
-                                                        int* __restrict__ start) {
+// One thread per table row (coalesced over rows): the exclusive prefix of H[., v] over chunks, in
+// place, and the row total into start[v].
+__global__ __launch_bounds__(256) void emb_prefix_kernel(int nchunks, int Vt, int* __restrict__ H,
+                                                         int* __restrict__ start) {
+    const int v = blockIdx.x * 256 + threadIdx.x;
+    if (v >= Vt) return;
+    int acc = 0;
+    // 16 independent loads in flight, then the running sum over them
+    for (int b0 = 0; b0 < nchunks; b0 += 16) {
+        int c[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) c[j] = (b0 + j < nchunks) ? H[(size_t)(b0 + j) * Vt + v] : 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (b0 + j < nchunks) H[(size_t)(b0 + j) * Vt + v] = acc;
+            acc += c[j];
+        }
+    }
+    start[v] = acc;
+}
+
+// One workgroup of 1024 threads: exclusive scan of the row totals in start[0..Vt) (contiguous runs
+// per thread, then a block scan of the run sums); start[Vt] = all owned tokens.
+__global__ __launch_bounds__(1024) void emb_scan_kernel(int Vt, int* __restrict__ start) {
     __shared__ int wsum[16];
     const int tid = threadIdx.x;
     const int per = (Vt + 1023) / 1024;
     const int lo = min(Vt, tid * per), hi = min(Vt, lo + per);
     int run = 0;
-    for (int v = lo; v < hi; ++v) {
-        int acc = 0;
-        for (int b = 0; b < nchunks; ++b) {
-            int* h = H + (size_t)b * Vt + v;
-            const int c = *h;
-            *h = acc;
-            acc += c;
-        }
-        start[v] = acc;    // row total for now
-        run += acc;
-    }
+    for (int v = lo; v < hi; ++v) run += start[v];
     int incl = run;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -175,7 +187,8 @@ hipError_t embedding_bwd(int dt, int N, int h, int Vt, int r, const int32_t* ids
     w += al256(n * sizeof(int));
     int* start = (int*)w;
     hipLaunchKernelGGL(emb_rank_kernel, dim3(nch), dim3(EMB_CHUNK), 0, st, N, Vt, r, ids, H, rank);
-    hipLaunchKernelGGL(emb_scan_kernel, dim3(1), dim3(1024), 0, st, nch, Vt, H, start);
+    hipLaunchKernelGGL(emb_prefix_kernel, dim3((Vt + 255) / 256), dim3(256), 0, st, nch, Vt, H, start);
+    hipLaunchKernelGGL(emb_scan_kernel, dim3(1), dim3(1024), 0, st, Vt, start);
     if (N > 0)
         hipLaunchKernelGGL(emb_place_kernel, dim3(nch), dim3(EMB_CHUNK), 0, st, N, Vt, r, ids, H, rank, start, order);
     dim3 grid((unsigned)Vt, (unsigned)((h + 2047) / 2048));

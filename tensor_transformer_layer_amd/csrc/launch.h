@@ -99,6 +99,10 @@ int colsum_row_blocks(int rows);
 hipError_t colsum(int dt, int rows, int n, const void* G, void* out, int accumulate, float* ws, hipStream_t st);
 hipError_t sum_partials(int in_dt, int out_dt, size_t rows, int cols, int t, const void* const* parts,
                         const void* bias, const void* residual, void* out, const DropParams& drop, hipStream_t st);
+// y = D(x) over [rows, n] (n % 8 == 0, in place allowed) and out (+)= column sums of y (fp32
+// partials in ws: colsum_row_blocks(rows) x n floats)
+hipError_t dropout_colsum(int dt, int rows, int n, const void* x, void* y, const DropParams& dp, void* out,
+                          int accumulate, float* ws, hipStream_t st);
 // y = D(x) over n contiguous elements of a tensor whose row length is a multiple of 8
 hipError_t dropout(int dt, size_t n, const void* x, void* y, const DropParams& drop, hipStream_t st);
 

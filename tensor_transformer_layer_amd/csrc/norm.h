@@ -316,9 +316,12 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(RowSumJobs jobs, int n
 // 8 columns; block y covers the row range [y*rpb, (y+1)*rpb), wave w its rows w, w+4, ...; the
 // four wave sums are added in wave order and written as part[y][n].
 // ---------------------------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void colsum_partial_kernel(int rows, int n, int rpb, const T* __restrict__ G,
-                                                            float* __restrict__ part) {
+// DROP: y = D(G) is written (in place allowed: each element is read, then written, by one thread)
+// and the column sums are those of D(G) (fp32 values before rounding to T).
+template <typename T, bool DROP = false>
+__global__ __launch_bounds__(256) void colsum_partial_kernel(int rows, int n, int rpb, const T* G,
+                                                            float* __restrict__ part, DropParams dp = DropParams{},
+                                                            T* y = nullptr) {
     __shared__ float red[4][512];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = (blockIdx.x * 64 + lane) * 8;
@@ -329,6 +332,11 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(int rows, int n, in
         for (int r = r0 + wave; r < r1; r += 4) {
             float v[8];
             load8(G + (size_t)r * n + c, v);
+            if constexpr (DROP) {
+                const size_t i = (size_t)r * n + c;
+                apply_keep8(v, keep8(i >> 3, dp), dp.scale);
+                store8(y + i, v);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) a[e] += v[e];
         }

@@ -148,6 +148,28 @@ hipError_t colsum(int dt, int rows, int n, const void* G, void* out, int accumul
                    : reduce_rows<float>(parts, outs, nb, n, accumulate, st);
 }
 
+hipError_t dropout_colsum(int dt, int rows, int n, const void* x, void* y, const DropParams& dp, void* out,
+                          int accumulate, float* ws, hipStream_t st) {
+    int rb = colsum_row_blocks(rows);
+    if (rows > 0) {
+        int rpb = (rows + rb - 1) / rb;
+        dim3 grid((n / 8 + 63) / 64, rb);
+        if (dt == 1)
+            hipLaunchKernelGGL((colsum_partial_kernel<bf16, true>), grid, dim3(256), 0, st, rows, n, rpb, (const bf16*)x,
+                               ws, dp, (bf16*)y);
+        else
+            hipLaunchKernelGGL((colsum_partial_kernel<float, true>), grid, dim3(256), 0, st, rows, n, rpb,
+                               (const float*)x, ws, dp, (float*)y);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int nb = rows > 0 ? rb : 0;
+    const float* parts[RR_JOBS] = {ws, nullptr, nullptr, nullptr};
+    void* outs[RR_JOBS] = {out, nullptr, nullptr, nullptr};
+    return dt == 1 ? reduce_rows<bf16>(parts, outs, nb, n, accumulate, st)
+                   : reduce_rows<float>(parts, outs, nb, n, accumulate, st);
+}
+
 hipError_t sum_partials(int in_dt, int out_dt, size_t rows, int cols, int t, const void* const* parts,
                         const void* bias, const void* residual, void* out, const DropParams& drop, hipStream_t st) {
     size_t n = rows * (size_t)cols;

@@ -15,11 +15,26 @@ The sums in brackets are the all-reduces of a multi-GPU run. Each stage method t
 tensor it needs as an argument, so a caller can run all t ranks on one device and sum their
 partials with tp_sum_partials, or hand one rank the sums it would have received.
 Only torch.empty is used here (device allocation); every computation is a library call.
+
+Dropout (optional; "Megatron-LM ..." digest §3.4, Random Number Generation Handling, and
+"Megatron-LM, annotated", §4.2: p = 0.1): D1 and D2 on the residual branches after g, with one
+stream per site shared by every rank, and attention dropout with a per-rank stream:
+
+    x1 = x + D1(sum_r Z_attn_r + bo)        x2 = x1 + D2(sum_r Z_mlp_r + b2)
+    dm = D2(G) feeds the MLP backward (db2 = colsum(dm)); da = D1(dx1) feeds the attention backward
+    (dbo = colsum(da)); the residual paths carry G and dx1 unchanged.
+
+Recompute (activation checkpointing after every layer, the Chinese reading notes on the paper,
+section on mixed precision and memory management): step(recompute=True) runs the forward again at
+the start of the backward from the layer input alone, as a checkpointed layer does; every kernel
+is deterministic and the dropout draws are counter-based, so the recomputed activations, masks
+and all gradients are bit-identical to the stored-activation step.
 """
 import torch
 
-from . import (TP_BF16, tp_attn_shard_bwd, tp_attn_shard_bwd_workspace, tp_attn_shard_fwd,
-               tp_layernorm_bwd, tp_layernorm_bwd_workspace, tp_layernorm_fwd,
+from . import (TP_BF16, dropout, tp_attn_dropout_mask_bytes, tp_attn_shard_bwd,
+               tp_attn_shard_bwd_workspace, tp_attn_shard_fwd, tp_colsum_workspace,
+               tp_dropout_colsum, tp_layernorm_bwd, tp_layernorm_bwd_workspace, tp_layernorm_fwd,
                tp_mlp_shard_bwd, tp_mlp_shard_bwd_workspace, tp_mlp_shard_fwd, tp_sum_partials,
                tp_sum_partials_layernorm)
 
@@ -28,9 +43,10 @@ EPS = 1e-5
 
 class LayerShard:
     """Rank r of t. ``p`` holds the rank's device tensors (bf16): ln1_g, ln1_b, Wqkv_r, bqkv_r, Wo_r, bo,
-    ln2_g, ln2_b, A_r, b1_r, B_r, b2 (LN parameters and the row-parallel biases are replicated)."""
+    ln2_g, ln2_b, A_r, b1_r, B_r, b2 (LN parameters and the row-parallel biases are replicated).
+    ``drop``: None, or {"p", "seed", "resid_streams": (site 1, site 2), "attn_stream": this rank's}."""
 
-    def __init__(self, b, s, h, heads, ffn, t, r, p, device="cuda:0"):
+    def __init__(self, b, s, h, heads, ffn, t, r, p, device="cuda:0", drop=None):
         self.b, self.s, self.h, self.heads, self.ffn, self.t, self.r = b, s, h, heads, ffn, t, r
         self.p = p
         T = b * s
@@ -56,15 +72,22 @@ class LayerShard:
         self.dln1_g, self.dln1_b = e((h,), **bf), e((h,), **bf)
         self.ws_bytes = max(tp_mlp_shard_bwd_workspace(T, h, ffn, t, TP_BF16),
                             tp_attn_shard_bwd_workspace(b, s, h, heads, t, TP_BF16),
-                            tp_layernorm_bwd_workspace(T, h, TP_BF16))
+                            tp_layernorm_bwd_workspace(T, h, TP_BF16), tp_colsum_workspace(T, h, TP_BF16))
         self.ws = e((self.ws_bytes,), dtype=torch.uint8, device=device)
+        self.d_attn = self.d_res1 = self.d_res2 = None
+        if drop is not None and drop["p"] > 0.0:
+            self.mask = e((max(tp_attn_dropout_mask_bytes(b, s, heads, t) // 4, 1),), dtype=torch.int32, device=device)
+            self.d_attn = dropout(drop["p"], drop["seed"], drop["attn_stream"], self.mask)
+            self.d_res1 = dropout(drop["p"], drop["seed"], drop["resid_streams"][0])
+            self.d_res2 = dropout(drop["p"], drop["seed"], drop["resid_streams"][1])
+            self.dm, self.da = e((T, h), **bf), e((T, h), **bf)
 
     # ---- forward stages ---------------------------------------------------------------------
     def attn_fwd(self, x):
         p, T, h = self.p, self.T, self.h
         tp_layernorm_fwd(T, h, TP_BF16, EPS, x, p["ln1_g"], p["ln1_b"], self.xn1, self.mean1, self.rstd1)
         tp_attn_shard_fwd(self.b, self.s, h, self.heads, self.t, self.r, TP_BF16, 1, self.xn1, p["Wqkv_r"],
-                          p["bqkv_r"], p["Wo_r"], self.QKV, self.O, self.lse, self.Z_attn)
+                          p["bqkv_r"], p["Wo_r"], self.QKV, self.O, self.lse, self.Z_attn, drop=self.d_attn)
         return self.Z_attn
 
     def mlp_fwd(self, x1):
@@ -74,11 +97,11 @@ class LayerShard:
         return self._mlp(self.xn2)
 
     def combine_mlp_fwd(self, attn_parts, x):
-        """g after the attention block fused with LN2: x1 = sum(attn_parts) + bo + x and
+        """g after the attention block fused with LN2: x1 = x + D1(sum(attn_parts) + bo) and
         xn2 = LN2(x1) in one pass, then the MLP shard on xn2."""
         p, T, h = self.p, self.T, self.h
         tp_sum_partials_layernorm(T, h, len(attn_parts), TP_BF16, attn_parts, p["bo"], x, self.x1, EPS, p["ln2_g"],
-                                  p["ln2_b"], self.xn2, self.mean2, self.rstd2)
+                                  p["ln2_b"], self.xn2, self.mean2, self.rstd2, drop=self.d_res1)
         self.x1_in = self.x1
         return self._mlp(self.xn2)
 
@@ -88,29 +111,45 @@ class LayerShard:
                          self.Y, self.Z_mlp)
         return self.Z_mlp
 
-    def combine(self, parts, bias, residual, out):
-        """g / f on one device: out = sum(parts) + bias + residual (bf16)."""
-        tp_sum_partials(self.T, self.h, len(parts), TP_BF16, parts, bias, residual, out, TP_BF16)
+    def combine(self, parts, bias, residual, out, drop=None):
+        """g / f on one device: out = residual + D(sum(parts) + bias) (bf16; D = drop or identity)."""
+        tp_sum_partials(self.T, self.h, len(parts), TP_BF16, parts, bias, residual, out, TP_BF16, drop=drop)
         return out
+
+    def combine_x2(self, mlp_parts):
+        """g after the MLP block: x2 = x1 + D2(sum(mlp_parts) + b2)."""
+        return self.combine(mlp_parts, self.p["b2"], self.x1_in, self.x2, self.d_res2)
 
     # ---- backward stages --------------------------------------------------------------------
     def mlp_bwd(self, G):
         p, T, h = self.p, self.T, self.h
-        tp_mlp_shard_bwd(T, h, self.ffn, self.t, self.r, TP_BF16, self.xn2, p["A_r"], p["B_r"], self.U, self.Y, G,
+        dm = G
+        if self.d_res2 is not None:   # dm = D2(G); db2 = colsum(dm)
+            tp_dropout_colsum(T, h, TP_BF16, G, self.dm, self.d_res2, self.db2, 0, self.ws, self.ws_bytes)
+            dm = self.dm
+        tp_mlp_shard_bwd(T, h, self.ffn, self.t, self.r, TP_BF16, self.xn2, p["A_r"], p["B_r"], self.U, self.Y, dm,
                          self.dXn2, self.dA, self.db1, self.dB, 0, self.ws, self.ws_bytes)
         return self.dXn2
 
     def ln2_bwd(self, dxn2_sum, G):
-        """dx1 = G + LN2^T(dXn2), with db2 = colsum(G) and dbo = colsum(dx1) taken in the same pass."""
+        """dx1 = G + LN2^T(dXn2); without dropout db2 = colsum(G) and dbo = colsum(dx1) are taken in
+        the same pass (with dropout they are sums of the dropped gradients, taken in mlp_bwd and
+        attn_bwd)."""
+        fused = self.d_res1 is None
         tp_layernorm_bwd(self.T, self.h, TP_BF16, self.x1_in, self.p["ln2_g"], self.mean2, self.rstd2, dxn2_sum, G,
-                         self.dx1, self.dln2_g, self.dln2_b, self.db2, self.dbo, 0, self.ws, self.ws_bytes)
+                         self.dx1, self.dln2_g, self.dln2_b, self.db2 if fused else None,
+                         self.dbo if fused else None, 0, self.ws, self.ws_bytes)
         return self.dx1
 
     def attn_bwd(self, dx1):
         p, T, h = self.p, self.T, self.h
+        da = dx1
+        if self.d_res1 is not None:   # da = D1(dx1); dbo = colsum(da)
+            tp_dropout_colsum(T, h, TP_BF16, dx1, self.da, self.d_res1, self.dbo, 0, self.ws, self.ws_bytes)
+            da = self.da
         tp_attn_shard_bwd(self.b, self.s, h, self.heads, self.t, self.r, TP_BF16, 1, self.xn1, p["Wqkv_r"],
-                          p["Wo_r"], self.QKV, self.O, self.lse, dx1, self.dXn1, self.dWqkv, self.dbqkv, self.dWo, 0,
-                          self.ws, self.ws_bytes)
+                          p["Wo_r"], self.QKV, self.O, self.lse, da, self.dXn1, self.dWqkv, self.dbqkv, self.dWo, 0,
+                          self.ws, self.ws_bytes, drop=self.d_attn)
         return self.dXn1
 
     def ln1_bwd(self, x, dxn1_sum, dx1):
@@ -119,13 +158,16 @@ class LayerShard:
         return self.dx
 
     # ---- one rank's whole step with the peers' sums handed in -----------------------------
-    def step(self, x, G, attn_sum, mlp_sum, dxn2_sum, dxn1_sum):
+    def step(self, x, G, attn_sum, mlp_sum, dxn2_sum, dxn1_sum, recompute=False):
         """Forward + backward of this rank. The four *_sum tensors are what the rank would receive
-        from the all-reduces (the sum over ranks of the partials, before bias and residual)."""
-        p = self.p
+        from the all-reduces (the sum over ranks of the partials, before bias and residual).
+        recompute: run the forward again from x before the backward (activation checkpointing)."""
         self.attn_fwd(x)
         self.combine_mlp_fwd([attn_sum], x)
-        self.combine([mlp_sum], p["b2"], self.x1, self.x2)
+        self.combine_x2([mlp_sum])
+        if recompute:
+            self.attn_fwd(x)
+            self.combine_mlp_fwd([attn_sum], x)
         self.mlp_bwd(G)
         self.ln2_bwd(dxn2_sum, G)
         self.attn_bwd(self.dx1)

@@ -45,6 +45,29 @@ def test_dropout_apply(dtype, p):
     assert np.array_equal(host(xi), got)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dropout_colsum(dtype):
+    T, n, p = 1000, 136, 0.25
+    x = nonzero((T, n), 42, dtype)
+    d = tp.dropout(p, seed=77, stream=5)
+    y, cs = empty((T, n), dtype), empty((n,), dtype)
+    nb = tp.tp_colsum_workspace(T, n, TPDT[dtype])
+    say(f"[drop] dropout+colsum {dtype}")
+    tp.tp_dropout_colsum(T, n, TPDT[dtype], dev(x, dtype), y, d, cs, 0, ws(nb), nb)
+    keep = rng.residual_keep(T, n, p, 77, 5)
+    ref = rng.dropout_apply(x, keep, p)
+    got = host(y)
+    assert np.array_equal(got != 0, keep)
+    assert rel_l2(got, ref) <= TOL[dtype]
+    assert rel_l2(host(cs), ref.sum(axis=0)) <= TOL[dtype]
+    # accumulate, in place
+    base = tp_synth.normal(43, 1, (n,), 1.0, dtype)
+    cs2, xi = dev(base, dtype), dev(x, dtype)
+    tp.tp_dropout_colsum(T, n, TPDT[dtype], xi, xi, d, cs2, 1, ws(nb), nb)
+    assert np.array_equal(host(xi), got)
+    assert rel_l2(host(cs2), ref.sum(axis=0) + base) <= TOL[dtype]
+
+
 def test_dropout_full_size_mask():
     """The 8.3B activation [8192, 3072]: every keep bit against the oracle's generator."""
     T, n, p = 8192, 3072, 0.1

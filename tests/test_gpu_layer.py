@@ -16,7 +16,14 @@ tp = pytest.importorskip("tensor_transformer_layer_amd")
 from tensor_transformer_layer_amd.layer import LayerShard, rank_params  # noqa: E402
 
 
-def run_layer(p, b, s, h, heads, ffn, t):
+def rank_drop(drop, r):
+    if drop is None:
+        return None
+    return {"p": drop["p"], "seed": drop["seed"], "resid_streams": drop["resid_streams"],
+            "attn_stream": drop["attn_streams"][r]}
+
+
+def run_layer(p, b, s, h, heads, ffn, t, drop=None):
     dev = "cuda:0"
 
     def d(a):
@@ -24,11 +31,12 @@ def run_layer(p, b, s, h, heads, ffn, t):
 
     T = b * s
     x, G = d(p["x"]), d(p["G"])
-    shards = [LayerShard(b, s, h, heads, ffn, t, r, rank_params(p, heads, t, r, dev), dev) for r in range(t)]
+    shards = [LayerShard(b, s, h, heads, ffn, t, r, rank_params(p, heads, t, r, dev), dev, rank_drop(drop, r))
+              for r in range(t)]
     bf = dict(dtype=torch.bfloat16, device=dev)
     x1, x2 = torch.empty((T, h), **bf), torch.empty((T, h), **bf)
-    shards[0].combine([sh.attn_fwd(x) for sh in shards], shards[0].p["bo"], x, x1)
-    shards[0].combine([sh.mlp_fwd(x1) for sh in shards], shards[0].p["b2"], x1, x2)
+    shards[0].combine([sh.attn_fwd(x) for sh in shards], shards[0].p["bo"], x, x1, shards[0].d_res1)
+    shards[0].combine([sh.mlp_fwd(x1) for sh in shards], shards[0].p["b2"], x1, x2, shards[0].d_res2)
     dxn2 = torch.empty((T, h), **bf)
     shards[0].combine([sh.mlp_bwd(G) for sh in shards], None, None, dxn2)
     dx1 = shards[0].ln2_bwd(dxn2, G)
@@ -97,3 +105,66 @@ def test_layer_step_method_rank0():
     say("[layer.step] " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     for k, e in errs.items():
         assert e <= 1e-2, (k, e)
+
+
+DROP = {"p": 0.1, "seed": 0xC0FFEE1234, "resid_streams": (11, 12), "attn_streams": [100, 101]}
+
+
+def test_layer_step_dropout_every_output():
+    """Every dropout site on (p = 0.1): residual sites with shared streams, attention with per-rank
+    streams; every output and gradient of both ranks against the oracle's split layer."""
+    b, s, h, heads, ffn, t = 2, 160, 384, 4, 1536, 2
+    p = tp_synth.layer_inputs(4545, b, s, h, ffn, "bf16", bias_std=0.05, ln_random=True)
+    shards, x1, x2, dx1, dx = run_layer(p, b, s, h, heads, ffn, t, DROP)
+    f = oracle.layer_split_fwd(p["x"], p, b, s, heads, t, drop=DROP)
+    g = oracle.layer_split_bwd(p["x"], p, f, p["G"], b, s, heads, t)
+    ht, Ft = h // t, ffn // t
+    errs = {"x1": rel_l2(host(x1), f["x1"]), "x2": rel_l2(host(x2), f["x2"]), "dx1": rel_l2(host(dx1), g["dx1"]),
+            "dx": rel_l2(host(dx), g["dx"])}
+    sh0 = shards[0]
+    for k, ref in (("dln1_g", g["dln1_g"]), ("dln2_g", g["dln2_g"]), ("db2", g["mlp"]["db2"]),
+                   ("dbo", g["attn"]["dbo"])):
+        errs[k] = rel_l2(host(getattr(sh0, k)), ref)
+    for r, sh in enumerate(shards):
+        qcols = np.concatenate([np.arange(i * h + r * ht, i * h + (r + 1) * ht) for i in range(3)])
+        want = {"dA": g["mlp"]["dA"][:, r * Ft:(r + 1) * Ft], "dB": g["mlp"]["dB"][r * Ft:(r + 1) * Ft],
+                "dWqkv": g["attn"]["dWqkv"][:, qcols], "dbqkv": g["attn"]["dbqkv"][qcols],
+                "dWo": g["attn"]["dWo"][r * ht:(r + 1) * ht]}
+        for k, ref in want.items():
+            errs[f"{k}[{r}]"] = rel_l2(host(getattr(sh, k)), ref)
+    say("[layer+drop] " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    for k, e in errs.items():
+        assert e <= 1e-2, (k, e)
+
+
+@pytest.mark.parametrize("drop", [None, DROP])
+def test_layer_step_recompute_is_bit_identical(drop):
+    """step(recompute=True) re-runs the forward from x before the backward: every output and
+    gradient must equal the stored-activation step bit for bit (deterministic kernels,
+    counter-based dropout)."""
+    b, s, h, heads, ffn, t = 2, 128, 256, 4, 1024, 2
+    p = tp_synth.layer_inputs(4646, b, s, h, ffn, "bf16", bias_std=0.05, ln_random=True)
+    shards, _x1, _x2, _dx1, _dx = run_layer(p, b, s, h, heads, ffn, t, drop)
+    dev = "cuda:0"
+    T = b * s
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    x = torch.from_numpy(np.ascontiguousarray(p["x"])).to(torch.bfloat16).to(dev)
+    G = torch.from_numpy(np.ascontiguousarray(p["G"])).to(torch.bfloat16).to(dev)
+    sums = [torch.empty((T, h), **bf) for _ in range(4)]
+    shards[0].combine([sh.attn_fwd(x) for sh in shards], None, None, sums[0])
+    x1 = torch.empty((T, h), **bf)
+    shards[0].combine([sums[0]], shards[0].p["bo"], x, x1, shards[0].d_res1)
+    shards[0].combine([sh.mlp_fwd(x1) for sh in shards], None, None, sums[1])
+    shards[0].combine([sh.mlp_bwd(G) for sh in shards], None, None, sums[2])
+    dx1 = shards[0].ln2_bwd(sums[2], G)
+    shards[0].combine([sh.attn_bwd(dx1) for sh in shards], None, None, sums[3])
+    names = ("x2", "dx", "dA", "db1", "dB", "db2", "dWqkv", "dbqkv", "dWo", "dbo", "dln1_g", "dln1_b", "dln2_g",
+             "dln2_b")
+    say(f"[layer.step recompute] drop={drop is not None}")
+    shards[0].step(x, G, *sums, recompute=False)
+    torch.cuda.synchronize()
+    first = {k: getattr(shards[0], k).clone() for k in names}
+    shards[0].step(x, G, *sums, recompute=True)
+    torch.cuda.synchronize()
+    for k in names:
+        assert torch.equal(getattr(shards[0], k), first[k]), k
