@@ -111,10 +111,10 @@ template <int R, int NT> struct Operand<R, NT, MNCONTIG> {
     static constexpr bool DMA = false;
     static constexpr int BYTES = R * 128;
     static constexpr int MC = R / 8;          // 8-wide mn chunks across the tile
-    static constexpr int KB = (MC * 8 >= NT) ? 8 : 4;   // k-rows per thread
-    static constexpr int USED = MC * (64 / KB);        // threads that carry a block
+    static constexpr int KB = (MC * 16 <= NT) ? 4 : 8;  // k-rows per thread: 4 when the threads suffice
+    static constexpr int USED = MC * (64 / KB);         // threads that carry a block
     static constexpr int NLOAD = KB, NSTORE = 8;
-    static_assert(USED <= NT && (MC * 8 == NT || MC * 16 <= NT), "thread mapping must cover the tile exactly");
+    static_assert(USED <= NT, "thread mapping must cover the tile");
     Operand<R, NT, KCONTIG> kc;   // fragment addressing of the K-contiguous layout
     u32x4 v[KB];
     __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, int ld, int mn0, int MN, int k0, int K, int tid) {
