@@ -174,6 +174,8 @@ def main():
                          "(the recomputed forward's FLOPs are not counted)")
     ap.add_argument("--embedding", action="store_true",
                     help="add rank 0's vocabulary-parallel input-embedding lookup and its backward to the step")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the step into a HIP graph and time its replays (prints its own JSON line)")
     ap.add_argument("--heads", type=int, default=HEADS,
                     help="attention heads of the layer (the pages' 8.3B head-count sweep uses 16, 24, 32; the "
                          "FLOPs and all other shapes are unchanged, heads per rank = heads / 8)")
@@ -284,6 +286,8 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
+    if args.graph:
+        return bench_graph(args, torch, step, heads, stream)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(args.steps):
@@ -333,6 +337,41 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, xe, heads=heads)
     print(json.dumps(out), flush=True)
+
+
+def bench_graph(args, torch, step, heads, stream):
+    """The same step captured once into a HIP graph (every call is a kernel launch on the captured
+    stream) and replayed; each replay is bracketed by events outside the graph."""
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.graph(graph, stream=side):
+        step(False)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(args.steps):
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graph.replay()
+        b_.record(stream)
+        ev.append((a, b_))
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b_) for a, b_ in ev])
+    ms = float(per.mean())
+    fl = layer_flops(B, S, H, heads, FFN, TP) + xent_flops(B * S, H, VOCAB_PAD // TP)
+    value = fl / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "layer-shard TFLOP/s fwd+bwd (% bf16 MFMA peak), 8.3B shape t=8, 1 GPU, HIP graph replay",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, uniform targets)",
+        "config": {"workload": "the default step (layer shard fwd+bwd + vocab-parallel xent shard) as one graph",
+                   "dropout": args.dropout, "recompute": args.recompute, "embedding": args.embedding},
+        "pct_bf16_peak": round(100 * value * 1e12 / PEAK_BF16, 2),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(per, q)), 4) for q in (10, 50, 90)]}), flush=True)
 
 
 def bench_vocab_bwd(args, tp, torch, T, Vt, Xv, E0, tg, peers, stream):
