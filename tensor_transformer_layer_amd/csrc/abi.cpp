@@ -193,9 +193,7 @@ tp_status check_vocab(const char* fn, int N, int h, int Vpad, int t, int r, tp_d
 }
 
 size_t xent_ws(int N, int h, int Vt) {
-    GemmPlan p = plan_gemm_bf16(Vt, N, h, false);
-    size_t tiles_m = (size_t)(Vt + p.bm - 1) / p.bm;
-    return al256(tiles_m * (size_t)N * 16);
+    return al256((size_t)plan_vocab(Vt, N, h).tiles_m * (size_t)N * 16);
 }
 
 }  // namespace
@@ -364,14 +362,25 @@ tp_status tp_vocab_xent_shard_fwd(int N, int h, int Vpad, int Vreal, int t, int 
     if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
     if (need > 0) NEED(ws);
     if (N == 0) return ok();
-    GemmPlan p = plan_gemm_bf16(Vt, N, h, false);
-    GemmReq g = req(Vt, N, h, E_r, h, 0, X, h, 0, EPI_XENT, ws, 0);
+    // rows [0, main_rows) and [main_rows, Vt) of the shard; the tail's partials follow the main
+    // part's tile rows, so the merge reads the tiles in row order
+    const VocabPlan vp = plan_vocab(Vt, N, h);
+    GemmReq g = req(vp.main_rows, N, h, E_r, h, 0, X, h, 0, EPI_XENT, ws, 0);
     g.targets = targets;
     g.col0 = r * Vt;
     g.Vreal = Vreal;
     g.mask = mask_padding;
-    HIP_TRY(gemm_bf16(g, p, nullptr, stream), "tp_vocab_xent_shard_fwd: fused logits GEMM");
-    HIP_TRY(xent_merge(ws, (Vt + p.bm - 1) / p.bm, N, r * Vt, max_r, sumexp_r, tgt_r, argmax_r, stream),
+    HIP_TRY(gemm_bf16(g, vp.main, nullptr, stream), "tp_vocab_xent_shard_fwd: fused logits GEMM");
+    if (vp.main_rows < Vt) {
+        const int main_tiles = vp.main_rows / vp.main.bm;
+        g.M = Vt - vp.main_rows;
+        g.A = (const char*)E_r + (size_t)vp.main_rows * h * 2;
+        g.out = (char*)ws + (size_t)main_tiles * N * 16;
+        g.col0 = r * Vt + vp.main_rows;
+        g.row0 = vp.main_rows;
+        HIP_TRY(gemm_bf16(g, vp.tail, nullptr, stream), "tp_vocab_xent_shard_fwd: fused logits GEMM (last rows)");
+    }
+    HIP_TRY(xent_merge(ws, vp.tiles_m, N, r * Vt, max_r, sumexp_r, tgt_r, argmax_r, stream),
             "tp_vocab_xent_shard_fwd: tile merge");
     return ok();
 }

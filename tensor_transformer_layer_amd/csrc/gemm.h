@@ -31,17 +31,22 @@ namespace tp {
 
 enum Layout { KCONTIG = 0, MNCONTIG = 1 };
 
-template <int BM_, int BN_, int WGM_, int WGN_>
+// NS = LDS stages: 2 (double buffering), or more for configurations whose operands both go
+// through DMA, where the loads of tile k + NS - 1 are in flight while tile k is multiplied.
+template <int BM_, int BN_, int WGM_, int WGN_, int NS_ = 2>
 struct GemmCfg {
     static constexpr int BM = BM_, BN = BN_, BK = 64;
     static constexpr int WGM = WGM_, WGN = WGN_;
     static constexpr int NW = WGM * WGN, NT = 64 * NW;
     static constexpr int WM = BM / WGM, WN = BN / WGN;
     static constexpr int TM = WM / 32, TN = WN / 32;
+    static constexpr int NS = NS_;
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int LDS = 2 * STAGE;
+    static constexpr int B_BASE = NS * A_BYTES;   // LDS: [A stage 0 .. NS-1 | B stage 0 .. NS-1]
+    static constexpr int LDS = NS * STAGE;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert(NS >= 2 && LDS <= 160 * 1024, "stages must fit the 160 KB of LDS");
 };
 
 // 256x256 and 256x192 with 8 waves (128x64 / 64x96 per wave, two waves per SIMD) and 128x128
@@ -50,6 +55,9 @@ struct GemmCfg {
 typedef GemmCfg<256, 256, 2, 4> Cfg256x256;
 typedef GemmCfg<256, 192, 4, 2> Cfg256x192;   // 8 waves, 64x96 per wave: N = 1536 / 3072 / 1152 in whole tiles
 typedef GemmCfg<128, 128, 2, 2> Cfg128x128;
+// 64x64 with 4 waves of 32x32 and four LDS stages (32 KB each side: two workgroups per CU): for
+// the thin remainder of a large GEMM, where few MFMAs per k-step leave the loads exposed
+typedef GemmCfg<64, 64, 2, 2, 4> Cfg64x64s4;
 
 // Buffer resource over [base, base + bytes): loads at offsets >= bytes return 0, which is how
 // masked chunks are zero-filled without a branch.
@@ -356,7 +364,7 @@ template <class C, int LA, int LB, int ST>
 __device__ __forceinline__ void read_frags(const GemmState<C, LA, LB>& g, const char* smem, int s, bf16x8 (&af)[C::TM],
                                            bf16x8 (&bf)[C::TN]) {
     const char* As = smem + ST * C::A_BYTES;
-    const char* Bs = smem + 2 * C::A_BYTES + ST * C::B_BYTES;
+    const char* Bs = smem + C::B_BASE + ST * C::B_BYTES;
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) af[i] = g.oa.frag(As, i, s);
 #pragma unroll
@@ -384,13 +392,13 @@ __device__ __forceinline__ void load_stage(GemmState<C, LA, LB>& g, char* smem, 
     if constexpr (decltype(g.oa)::DMA) g.oa.load(g.ra, g.lda, g.m0, g.M, k0, g.kend, g.tid, smem + stage * C::A_BYTES);
     else g.oa.fetch(g.ra, g.lda, g.m0, g.M, k0, g.kend, g.tid);
     if constexpr (decltype(g.ob)::DMA)
-        g.ob.load(g.rb, g.ldb, g.n0, g.N, k0, g.kend, g.tid, smem + 2 * C::A_BYTES + stage * C::B_BYTES);
+        g.ob.load(g.rb, g.ldb, g.n0, g.N, k0, g.kend, g.tid, smem + C::B_BASE + stage * C::B_BYTES);
     else g.ob.fetch(g.rb, g.ldb, g.n0, g.N, k0, g.kend, g.tid);
 }
 template <class C, int LA, int LB>
 __device__ __forceinline__ void store_stage(const GemmState<C, LA, LB>& g, char* smem, int stage) {
     if constexpr (!decltype(g.oa)::DMA) g.oa.store(smem + stage * C::A_BYTES, g.tid);
-    if constexpr (!decltype(g.ob)::DMA) g.ob.store(smem + 2 * C::A_BYTES + stage * C::B_BYTES, g.tid);
+    if constexpr (!decltype(g.ob)::DMA) g.ob.store(smem + C::B_BASE + stage * C::B_BYTES, g.tid);
 }
 
 constexpr int SG_DS_WRITE = 0x200;
@@ -436,6 +444,60 @@ __device__ __forceinline__ void gemm_tile(GemmState<C, LA, LB>& g, char* smem, f
     if (more) read_frags<C, LA, LB, ST ^ 1>(g, smem, 0, g.a0, g.b0);
 }
 
+// NS > 2 (both operands DMA): the tile in stage ST fetches tile kt + NS - 1 into stage
+// (ST + NS - 1) % NS, the one read during the previous tile and released by its barrier. The
+// fetch is issued even past the end of K (it zero-fills a stage nobody reads), so every wave has
+// the same count of DMA instructions in flight and the wait for tile kt + 1 is a fixed vmcnt.
+template <class C, int LA, int LB, int ST>
+__device__ __forceinline__ void gemm_tile_ms(GemmState<C, LA, LB>& g, char* smem, f32x16 (&acc)[C::TM][C::TN], int kt,
+                                             int nk) {
+    static_assert(decltype(g.oa)::DMA && decltype(g.ob)::DMA, "multi-stage tiles need DMA operands");
+    constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
+    constexpr int PER_TILE = decltype(g.oa)::IPW + decltype(g.ob)::IPW;   // DMA instructions per wave per tile
+    load_stage(g, smem, (ST + C::NS - 1) % C::NS, g.kbeg + (kt + C::NS - 1) * C::BK);
+    read_frags<C, LA, LB, ST>(g, smem, 1, g.a1, g.b1);
+    mfma_step<C>(acc, g.a0, g.b0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags<C, LA, LB, ST>(g, smem, 2, g.a0, g.b0);
+    mfma_step<C>(acc, g.a1, g.b1);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags<C, LA, LB, ST>(g, smem, 3, g.a1, g.b1);
+    mfma_step<C>(acc, g.a0, g.b0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step<C>(acc, g.a1, g.b1);
+    __builtin_amdgcn_sched_barrier(0);
+    // this wave's DMA of tile kt + 1 has landed (tiles kt + 2 .. kt + NS - 1 may still be in flight)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((C::NS - 2) * PER_TILE) : "memory");
+    __syncthreads();
+    if (kt + 1 < nk) read_frags<C, LA, LB, (ST + 1) % C::NS>(g, smem, 0, g.a0, g.b0);
+}
+
+// NS consecutive tiles, stages 0 .. NS-1.
+template <class C, int LA, int LB, int ST>
+__device__ __forceinline__ void gemm_tiles_ms_round(GemmState<C, LA, LB>& g, char* smem, f32x16 (&acc)[C::TM][C::TN],
+                                                    int kt, int nk) {
+    gemm_tile_ms<C, LA, LB, ST>(g, smem, acc, kt + ST, nk);
+    if constexpr (ST + 1 < C::NS) gemm_tiles_ms_round<C, LA, LB, ST + 1>(g, smem, acc, kt, nk);
+}
+
+// The last nk - kt < NS tiles (kt a multiple of NS).
+template <class C, int LA, int LB, int ST>
+__device__ __forceinline__ void gemm_tiles_ms_tail(GemmState<C, LA, LB>& g, char* smem, f32x16 (&acc)[C::TM][C::TN],
+                                                   int kt, int nk) {
+    if constexpr (ST < C::NS - 1) {
+        if (kt < nk) {
+            gemm_tile_ms<C, LA, LB, ST>(g, smem, acc, kt, nk);
+            gemm_tiles_ms_tail<C, LA, LB, ST + 1>(g, smem, acc, kt + 1, nk);
+        }
+    }
+}
+
 template <class C, int LA, int LB, class Epi>
 __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restrict__ A, int lda,
                                                              const bf16* __restrict__ B, int ldb,
@@ -471,19 +533,34 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restr
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int nk = g.kend > g.kbeg ? (g.kend - g.kbeg + C::BK - 1) / C::BK : 0;
-    if (nk > 0) {
-        load_stage(g, smem, 0, g.kbeg);
-        store_stage(g, smem, 0);
+    if constexpr (C::NS == 2) {
+        if (nk > 0) {
+            load_stage(g, smem, 0, g.kbeg);
+            store_stage(g, smem, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (nk > 0) read_frags<C, LA, LB, 0>(g, smem, 0, g.a0, g.b0);
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            gemm_tile<C, LA, LB, 0>(g, smem, acc, kt, nk);
+            gemm_tile<C, LA, LB, 1>(g, smem, acc, kt + 1, nk);
+        }
+        if (kt < nk) gemm_tile<C, LA, LB, 0>(g, smem, acc, kt, nk);
+    } else if (nk > 0) {
+        constexpr int PER_TILE = decltype(g.oa)::IPW + decltype(g.ob)::IPW;
+#pragma unroll
+        for (int s = 0; s < C::NS - 1; ++s) load_stage(g, smem, s, g.kbeg + s * C::BK);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((C::NS - 2) * PER_TILE) : "memory");
+        __syncthreads();
+        read_frags<C, LA, LB, 0>(g, smem, 0, g.a0, g.b0);
+        int kt = 0;
+        for (; kt + C::NS <= nk; kt += C::NS) gemm_tiles_ms_round<C, LA, LB, 0>(g, smem, acc, kt, nk);
+        gemm_tiles_ms_tail<C, LA, LB, 0>(g, smem, acc, kt, nk);
+        // the zero-fill DMAs issued past the end of K land before the epilogue reuses the LDS
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (nk > 0) read_frags<C, LA, LB, 0>(g, smem, 0, g.a0, g.b0);
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        gemm_tile<C, LA, LB, 0>(g, smem, acc, kt, nk);
-        gemm_tile<C, LA, LB, 1>(g, smem, acc, kt + 1, nk);
-    }
-    if (kt < nk) gemm_tile<C, LA, LB, 0>(g, smem, acc, kt, nk);
     ep.template apply<C>(acc, g.m0, g.n0, g.m0 + wm * C::WM, g.n0 + wn * C::WN, lane, M, N, smem);
 }
 

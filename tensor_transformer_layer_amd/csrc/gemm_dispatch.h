@@ -32,6 +32,9 @@ static hipError_t launch_plan(const GemmReq& r, const GemmPlan& p, const Epi& e,
         case 0: return launch_cfg<Cfg256x256, LA, LB>(r, p.splits, e, st);
         case 1: return launch_cfg<Cfg128x128, LA, LB>(r, p.splits, e, st);
         case 2: return launch_cfg<Cfg256x192, LA, LB>(r, p.splits, e, st);
+        case 3:
+            if constexpr (LA == KCONTIG && LB == KCONTIG) return launch_cfg<Cfg64x64s4, LA, LB>(r, p.splits, e, st);
+            break;
     }
     return hipErrorInvalidValue;
 }
@@ -72,7 +75,7 @@ static hipError_t gemm_run(const GemmReq& r, const GemmPlan& p, void* ws, hipStr
             break;
         case EPI_XENT:
             if constexpr ((KINDS & (1 << EPI_XENT)) != 0)
-                return launch_plan<LA, LB>(r, p, EpiXent{(XentPartial*)r.out, r.targets, r.col0, r.Vreal, r.mask}, st);
+                return launch_plan<LA, LB>(r, p, EpiXent{(XentPartial*)r.out, r.targets, r.col0, r.Vreal, r.mask, r.row0}, st);
             break;
         case EPI_XENT_GRAD:
             if constexpr ((KINDS & (1 << EPI_XENT_GRAD)) != 0) {

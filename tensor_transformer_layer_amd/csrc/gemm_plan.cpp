@@ -24,7 +24,7 @@ static const TunedPlan kTuned[] = {
     {8192, 3072, 384, 0, 2, 1},    // output projection fwd
     {8192, 384, 3072, 0, 1, 1},    // dO
     {8192, 3072, 1152, 0, 2, 1},   // dXn
-    {6400, 8192, 3072, 0, 1, 1},   // vocabulary logits
+    {6400, 8192, 3072, 0, 1, 1},   // vocabulary logits (stored, and their gradient)
     {1536, 3072, 8192, 1, 0, 3},   // dB
     {3072, 1536, 8192, 1, 0, 3},   // dA
     {384, 3072, 8192, 1, 1, 6},    // dWo
@@ -69,6 +69,24 @@ GemmPlan plan_gemm_bf16(int M, int N, int K, bool allow_split) {
 // spill).
 GemmPlan plan_gemm_fp8(int M, int N, int K, bool allow_split) {
     return plan_model(M, N, K, allow_split, 128, 5.0e15, 6);
+}
+
+VocabPlan plan_vocab(int Vt, int N, int K) {
+    VocabPlan v;
+    const long tn = (N + 255) / 256, total = (long)((Vt + 255) / 256) * tn, rounds = total / kCUs;
+    const long rows_main = tn > 0 ? rounds * kCUs / tn : 0;
+    if (rounds == 0 || total % kCUs == 0 || rows_main == 0 || rows_main * 256 >= Vt) {
+        v.main = (rounds > 0 && total % kCUs == 0) ? GemmPlan{0, 1, 256, 256} : plan_gemm_bf16(Vt, N, K, false);
+        v.main_rows = Vt;
+        v.tail = v.main;
+        v.tiles_m = (Vt + v.main.bm - 1) / v.main.bm;
+        return v;
+    }
+    v.main = GemmPlan{0, 1, 256, 256};
+    v.tail = GemmPlan{3, 1, 64, 64};
+    v.main_rows = (int)rows_main * 256;
+    v.tiles_m = (int)rows_main + (Vt - v.main_rows + 63) / 64;
+    return v;
 }
 
 size_t split_ws_bytes(const GemmPlan& p, int M, int N) {

@@ -29,6 +29,7 @@ struct GemmReq {
     const void* bias; const void* aux; int accumulate;
     // EPI_XENT, EPI_XENT_GRAD
     const int32_t* targets; int col0, Vreal, mask;
+    int row0;   // EPI_XENT: added to the reported argmax rows (a launch over a slice of the rows)
     // EPI_XENT_GRAD: merged per-token max and sum, upstream gradient; out2 = token-major copy (ld2)
     const float* stat_m; const float* stat_s; const float* dloss; int ld2;
     // fp8 GEMM: device pointers to the per-tensor descales of A and B
@@ -36,7 +37,8 @@ struct GemmReq {
 };
 
 struct GemmPlan {
-    int cfg;      // 0: 256x256 (8 waves), 1: 128x128 (4 waves), 2: 256x192 (8 waves)
+    int cfg;      // 0: 256x256 (8 waves), 1: 128x128 (4 waves), 2: 256x192 (8 waves),
+                  // 3: 64x64 (4 waves, 4 LDS stages; both operands K-contiguous only)
     int splits;   // K splits (>1 only when the request allows it)
     int bm, bn;
 };
@@ -74,8 +76,20 @@ hipError_t attn_fwd(int b, int s, int h_t, int heads_t, int d, int causal, const
 hipError_t attn_bwd(int b, int s, int h_t, int heads_t, int d, int causal, const void* QKV, const void* O,
                     const float* lse, const void* dO, float* Dws, void* dQKV, const DropParams& dp, hipStream_t st);
 
+// Fused logits GEMM of a vocabulary shard (Vt rows x N tokens, depth K), in two launches: 256x256
+// tiles over rows [0, main_rows) -- as many whole rounds of tiles over the 256 CUs as the shape
+// holds -- and 64x64 tiles (two workgroups per CU) over the remaining rows, so the last round
+// is not a partly filled round of large tiles. When the shape has no whole round, or its tiles
+// fill whole rounds, one launch with the ordinary plan covers all rows (main_rows = Vt).
+// tiles_m = tile rows of both parts (the per-token partials the merge reads).
+struct VocabPlan {
+    int main_rows;
+    GemmPlan main, tail;
+    int tiles_m;
+};
+VocabPlan plan_vocab(int Vt, int N, int K);
+
 // Cross-entropy merge / combine
-size_t xent_tiles_m(int Vt);
 hipError_t xent_merge(const void* part, int tiles_m, int N, int col0, float* mx, float* se, float* tg,
                       int32_t* am, hipStream_t st);
 hipError_t xent_combine(int N, int t, const float* const* mx, const float* const* se, const float* const* tg,

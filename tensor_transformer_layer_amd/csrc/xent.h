@@ -40,6 +40,7 @@ struct EpiXent {
     int col0;                 // global id of local row 0 (r * V_t)
     int Vreal;
     int mask;                 // 1: rows with col0 + row >= Vreal are -inf
+    int row0;                 // added to the reported argmax row (launches over a slice of the shard's rows)
     __device__ __forceinline__ void set_split(int) {}
 
     template <class C>
@@ -115,6 +116,7 @@ struct EpiXent {
                 p.am = am;
                 p.tv += q.tv;
             }
+            if (p.am != INT_MAX) p.am += row0;
             part[(size_t)tm * N + n] = p;
         }
     }

@@ -75,6 +75,31 @@ def test_xent_small_ragged(mask):
     assert abs(host(mean)[0] - ref.mean()) <= 1e-2 * abs(ref.mean())
 
 
+@pytest.mark.parametrize("mask,h", [(1, 136), (0, 520)])
+def test_xent_two_part_launch(mask, h):
+    """A shard whose 256x256 tiles overflow whole rounds over the 256 CUs (V_t = 4160 rows,
+    N = 4136 tokens: 17 x 17 tiles): the library runs 256x256 tiles over the first 3840 rows and
+    64x64 tiles (four LDS stages) over the last 320, which hold the padded rows of the last rank
+    (Vreal = 8300 of Vpad = 8320, t = 2). h = 136 gives fewer K tiles than stages, h = 520 two
+    rounds of stages and one more tile. Both ranks against the oracle; max, argmax and target
+    logits bit-exact against the kernel's own fp32 logits."""
+    N, Vreal, t, Vpad = 4136, 8300, 2, 8320
+    inp = tp_synth.xent_inputs(97 + h, N, h, Vreal, Vpad, "bf16", e_std=0.2)
+    say(f"[xent] two-part launch N={N} h={h} Vpad={Vpad} mask={mask}")
+    out = run_xent(inp, N, h, Vpad, Vreal, t, range(t), mask)
+    Vt = Vpad // t
+    for r in range(t):
+        check_bitexact_from_logits(out[r], r, Vt, Vreal, mask, inp["targets"])
+        st = oracle.xent_shard_stats(inp["X"], oracle.vocab_shard(inp["E"], t, r), inp["targets"], t, r, Vreal,
+                                     bool(mask))
+        for k in ("max", "sumexp", "tgt"):
+            e = rel_l2(host(out[r][k]), st[k])
+            assert e <= 1e-2, (r, k, e)
+    # the argmax lands in the 64x64 part for some tokens
+    am = out[0]["argmax"].cpu().numpy()
+    assert (am >= 3840).any() and (am < 3840).any()
+
+
 def test_xent_8p3b_workload_sampled():
     """The 8.3B vocabulary workload: N=8192, h=3072, Vpad=51200 (t=8, V_t=6400), Vreal=50257,
     all 8 ranks; the oracle takes 64 sampled tokens over the whole padded vocabulary."""
