@@ -13,9 +13,12 @@
 //     Nothing is transposed in HBM.
 //   * Out-of-range chunks (rows past the edge, k past the end of this split) are fetched at an
 //     offset past the buffer's end, which the buffer load returns as 0.
-//   * The next K tile is fetched into the other LDS stage at the start of a tile; fragments of
-//     k-step s+1 are read while the MFMAs of k-step s run (order pinned with
-//     sched_group_barrier); one barrier per K tile.
+//   * Per-lane global offsets are computed once per output tile; each K tile's fetch is then one
+//     load per 16-byte chunk with the K advance in the scalar offset (a ragged last K tile masks
+//     its chunks per lane).
+//   * The next K tile is fetched into the other LDS stage during the current one (at its start,
+//     or behind its first MFMAs, see gemm_tile); fragments of k-step s+1 are read while the
+//     MFMAs of k-step s run (order pinned with sched_group_barrier); one barrier per K tile.
 //   * Tiles are mapped XCD-aware: consecutive workgroups go round-robin to the 8 XCDs, so the
 //     block id is remapped to give each XCD a contiguous, grouped range of output tiles that
 //     share A and B panels in that XCD's L2.
@@ -64,7 +67,9 @@ typedef GemmCfg<64, 64, 2, 2, 4> Cfg64x64s4;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-constexpr int kOOB = 0x7fffffff;
+// Offset of a masked chunk: at or past the end of every buffer (launches keep operands below it)
+// and far enough below 2^32 that adding a scalar K offset (< 2^31) cannot wrap.
+constexpr int kOOB = 0x7f000000;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -88,16 +93,32 @@ template <int R, int NT> struct Operand<R, NT, KCONTIG> {
     static constexpr int IPW = BYTES / 1024 / (NT / 64);
     static_assert(IPW >= 1 && BYTES % (1024 * (NT / 64)) == 0, "tile/threads mismatch");
     int a[4];
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int ld, int mn0, int MN, int k0, int K, int tid,
-                                         char* lds) const {
-        const int wave = tid >> 6, lane = tid & 63;
+    int voff[IPW];   // byte offset of this lane's chunk at k0 = 0, or kOOB for rows past the edge
+    int ldsb;        // the wave's first kilobyte in a stage (wave-uniform)
+    // Once per tile: per-lane offsets, so each K tile's fetch is one DMA per kilobyte with the K
+    // advance in the scalar offset.
+    __device__ __forceinline__ void setup(int ld, int mn0, int MN, int tid) {
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+        ldsb = wave * IPW * 1024;
 #pragma unroll
         for (int j = 0; j < IPW; ++j) {
-            const int blk = wave * IPW + j;
-            const int c = blk * 64 + lane, row = c >> 3, p = c & 7;
-            const int kc = p ^ ((row ^ (row >> 3)) & 7);
-            const int mn = mn0 + row, k = k0 + kc * 8;
-            dma16(rs, (mn < MN && k < K) ? (mn * ld + k) * 2 : kOOB, lds + blk * 1024);
+            const int c = (wave * IPW + j) * 64 + lane, row = c >> 3;
+            const int kc = (c & 7) ^ ((row ^ (row >> 3)) & 7);
+            voff[j] = (mn0 + row < MN) ? ((mn0 + row) * ld + kc * 8) * 2 : kOOB;
+        }
+    }
+    // DMA the K tile at k0 (k < K valid; a ragged last tile masks its chunks per lane).
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int k0, int K, int tid, char* lds) const {
+        const bool full = k0 + 64 <= K;
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+            int vo = voff[j];
+            if (!full) {
+                const int c = ldsb / 16 + j * 64 + (tid & 63), row = c >> 3;
+                const int kc = (c & 7) ^ ((row ^ (row >> 3)) & 7);
+                vo = (k0 + kc * 8 < K) ? vo : kOOB;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + ldsb + j * 1024), 16, vo, k0 * 2, 0, 0);
         }
     }
     // row = first row of the wave's 32-row groups + lane % 32; the swizzle of row + 32i differs
@@ -125,14 +146,21 @@ template <int R, int NT> struct Operand<R, NT, MNCONTIG> {
     static_assert(USED <= NT, "thread mapping must cover the tile");
     Operand<R, NT, KCONTIG> kc;   // fragment addressing of the K-contiguous layout
     u32x4 v[KB];
-    __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, int ld, int mn0, int MN, int k0, int K, int tid) {
-        int mc = tid % MC, kg = tid / MC;
-        int mn = mn0 + mc * 8;
+    int voff;    // byte offset of this thread's first k-row at k0 = 0, or kOOB
+    int ldb;     // row pitch in bytes
+    __device__ __forceinline__ void setup(int ld, int mn0, int MN, int tid) {
+        const int mc = tid % MC, kg = tid / MC, mn = mn0 + mc * 8;
+        voff = (tid < USED && mn < MN) ? (kg * KB * ld + mn) * 2 : kOOB;
+        ldb = ld * 2;
+    }
+    // k-row k0 + kg*KB + j of the tile: the thread's offset plus a scalar (k0 + j) * ld * 2
+    __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, int k0, int K, int tid) {
+        const bool full = k0 + 64 <= K;
+        const int kg = tid / MC;
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
-            int k = k0 + kg * KB + j;
-            int off = (tid < USED && mn < MN && k < K) ? (k * ld + mn) * 2 : kOOB;
-            v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+            const int vo = (full || k0 + kg * KB + j < K) ? voff : kOOB;
+            v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (k0 + j) * ldb, 0);
         }
     }
     __device__ __forceinline__ void store(char* lds, int tid) const {
@@ -388,12 +416,19 @@ constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
 // Issue the loads of the K tile at k0: DMA operands go straight into LDS stage `stage`,
 // register-staged operands into their registers (written to LDS by store_stage()).
 template <class C, int LA, int LB>
+__device__ __forceinline__ void load_stage_dma(GemmState<C, LA, LB>& g, char* smem, int stage, int k0) {
+    if constexpr (decltype(g.oa)::DMA) g.oa.load(g.ra, k0, g.kend, g.tid, smem + stage * C::A_BYTES);
+    if constexpr (decltype(g.ob)::DMA) g.ob.load(g.rb, k0, g.kend, g.tid, smem + C::B_BASE + stage * C::B_BYTES);
+}
+template <class C, int LA, int LB>
+__device__ __forceinline__ void load_stage_reg(GemmState<C, LA, LB>& g, int k0) {
+    if constexpr (!decltype(g.oa)::DMA) g.oa.fetch(g.ra, k0, g.kend, g.tid);
+    if constexpr (!decltype(g.ob)::DMA) g.ob.fetch(g.rb, k0, g.kend, g.tid);
+}
+template <class C, int LA, int LB>
 __device__ __forceinline__ void load_stage(GemmState<C, LA, LB>& g, char* smem, int stage, int k0) {
-    if constexpr (decltype(g.oa)::DMA) g.oa.load(g.ra, g.lda, g.m0, g.M, k0, g.kend, g.tid, smem + stage * C::A_BYTES);
-    else g.oa.fetch(g.ra, g.lda, g.m0, g.M, k0, g.kend, g.tid);
-    if constexpr (decltype(g.ob)::DMA)
-        g.ob.load(g.rb, g.ldb, g.n0, g.N, k0, g.kend, g.tid, smem + C::B_BASE + stage * C::B_BYTES);
-    else g.ob.fetch(g.rb, g.ldb, g.n0, g.N, k0, g.kend, g.tid);
+    load_stage_dma(g, smem, stage, k0);
+    load_stage_reg(g, k0);
 }
 template <class C, int LA, int LB>
 __device__ __forceinline__ void store_stage(const GemmState<C, LA, LB>& g, char* smem, int stage) {
@@ -413,11 +448,23 @@ __device__ __forceinline__ void gemm_tile(GemmState<C, LA, LB>& g, char* smem, f
     constexpr bool REG = !decltype(g.oa)::DMA || !decltype(g.ob)::DMA;
     constexpr int NDW = (decltype(g.oa)::DMA ? 0 : 8) + (decltype(g.ob)::DMA ? 0 : 8);
     const bool more = kt + 1 < nk;
-    if (more) load_stage(g, smem, ST ^ 1, g.kbeg + (kt + 1) * C::BK);
+    // DMA of the next tile: issued behind the first MFMAs (which then start right after the
+    // barrier) when a register-staged operand is also in flight or the tile is 256x256; first
+    // thing in the tile otherwise (measured on MI355X: 256x192 and 128x128 tiles with both
+    // operands on DMA need the longer lead)
+    constexpr bool LATE = REG || (C::BM * C::BN >= 256 * 256);
+    if (more) load_stage_reg(g, g.kbeg + (kt + 1) * C::BK);
+    if constexpr (!LATE) {
+        if (more) load_stage_dma(g, smem, ST ^ 1, g.kbeg + (kt + 1) * C::BK);
+    }
     read_frags<C, LA, LB, ST>(g, smem, 1, g.a1, g.b1);
     mfma_step<C>(acc, g.a0, g.b0);
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (LATE) {
+        if (more) load_stage_dma(g, smem, ST ^ 1, g.kbeg + (kt + 1) * C::BK);
+    }
     __builtin_amdgcn_sched_barrier(0);
     read_frags<C, LA, LB, ST>(g, smem, 2, g.a0, g.b0);
     mfma_step<C>(acc, g.a1, g.b1);
@@ -454,11 +501,13 @@ __device__ __forceinline__ void gemm_tile_ms(GemmState<C, LA, LB>& g, char* smem
     static_assert(decltype(g.oa)::DMA && decltype(g.ob)::DMA, "multi-stage tiles need DMA operands");
     constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
     constexpr int PER_TILE = decltype(g.oa)::IPW + decltype(g.ob)::IPW;   // DMA instructions per wave per tile
-    load_stage(g, smem, (ST + C::NS - 1) % C::NS, g.kbeg + (kt + C::NS - 1) * C::BK);
     read_frags<C, LA, LB, ST>(g, smem, 1, g.a1, g.b1);
     mfma_step<C>(acc, g.a0, g.b0);
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // behind the first MFMAs: NS - 1 tiles of lead already cover the load latency
+    load_stage_dma(g, smem, (ST + C::NS - 1) % C::NS, g.kbeg + (kt + C::NS - 1) * C::BK);
     __builtin_amdgcn_sched_barrier(0);
     read_frags<C, LA, LB, ST>(g, smem, 2, g.a0, g.b0);
     mfma_step<C>(acc, g.a1, g.b1);
@@ -523,6 +572,8 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restr
     g.tid = tid;
     g.oa.init(wm * C::WM + (lane & 31), lane);
     g.ob.init(wn * C::WN + (lane & 31), lane);
+    g.oa.setup(lda, g.m0, M, tid);
+    g.ob.setup(ldb, g.n0, N, tid);
 
     f32x16 acc[C::TM][C::TN];
 #pragma unroll

@@ -17,7 +17,7 @@ static hipError_t launch_cfg(const GemmReq& r, int splits, const Epi& e, hipStre
     // bytes addressable through each operand (buffer loads beyond them return 0)
     size_t a_bytes = (size_t)(LA == KCONTIG ? r.M : r.K) * r.lda * 2;
     size_t b_bytes = (size_t)(LB == KCONTIG ? r.N : r.K) * r.ldb * 2;
-    if (a_bytes >= 0x7fff0000u || b_bytes >= 0x7fff0000u) return hipErrorInvalidValue;
+    if (a_bytes >= (size_t)kOOB || b_bytes >= (size_t)kOOB) return hipErrorInvalidValue;
     // vector epilogues move 8 columns at a time
     if (Epi::kVec8 && (r.N % 8 != 0 || r.ldc % 8 != 0)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_bf16_kernel<C, LA, LB, Epi>), dim3(tiles, splits), dim3(C::NT), 0, st,

@@ -185,7 +185,7 @@ static hipError_t launch8(const GemmReq& r, int splits, const Epi& e, hipStream_
     if (tiles == 0) return hipSuccess;
     const int kps = ((r.K + splits - 1) / splits + BK8 - 1) / BK8 * BK8;
     const size_t a_bytes = (size_t)r.M * r.lda, b_bytes = (size_t)r.N * r.ldb;
-    if (a_bytes >= 0x7fff0000u || b_bytes >= 0x7fff0000u) return hipErrorInvalidValue;
+    if (a_bytes >= (size_t)kOOB || b_bytes >= (size_t)kOOB) return hipErrorInvalidValue;
     if (Epi::kVec8 && (r.N % 8 != 0 || r.ldc % 8 != 0)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_fp8_kernel<C, Epi>), dim3(tiles, splits), dim3(C::NT), 0, st, (const uint8_t*)r.A, r.lda,
                        (const uint8_t*)r.B, r.ldb, r.descale_a, r.descale_b, r.M, r.N, r.K, kps, (uint32_t)a_bytes,
