@@ -201,6 +201,18 @@ __device__ __forceinline__ void map_tile(int bid, int nblocks, int tiles_m, int 
     tn = in / gsz;
 }
 
+// Split-K launches: block id -> (K split, output tile) over tiles x splits units in split-major
+// order, each XCD taking a contiguous range of units. An XCD then works on one K range of a
+// compact group of tiles, so the operand panels its L2 must hold are a third (for three splits)
+// of what a tile-major order spread over all XCDs needs.
+__device__ __forceinline__ void map_unit(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn,
+                                         int& split) {
+    if ((nblocks & 7) == 0) bid = (bid & 7) * (nblocks >> 3) + (bid >> 3);
+    const int tiles = tiles_m * tiles_n;
+    split = bid / tiles;
+    map_tile(bid - split * tiles, 1, tiles_m, tiles_n, tm, tn);   // nblocks = 1: no second remap
+}
+
 // ----------------------------------------------------------------------------------------------
 // Epilogues. Each exposes op8(row, col, v[8]) for 8 consecutive columns of one row (col % 8 == 0,
 // N and ld multiples of 8, checked at launch) and is applied through apply_staged(): a wave's
@@ -376,7 +388,7 @@ struct EpiPartial {
 };
 
 // ----------------------------------------------------------------------------------------------
-// bf16 MFMA kernel. gridDim.x = output tiles; gridDim.y = K splits (each covers k_per_split).
+// bf16 MFMA kernel. gridDim.x = output tiles x K splits (each split covers k_per_split), see map_unit.
 // LDS: [A stage 0 | A stage 1 | B stage 0 | B stage 1].
 // ----------------------------------------------------------------------------------------------
 template <class C, int LA, int LB>
@@ -557,9 +569,10 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restr
     const int wm = wave / C::WGN, wn = wave % C::WGN;
     const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
     int tm, tn;
-    map_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    int split;
+    map_unit(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn, split);
     Epi ep = epi;
-    ep.set_split(blockIdx.y);
+    ep.set_split(split);
 
     GemmState<C, LA, LB> g;
     g.ra = make_rsrc(A, a_bytes);
@@ -567,7 +580,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restr
     g.lda = lda; g.ldb = ldb;
     g.m0 = tm * C::BM; g.n0 = tn * C::BN;
     g.M = M; g.N = N;
-    g.kbeg = blockIdx.y * k_per_split;
+    g.kbeg = split * k_per_split;
     g.kend = min(K, g.kbeg + k_per_split);
     g.tid = tid;
     g.oa.init(wm * C::WM + (lane & 31), lane);

@@ -20,7 +20,7 @@ static hipError_t launch_cfg(const GemmReq& r, int splits, const Epi& e, hipStre
     if (a_bytes >= (size_t)kOOB || b_bytes >= (size_t)kOOB) return hipErrorInvalidValue;
     // vector epilogues move 8 columns at a time
     if (Epi::kVec8 && (r.N % 8 != 0 || r.ldc % 8 != 0)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_bf16_kernel<C, LA, LB, Epi>), dim3(tiles, splits), dim3(C::NT), 0, st,
+    hipLaunchKernelGGL((gemm_bf16_kernel<C, LA, LB, Epi>), dim3(tiles * splits), dim3(C::NT), 0, st,
                        (const bf16*)r.A, r.lda, (const bf16*)r.B, r.ldb, r.M, r.N, r.K, kps, (uint32_t)a_bytes,
                        (uint32_t)b_bytes, e);
     return hipGetLastError();

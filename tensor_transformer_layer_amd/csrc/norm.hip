@@ -173,6 +173,7 @@ hipError_t dropout_colsum(int dt, int rows, int n, const void* x, void* y, const
 hipError_t sum_partials(int in_dt, int out_dt, size_t rows, int cols, int t, const void* const* parts,
                         const void* bias, const void* residual, void* out, const DropParams& drop, hipStream_t st) {
     size_t n = rows * (size_t)cols;
+    if (t < 1 || t > SUM_MAX_T) return hipErrorInvalidValue;
     if (n == 0) return hipSuccess;
     PartPtrs pp;
     for (int r = 0; r < t; ++r) pp.p[r] = parts[r];
