@@ -155,8 +155,8 @@ def _oracle_step(oracle, p, xe, x, G, Wqkv_r, bq, Wo_r, A_r, b1_r, B_r, seqs, he
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="copy 512 MiB device-to-device once before the steps (calibrates HBM byte counters)")

@@ -109,16 +109,22 @@ template <int R, int NT> struct Operand<R, NT, KCONTIG> {
     }
     // DMA the K tile at k0 (k < K valid; a ragged last tile masks its chunks per lane).
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int k0, int K, int tid, char* lds) const {
-        const bool full = k0 + 64 <= K;
+        if (k0 + 64 <= K) {
 #pragma unroll
-        for (int j = 0; j < IPW; ++j) {
-            int vo = voff[j];
-            if (!full) {
+            for (int j = 0; j < IPW; ++j) {
+                const int vo = voff[j];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + ldsb + j * 1024), 16, vo, k0 * 2, 0,
+                                                         0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < IPW; ++j) {
                 const int c = ldsb / 16 + j * 64 + (tid & 63), row = c >> 3;
                 const int kc = (c & 7) ^ ((row ^ (row >> 3)) & 7);
-                vo = (k0 + kc * 8 < K) ? vo : kOOB;
+                const int vo = (k0 + kc * 8 < K) ? voff[j] : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + ldsb + j * 1024), 16, vo, k0 * 2, 0,
+                                                         0);
             }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + ldsb + j * 1024), 16, vo, k0 * 2, 0, 0);
         }
     }
     // row = first row of the wave's 32-row groups + lane % 32; the swizzle of row + 32i differs
@@ -465,6 +471,11 @@ __device__ __forceinline__ void gemm_tile(GemmState<C, LA, LB>& g, char* smem, f
     // thing in the tile otherwise (measured on MI355X: 256x192 and 128x128 tiles with both
     // operands on DMA need the longer lead)
     constexpr bool LATE = REG || (C::BM * C::BN >= 256 * 256);
+    // Barrier before the last k-step (see the end of the tile): not for the 256x256 tiles with two
+    // register-staged operands (the extra live fragments spill) nor for the 256x192 and 128x128
+    // tiles fed only by DMA (measured slower).
+    constexpr bool BOTH_REG = !decltype(g.oa)::DMA && !decltype(g.ob)::DMA;
+    constexpr bool EARLY_BARRIER = REG ? !(BOTH_REG && C::BM * C::BN >= 256 * 256) : C::BM * C::BN >= 256 * 256;
     if (more) load_stage_reg(g, g.kbeg + (kt + 1) * C::BK);
     if constexpr (!LATE) {
         if (more) load_stage_dma(g, smem, ST ^ 1, g.kbeg + (kt + 1) * C::BK);
@@ -496,11 +507,26 @@ __device__ __forceinline__ void gemm_tile(GemmState<C, LA, LB>& g, char* smem, f
         __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    mfma_step<C>(acc, g.a1, g.b1);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA into the next stage has landed
-    __syncthreads();
-    if (more) read_frags<C, LA, LB, ST ^ 1>(g, smem, 0, g.a0, g.b0);
+    if constexpr (EARLY_BARRIER) {
+        // The barrier comes before k-step 3's MFMAs, whose fragments are already in registers:
+        // the next tile's first fragments then load under those MFMAs instead of after an idle
+        // barrier. Before it, this wave's reads of this stage and its writes (DMA, register-staged
+        // stores) of the next stage have completed; no memory fence beyond that.
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags<C, LA, LB, ST ^ 1>(g, smem, 0, g.a0, g.b0);   // unused past the last tile
+        mfma_step<C>(acc, g.a1, g.b1);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    } else {
+        mfma_step<C>(acc, g.a1, g.b1);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA into the next stage has landed
+        __syncthreads();
+        if (more) read_frags<C, LA, LB, ST ^ 1>(g, smem, 0, g.a0, g.b0);
+    }
 }
 
 // NS > 2 (both operands DMA): the tile in stage ST fetches tile kt + NS - 1 into stage
@@ -531,12 +557,16 @@ __device__ __forceinline__ void gemm_tile_ms(GemmState<C, LA, LB>& g, char* smem
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_step<C>(acc, g.a1, g.b1);
+    // as in gemm_tile: barrier before k-step 3's MFMAs, once this wave's DMA of tile kt + 1 has
+    // landed (tiles kt + 2 .. kt + NS - 1 stay in flight: no fence)
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((C::NS - 2) * PER_TILE) : "memory");
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // this wave's DMA of tile kt + 1 has landed (tiles kt + 2 .. kt + NS - 1 may still be in flight)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((C::NS - 2) * PER_TILE) : "memory");
-    __syncthreads();
-    if (kt + 1 < nk) read_frags<C, LA, LB, (ST + 1) % C::NS>(g, smem, 0, g.a0, g.b0);
+    read_frags<C, LA, LB, (ST + 1) % C::NS>(g, smem, 0, g.a0, g.b0);   // unused past the last tile
+    mfma_step<C>(acc, g.a1, g.b1);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, NM, 0);
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // NS consecutive tiles, stages 0 .. NS-1.
@@ -616,7 +646,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restr
 #pragma unroll
         for (int s = 0; s < C::NS - 1; ++s) load_stage(g, smem, s, g.kbeg + s * C::BK);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((C::NS - 2) * PER_TILE) : "memory");
-        __syncthreads();
+        __builtin_amdgcn_s_barrier();
         read_frags<C, LA, LB, 0>(g, smem, 0, g.a0, g.b0);
         int kt = 0;
         for (; kt + C::NS <= nk; kt += C::NS) gemm_tiles_ms_round<C, LA, LB, 0>(g, smem, acc, kt, nk);
