@@ -19,6 +19,10 @@ template <> struct Raw8<bf16> {
     u32x4 v;
     __device__ __forceinline__ void load(const bf16* p) { v = *(const u32x4*)p; }
     __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
+    // the eight values rounded to bf16 (as store8 writes them)
+    __device__ __forceinline__ void set(const float (&a)[8]) {
+        v = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])};
+    }
     __device__ __forceinline__ float operator[](int e) const {
         uint32_t w = v[e >> 1];
         return __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -28,6 +32,10 @@ template <> struct Raw8<float> {
     f32x4 a, b;
     __device__ __forceinline__ void load(const float* p) { a = *(const f32x4*)p; b = *(const f32x4*)(p + 4); }
     __device__ __forceinline__ void zero() { a = f32x4{0.f, 0.f, 0.f, 0.f}; b = a; }
+    __device__ __forceinline__ void set(const float (&x)[8]) {
+        a = f32x4{x[0], x[1], x[2], x[3]};
+        b = f32x4{x[4], x[5], x[6], x[7]};
+    }
     __device__ __forceinline__ float operator[](int e) const { return e < 4 ? a[e] : b[e - 4]; }
 };
 
@@ -50,7 +58,8 @@ __device__ __forceinline__ void block_sum(float (&v)[NV], float (*red)[NV], int 
 }
 
 // ---------------------------------------------------------------------------------------------
-// LayerNorm forward: one wave per row, the row held in registers (C chunks of 8 per lane).
+// LayerNorm forward: one wave per row, the row held in registers (C chunks of 8 per lane) in its
+// storage type (bf16 rows take half the registers of fp32 copies: more waves resident).
 // ---------------------------------------------------------------------------------------------
 template <typename T, int C>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int h, float eps, const T* __restrict__ x,
@@ -61,17 +70,18 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int h, float eps,
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const T* xr = x + (size_t)row * h;
-    float v[C][8];
+    Raw8<T> v[C];
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < C; ++k) {
         int c = (lane + 64 * k) * 8;
-        if (c < h) {
-            load8(xr + c, v[k]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s += v[k][e];
-        }
+        if (c < h) v[k].load(xr + c);
+        else v[k].zero();
     }
+#pragma unroll
+    for (int k = 0; k < C; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += v[k][e];
     const float mu = wave_sum(s) / (float)h;
     float q = 0.f;
 #pragma unroll
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(256) void add_ln_fwd_kernel(int rows, int h, int t,
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const size_t ro = (size_t)row * h;
-    float v[C][8];
+    Raw8<T> v[C];
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < C; ++k) {
@@ -150,11 +160,9 @@ __global__ __launch_bounds__(256) void add_ln_fwd_kernel(int rows, int h, int t,
                 for (int e = 0; e < 8; ++e) a[e] += b[e];
             }
             store8(out + ro + c, a);
+            v[k].set(a);   // the stored (rounded) values
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                v[k][e] = to_f32(from_f32<T>(a[e]));   // the stored value
-                s += v[k][e];
-            }
+            for (int e = 0; e < 8; ++e) s += v[k][e];
         }
     }
     const float mu = wave_sum(s) / (float)h;
