@@ -7,7 +7,7 @@ C entry point in ``include/tp_shard.h``. Tensor arguments may be torch tensors (
 torch's current HIP stream. A non-zero status raises ``TPError`` with ``tp_last_error()``.
 Every computation happens in the library's HIP kernels; there is no fallback path. Importing
 this package fails if the library has not been built
-(``python -m tensor_transformer_layer_amd.build``).
+(``python tensor_transformer_layer_amd/build.py``).
 """
 import ctypes as C
 import os
@@ -48,7 +48,7 @@ class TPError(RuntimeError):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with 'python -m tensor_transformer_layer_amd.build'")
+    raise ImportError(f"{LIB_PATH} is missing: build it with 'python tensor_transformer_layer_amd/build.py'")
 lib = C.CDLL(LIB_PATH)
 
 _i, _z, _p, _f = C.c_int, C.c_size_t, C.c_void_p, C.c_float

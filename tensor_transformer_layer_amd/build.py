@@ -1,6 +1,6 @@
 """Build libtpshard.so for gfx950 with hipcc (in-tree, no JIT cache).
 
-    python -m tensor_transformer_layer_amd.build
+    python tensor_transformer_layer_amd/build.py   (run as a script: importing the package needs the library)
 
 Objects go to tensor_transformer_layer_amd/_build/, the library to
 tensor_transformer_layer_amd/libtpshard.so. Every HIP source is compiled with the packed-fp32
