@@ -182,7 +182,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
-              "(the multi-GPU all-reduces are not part of this build)", file=sys.stderr)
+              "(the library computes one rank's share; the multi-GPU all-reduces are not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -50,7 +50,7 @@ typedef enum tp_status {
     TP_ERR_DTYPE = 3,       /* unknown dtype */
     TP_ERR_WORKSPACE = 4,   /* ws_bytes smaller than the *_workspace query returns */
     TP_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
-    TP_ERR_UNSUPPORTED = 6  /* valid request this build does not implement (e.g. fp32 attention) */
+    TP_ERR_UNSUPPORTED = 6  /* valid request the library does not implement (e.g. fp32 attention) */
 } tp_status;
 
 typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
