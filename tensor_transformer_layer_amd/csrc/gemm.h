@@ -61,6 +61,9 @@ typedef GemmCfg<128, 128, 2, 2> Cfg128x128;
 // 64x64 with 4 waves of 32x32 and four LDS stages (32 KB each side: two workgroups per CU): for
 // the thin remainder of a large GEMM, where few MFMAs per k-step leave the loads exposed
 typedef GemmCfg<64, 64, 2, 2, 4> Cfg64x64s4;
+// 128x128 with three stages (96 KB: one workgroup per CU) for GEMMs with about one such tile per
+// CU, where a single workgroup must hide the loads itself
+typedef GemmCfg<128, 128, 2, 2, 3> Cfg128x128s3;
 
 // Buffer resource over [base, base + bytes): loads at offsets >= bytes return 0, which is how
 // masked chunks are zero-filled without a branch.

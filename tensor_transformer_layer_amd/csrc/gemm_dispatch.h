@@ -32,9 +32,13 @@ static hipError_t launch_plan(const GemmReq& r, const GemmPlan& p, const Epi& e,
         case 0: return launch_cfg<Cfg256x256, LA, LB>(r, p.splits, e, st);
         case 1: return launch_cfg<Cfg128x128, LA, LB>(r, p.splits, e, st);
         case 2: return launch_cfg<Cfg256x192, LA, LB>(r, p.splits, e, st);
+        // multi-stage shapes need both operands on DMA; other layouts take the two-stage 128x128
         case 3:
             if constexpr (LA == KCONTIG && LB == KCONTIG) return launch_cfg<Cfg64x64s4, LA, LB>(r, p.splits, e, st);
-            break;
+            else return launch_cfg<Cfg128x128, LA, LB>(r, p.splits, e, st);
+        case 4:
+            if constexpr (LA == KCONTIG && LB == KCONTIG) return launch_cfg<Cfg128x128s3, LA, LB>(r, p.splits, e, st);
+            else return launch_cfg<Cfg128x128, LA, LB>(r, p.splits, e, st);
     }
     return hipErrorInvalidValue;
 }

@@ -4,9 +4,11 @@
 
 namespace tp {
 
-static const int kNCfg = 3;
-static const int kBM[kNCfg] = {256, 128, 256};
-static const int kBN[kNCfg] = {256, 128, 192};
+static const int kNCfg = 3;   // configurations the time model chooses among
+// tile shape of every configuration (3: 64x64 four-stage, 4: 128x128 three-stage; both need
+// K-contiguous operands and are picked only by plans below)
+static const int kBM[5] = {256, 128, 256, 64, 128};
+static const int kBN[5] = {256, 128, 192, 64, 128};
 // relative per-tile MFMA efficiency, measured on MI355X at the layer's shapes (K = 1536..3072)
 static const double kEff[kNCfg] = {1.0, 0.93, 0.95};
 // workgroups of each configuration resident per CU
@@ -22,7 +24,7 @@ static const TunedPlan kTuned[] = {
     {8192, 3072, 1536, 0, 2, 1},   // MLP GEMM2 fwd, dX
     {8192, 1152, 3072, 0, 2, 1},   // QKV fwd
     {8192, 3072, 384, 0, 2, 1},    // output projection fwd
-    {8192, 384, 3072, 0, 1, 1},    // dO
+    {8192, 384, 3072, 0, 4, 1},    // dO (192 tiles: one three-stage workgroup per CU)
     {8192, 3072, 1152, 0, 2, 1},   // dXn
     {6400, 8192, 3072, 0, 1, 1},   // vocabulary logits (stored, and their gradient)
     {1536, 3072, 8192, 1, 0, 3},   // dB

@@ -38,7 +38,8 @@ struct GemmReq {
 
 struct GemmPlan {
     int cfg;      // 0: 256x256 (8 waves), 1: 128x128 (4 waves), 2: 256x192 (8 waves),
-                  // 3: 64x64 (4 waves, 4 LDS stages; both operands K-contiguous only)
+                  // 3: 64x64 (4 waves, 4 LDS stages), 4: 128x128 (4 waves, 3 LDS stages); 3 and 4
+                  // with both operands K-contiguous (otherwise the two-stage 128x128 runs)
     int splits;   // K splits (>1 only when the request allows it)
     int bm, bn;
 };
