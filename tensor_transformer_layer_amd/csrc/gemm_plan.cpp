@@ -30,7 +30,7 @@ static const TunedPlan kTuned[] = {
     {1536, 3072, 8192, 1, 0, 3},   // dB
     {3072, 1536, 8192, 1, 0, 3},   // dA
     {384, 3072, 8192, 1, 1, 6},    // dWo
-    {3072, 1152, 8192, 1, 2, 3},   // dWqkv
+    {3072, 1152, 8192, 1, 0, 4},   // dWqkv (240 units of 256x256)
 };
 
 // Time model over the three tile shapes and split counts: rounds of resident tiles x per-tile
