@@ -31,9 +31,17 @@ __global__ __launch_bounds__(256) void xent_merge_kernel(const XentPartial* __re
     XentAcc a;
     a.init();
     if (n < N) {
-        for (int tm = ph; tm < tiles_m; tm += 4) {
-            XentPartial p = part[(size_t)tm * N + n];
-            a.add(p.mx, p.se, p.tv, p.am);
+        // up to eight of the phase's partials in flight at once, then merged in tile order
+        for (int t0 = ph; t0 < tiles_m; t0 += 32) {
+            XentPartial q[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int tm = t0 + 4 * j;
+                q[j] = tm < tiles_m ? part[(size_t)tm * N + n] : XentPartial{-INFINITY, 0.f, 0.f, INT_MAX};
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (t0 + 4 * j < tiles_m) a.add(q[j].mx, q[j].se, q[j].tv, q[j].am);
         }
     }
     red[ph][tl] = XentPartial{a.mx, a.se, a.tv, a.am};
