@@ -11,8 +11,15 @@
  * is the caller's job; tp_sum_partials does it on one device.
  *
  * Conventions shared by every call
- *  - All tensor pointers are DEVICE pointers owned by the caller. The library never allocates,
- *    frees or synchronises; it launches only on the stream it is given (0 = null stream).
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library never allocates
+ *    device memory, frees or synchronises with the host. It launches on the stream it is given
+ *    (0 = null stream), except that tp_mlp_shard_bwd and tp_attn_shard_bwd also run part of their
+ *    work (column sums, split-K reductions, the dWo GEMM) on a second stream of the device's own,
+ *    forked from the given stream by an event and joined back into it before they return: the
+ *    given stream sees all of the call's work in order, and HIP graph capture records the fork
+ *    and join. That stream and its events are created on the device's first such call, which
+ *    therefore must not happen inside a graph capture; calls that use them are serialised on
+ *    the host by a lock.
  *  - Row-major, contiguous, 16-byte aligned. Tokens are rows: token = batch*s + position.
  *  - dt selects the element type of activations, weights, saved tensors and partials
  *    (TP_BF16: bfloat16 in, fp32 accumulate, bfloat16 out; TP_F32: fp32 throughout).

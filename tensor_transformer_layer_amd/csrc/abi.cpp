@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -41,6 +42,46 @@ tp_status ok() {
     } while (0)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// A second stream per device for work that can run beside the caller's stream inside one call
+// (column sums, split-K reductions and a weight-gradient GEMM next to GEMMs that leave CUs idle).
+// Default priority. Work goes to it after an event recorded on the caller's stream (fork), and the
+// caller's stream waits for an event recorded after the last of it (join) before the call
+// returns, so every entry point keeps single-stream semantics; both steps are an event record and
+// a stream wait, which HIP graph capture records as a fork and a join. The stream and its events
+// are created on a device's first such call (not during a graph capture: run the step once first).
+// Calls that use them are serialised on the host by a mutex (the events are reused).
+constexpr int kMaxDevices = 64;
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+hipError_t side_stream(SideStream*& out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    SideStream& sd = g_side[dev];
+    if (!sd.s) {
+        if ((e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking)) != hipSuccess) return e;
+        for (hipEvent_t& ev : sd.ev)
+            // device-scope fences only: both streams run on this device (a system-scope fence,
+            // the default, costs a cache writeback at every fork and join)
+            if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence)) != hipSuccess)
+                return e;
+    }
+    out = &sd;
+    return hipSuccess;
+}
+
+// `to` waits for the work issued on `from` so far (event slot i)
+hipError_t stream_after(const SideStream& sd, int i, hipStream_t from, hipStream_t to) {
+    hipError_t e = hipEventRecord(sd.ev[i], from);
+    return e != hipSuccess ? e : hipStreamWaitEvent(to, sd.ev[i], 0);
+}
 
 // required pointer: non-null and 16-byte aligned
 #define NEED(p)                                                                                      \
@@ -126,20 +167,24 @@ size_t wgrad_split_ws(tp_dtype dt, int M, int N, int K) {
 
 size_t colsum_ws(int T, int n) { return (size_t)colsum_row_blocks(T) * n * sizeof(float); }
 
+// dU | dB split partials | dA split partials | db1 column-sum partials (separate: the three can
+// be in use at once on the two streams)
 struct MlpWs {
-    size_t dU, scratch, total;
+    size_t dU, partB, partA, col, total;
 };
 MlpWs mlp_ws(int T, int h, int Ft, tp_dtype dt) {
     MlpWs w;
     w.dU = al256((size_t)T * Ft * esize(dt));
-    size_t s = std::max(wgrad_split_ws(dt, Ft, h, T), wgrad_split_ws(dt, h, Ft, T));
-    w.scratch = al256(std::max(s, colsum_ws(T, Ft)));
-    w.total = w.dU + w.scratch;
+    w.partB = al256(wgrad_split_ws(dt, Ft, h, T));
+    w.partA = al256(wgrad_split_ws(dt, h, Ft, T));
+    w.col = al256(colsum_ws(T, Ft));
+    w.total = w.dU + w.partB + w.partA + w.col;
     return w;
 }
 
+// dO | D | dQKV | dWo split partials | dWqkv split partials | dbqkv column-sum partials
 struct AttnWs {
-    size_t dO, D, dQKV, scratch, total;
+    size_t dO, D, dQKV, partWo, partWqkv, col, total;
 };
 AttnWs attn_ws(int b, int s, int h, int heads_t, int h_t) {
     long T = (long)b * s;
@@ -147,9 +192,10 @@ AttnWs attn_ws(int b, int s, int h, int heads_t, int h_t) {
     w.dO = al256((size_t)T * h_t * 2);
     w.D = al256((size_t)b * heads_t * s * sizeof(float));
     w.dQKV = al256((size_t)T * 3 * h_t * 2);
-    size_t sp = std::max(wgrad_split_ws(TP_BF16, h_t, h, (int)T), wgrad_split_ws(TP_BF16, h, 3 * h_t, (int)T));
-    w.scratch = al256(std::max(sp, colsum_ws((int)T, 3 * h_t)));
-    w.total = w.dO + w.D + w.dQKV + w.scratch;
+    w.partWo = al256(wgrad_split_ws(TP_BF16, h_t, h, (int)T));
+    w.partWqkv = al256(wgrad_split_ws(TP_BF16, h, 3 * h_t, (int)T));
+    w.col = al256(colsum_ws((int)T, 3 * h_t));
+    w.total = w.dO + w.D + w.dQKV + w.partWo + w.partWqkv + w.col;
     return w;
 }
 
@@ -241,23 +287,36 @@ tp_status tp_mlp_shard_bwd(int T, int h, int ffn, int t, int r, tp_dtype dt, con
     if (w.total > 0) NEED(ws);
     char* base = (char*)ws;
     void* dU = base;
-    void* scratch = base + w.dU;
+    void* partB = base + w.dU;
+    void* partA = base + w.dU + w.partB;
+    float* colp = (float*)(base + w.dU + w.partB + w.partA);
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* sd = nullptr;
+    HIP_TRY(side_stream(sd), "tp_mlp_shard_bwd: side stream");
     // dU = (G B_r^T) * GeLU'(U_r)
     GemmReq g = req(T, Ft, h, G, h, 0, B_r, h, 0, EPI_DGELU, dU, Ft);
     g.aux = U_r;
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_mlp_shard_bwd: dU GEMM");
-    // dB_r = Y_r^T G
+    // side: db1 = column sums of dU, beside the dB GEMM (whose 216 tiles leave CUs free)
+    HIP_TRY(stream_after(*sd, 0, stream, sd->s), "tp_mlp_shard_bwd: fork");
+    if (db1_r) HIP_TRY(colsum(dt == TP_BF16, T, Ft, dU, db1_r, accumulate, colp, sd->s), "tp_mlp_shard_bwd: db1");
+    // dB_r = Y_r^T G; its split-K reduction on the side stream, beside the dA GEMM
     g = req(Ft, h, T, Y_r, Ft, 1, G, h, 1, EPI_STORE, dB_r, h);
     g.accumulate = accumulate;
-    HIP_TRY(run_gemm(dt, g, true, scratch, stream), "tp_mlp_shard_bwd: dB GEMM");
+    g.defer_reduce = 1;
+    HIP_TRY(run_gemm(dt, g, true, partB, stream), "tp_mlp_shard_bwd: dB GEMM");
+    if (dt == TP_BF16) {
+        HIP_TRY(stream_after(*sd, 1, stream, sd->s), "tp_mlp_shard_bwd: fork");
+        HIP_TRY(gemm_splitk_reduce(g, plan_gemm_bf16(g.M, g.N, g.K, true), partB, sd->s), "tp_mlp_shard_bwd: dB reduction");
+    }
     // dA_r = X^T dU
     g = req(h, Ft, T, X, h, 1, dU, Ft, 1, EPI_STORE, dA_r, Ft);
     g.accumulate = accumulate;
-    HIP_TRY(run_gemm(dt, g, true, scratch, stream), "tp_mlp_shard_bwd: dA GEMM");
-    if (db1_r) HIP_TRY(colsum(dt == TP_BF16, T, Ft, dU, db1_r, accumulate, (float*)scratch, stream), "tp_mlp_shard_bwd: db1");
+    HIP_TRY(run_gemm(dt, g, true, partA, stream), "tp_mlp_shard_bwd: dA GEMM");
     // dX_r = dU A_r^T
     g = req(T, h, Ft, dU, Ft, 0, A_r, Ft, 0, EPI_STORE, dX_r, h);
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_mlp_shard_bwd: dX GEMM");
+    HIP_TRY(stream_after(*sd, 2, sd->s, stream), "tp_mlp_shard_bwd: join");
     return ok();
 }
 
@@ -317,26 +376,35 @@ tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dty
     void* dO = base;
     float* Dv = (float*)(base + w.dO);
     void* dQKV = base + w.dO + w.D;
-    void* scratch = base + w.dO + w.D + w.dQKV;
+    void* partWo = base + w.dO + w.D + w.dQKV;
+    void* partWqkv = base + w.dO + w.D + w.dQKV + w.partWo;
+    float* colp = (float*)(base + w.dO + w.D + w.dQKV + w.partWo + w.partWqkv);
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* sd = nullptr;
+    HIP_TRY(side_stream(sd), "tp_attn_shard_bwd: side stream");
+    // side: dWo_r = O_r^T G (needs neither dO nor the attention backward), beside the dO GEMM
+    // (whose 192 one-per-CU tiles leave room) and the attention kernels
+    HIP_TRY(stream_after(*sd, 0, stream, sd->s), "tp_attn_shard_bwd: fork");
     // dO = G Wo_r^T
     GemmReq g = req(T, h_t, h, G, h, 0, Wo_r, h, 0, EPI_STORE, dO, h_t);
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_bwd: dO GEMM");
-    // dWo_r = O_r^T G
     g = req(h_t, h, T, O_r, h_t, 1, G, h, 1, EPI_STORE, dWo_r, h);
     g.accumulate = accumulate;
-    HIP_TRY(run_gemm(dt, g, true, scratch, stream), "tp_attn_shard_bwd: dWo GEMM");
+    HIP_TRY(run_gemm(dt, g, true, partWo, sd->s), "tp_attn_shard_bwd: dWo GEMM");
     if (T > 0)
         HIP_TRY(attn_bwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, dO, Dv, dQKV, dp, stream),
                 "tp_attn_shard_bwd: attention backward");
+    // side: dbqkv = column sums of dQKV, beside the dWqkv GEMM
+    HIP_TRY(stream_after(*sd, 1, stream, sd->s), "tp_attn_shard_bwd: fork");
+    if (dbqkv_r) HIP_TRY(colsum(1, T, 3 * h_t, dQKV, dbqkv_r, accumulate, colp, sd->s), "tp_attn_shard_bwd: dbqkv");
     // dWqkv_r = Xn^T dQKV
     g = req(h, 3 * h_t, T, Xn, h, 1, dQKV, 3 * h_t, 1, EPI_STORE, dWqkv_r, 3 * h_t);
     g.accumulate = accumulate;
-    HIP_TRY(run_gemm(dt, g, true, scratch, stream), "tp_attn_shard_bwd: dWqkv GEMM");
-    if (dbqkv_r)
-        HIP_TRY(colsum(1, T, 3 * h_t, dQKV, dbqkv_r, accumulate, (float*)scratch, stream), "tp_attn_shard_bwd: dbqkv");
+    HIP_TRY(run_gemm(dt, g, true, partWqkv, stream), "tp_attn_shard_bwd: dWqkv GEMM");
     // dXn_r = dQKV Wqkv_r^T
     g = req(T, h, 3 * h_t, dQKV, 3 * h_t, 0, Wqkv_r, 3 * h_t, 0, EPI_STORE, dXn_r, h);
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_bwd: dXn GEMM");
+    HIP_TRY(stream_after(*sd, 2, sd->s, stream), "tp_attn_shard_bwd: join");
     return ok();
 }
 

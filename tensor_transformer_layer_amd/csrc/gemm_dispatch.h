@@ -9,6 +9,16 @@ namespace tp {
 
 static inline int cdiv_h(long a, long b) { return (int)((a + b - 1) / b); }
 
+// out = sum of the split partials in ws, in split order, through the plain bf16 store epilogue
+static inline hipError_t launch_splitk_reduce(const GemmReq& r, const GemmPlan& p, const void* ws, hipStream_t st) {
+    EpiStore<bf16> fin{(bf16*)r.out, r.ldc, (const bf16*)r.bias, r.accumulate};
+    size_t n = (size_t)r.M * r.N;
+    if (n == 0 || p.splits <= 1) return hipSuccess;
+    hipLaunchKernelGGL((splitk_reduce_kernel<EpiStore<bf16>>), dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, st,
+                       (const float*)ws, p.splits, n, r.M, r.N, fin);
+    return hipGetLastError();
+}
+
 template <class C, int LA, int LB, class Epi>
 static hipError_t launch_cfg(const GemmReq& r, int splits, const Epi& e, hipStream_t st) {
     int tiles = cdiv_h(r.M, C::BM) * cdiv_h(r.N, C::BN);
@@ -51,12 +61,8 @@ static hipError_t gemm_run(const GemmReq& r, const GemmPlan& p, void* ws, hipStr
             if (r.epi != EPI_STORE || ws == nullptr) return hipErrorInvalidValue;
             EpiPartial e{(float*)ws, r.N, (size_t)r.M * r.N, 0};
             hipError_t err = launch_plan<LA, LB>(r, p, e, st);
-            if (err != hipSuccess) return err;
-            EpiStore<bf16> fin{(bf16*)r.out, r.ldc, (const bf16*)r.bias, r.accumulate};
-            size_t n = (size_t)r.M * r.N;
-            hipLaunchKernelGGL((splitk_reduce_kernel<EpiStore<bf16>>), dim3((unsigned)((n / 8 + 255) / 256)),
-                               dim3(256), 0, st, (const float*)ws, p.splits, n, r.M, r.N, fin);
-            return hipGetLastError();
+            if (err != hipSuccess || r.defer_reduce) return err;
+            return launch_splitk_reduce(r, p, ws, st);
         }
         return hipErrorInvalidValue;
     }
