@@ -17,9 +17,9 @@
  *    work (column sums, split-K reductions, the dWo GEMM) on a second stream of the device's own,
  *    forked from the given stream by an event and joined back into it before they return: the
  *    given stream sees all of the call's work in order, and HIP graph capture records the fork
- *    and join. That stream and its events are created on the device's first such call, which
- *    therefore must not happen inside a graph capture; calls that use them are serialised on
- *    the host by a lock.
+ *    and join. That stream and its events are created on the device's first such call; a first
+ *    call made while the given stream is being captured creates nothing and runs all of its work
+ *    on the given stream. Calls that use them are serialised on the host by a lock.
  *  - Row-major, contiguous, 16-byte aligned. Tokens are rows: token = batch*s + position.
  *  - dt selects the element type of activations, weights, saved tensors and partials
  *    (TP_BF16: bfloat16 in, fp32 accumulate, bfloat16 out; TP_F32: fp32 throughout).

@@ -49,23 +49,33 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // caller's stream waits for an event recorded after the last of it (join) before the call
 // returns, so every entry point keeps single-stream semantics; both steps are an event record and
 // a stream wait, which HIP graph capture records as a fork and a join. The stream and its events
-// are created on a device's first such call (not during a graph capture: run the step once first).
+// are created on a device's first such call; if that call comes while the caller's stream is
+// being captured, nothing is created and the call runs all of its work on the caller's stream.
 // Calls that use them are serialised on the host by a mutex (the events are reused).
 constexpr int kMaxDevices = 64;
 struct SideStream {
     hipStream_t s = nullptr;
-    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
 };
 std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
 
-hipError_t side_stream(SideStream*& out) {
+// The current device's side stream, created on first use; nullptr while `caller` is capturing and
+// none exists yet.
+hipError_t side_stream(hipStream_t caller, SideStream*& out) {
+    out = nullptr;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     SideStream& sd = g_side[dev];
     if (!sd.s) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(caller, &cs) != hipSuccess) {
+            (void)hipGetLastError();   // a query refused during a capture: create nothing now
+            return hipSuccess;
+        }
+        if (cs != hipStreamCaptureStatusNone) return hipSuccess;
         if ((e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking)) != hipSuccess) return e;
         for (hipEvent_t& ev : sd.ev)
             // device-scope fences only: both streams run on this device (a system-scope fence,
@@ -77,11 +87,38 @@ hipError_t side_stream(SideStream*& out) {
     return hipSuccess;
 }
 
-// `to` waits for the work issued on `from` so far (event slot i)
-hipError_t stream_after(const SideStream& sd, int i, hipStream_t from, hipStream_t to) {
-    hipError_t e = hipEventRecord(sd.ev[i], from);
-    return e != hipSuccess ? e : hipStreamWaitEvent(to, sd.ev[i], 0);
-}
+// Fork/join of the side stream within one call. side() is where side work goes: the side stream
+// once forked, else the caller's stream. A call that returns early after a fork (an error) still
+// joins, so a graph capture is never left with an unjoined branch.
+class SideFork {
+  public:
+    SideFork(SideStream* sd, hipStream_t caller) : sd_(sd), caller_(caller) {}
+    SideFork(const SideFork&) = delete;
+    SideFork& operator=(const SideFork&) = delete;
+    ~SideFork() { (void)join(); }
+    hipStream_t side() const { return sd_ ? sd_->s : caller_; }
+    // the side stream waits for the caller's work so far (event slot 0 or 1)
+    hipError_t fork(int slot) {
+        if (!sd_) return hipSuccess;
+        forked_ = true;
+        return after(slot, caller_, sd_->s);
+    }
+    // the caller's stream waits for all side work
+    hipError_t join() {
+        if (!forked_) return hipSuccess;
+        forked_ = false;
+        return after(2, sd_->s, caller_);
+    }
+
+  private:
+    hipError_t after(int slot, hipStream_t from, hipStream_t to) {
+        hipError_t e = hipEventRecord(sd_->ev[slot], from);
+        return e != hipSuccess ? e : hipStreamWaitEvent(to, sd_->ev[slot], 0);
+    }
+    SideStream* sd_;
+    hipStream_t caller_;
+    bool forked_ = false;
+};
 
 // required pointer: non-null and 16-byte aligned
 #define NEED(p)                                                                                      \
@@ -292,22 +329,24 @@ tp_status tp_mlp_shard_bwd(int T, int h, int ffn, int t, int r, tp_dtype dt, con
     float* colp = (float*)(base + w.dU + w.partB + w.partA);
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideStream* sd = nullptr;
-    HIP_TRY(side_stream(sd), "tp_mlp_shard_bwd: side stream");
+    HIP_TRY(side_stream(stream, sd), "tp_mlp_shard_bwd: side stream");
+    SideFork side(sd, stream);
     // dU = (G B_r^T) * GeLU'(U_r)
     GemmReq g = req(T, Ft, h, G, h, 0, B_r, h, 0, EPI_DGELU, dU, Ft);
     g.aux = U_r;
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_mlp_shard_bwd: dU GEMM");
     // side: db1 = column sums of dU, beside the dB GEMM (whose 216 tiles leave CUs free)
-    HIP_TRY(stream_after(*sd, 0, stream, sd->s), "tp_mlp_shard_bwd: fork");
-    if (db1_r) HIP_TRY(colsum(dt == TP_BF16, T, Ft, dU, db1_r, accumulate, colp, sd->s), "tp_mlp_shard_bwd: db1");
+    HIP_TRY(side.fork(0), "tp_mlp_shard_bwd: fork");
+    if (db1_r) HIP_TRY(colsum(dt == TP_BF16, T, Ft, dU, db1_r, accumulate, colp, side.side()), "tp_mlp_shard_bwd: db1");
     // dB_r = Y_r^T G; its split-K reduction on the side stream, beside the dA GEMM
     g = req(Ft, h, T, Y_r, Ft, 1, G, h, 1, EPI_STORE, dB_r, h);
     g.accumulate = accumulate;
     g.defer_reduce = 1;
     HIP_TRY(run_gemm(dt, g, true, partB, stream), "tp_mlp_shard_bwd: dB GEMM");
     if (dt == TP_BF16) {
-        HIP_TRY(stream_after(*sd, 1, stream, sd->s), "tp_mlp_shard_bwd: fork");
-        HIP_TRY(gemm_splitk_reduce(g, plan_gemm_bf16(g.M, g.N, g.K, true), partB, sd->s), "tp_mlp_shard_bwd: dB reduction");
+        HIP_TRY(side.fork(1), "tp_mlp_shard_bwd: fork");
+        HIP_TRY(gemm_splitk_reduce(g, plan_gemm_bf16(g.M, g.N, g.K, true), partB, side.side()),
+                "tp_mlp_shard_bwd: dB reduction");
     }
     // dA_r = X^T dU
     g = req(h, Ft, T, X, h, 1, dU, Ft, 1, EPI_STORE, dA_r, Ft);
@@ -316,7 +355,7 @@ tp_status tp_mlp_shard_bwd(int T, int h, int ffn, int t, int r, tp_dtype dt, con
     // dX_r = dU A_r^T
     g = req(T, h, Ft, dU, Ft, 0, A_r, Ft, 0, EPI_STORE, dX_r, h);
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_mlp_shard_bwd: dX GEMM");
-    HIP_TRY(stream_after(*sd, 2, sd->s, stream), "tp_mlp_shard_bwd: join");
+    HIP_TRY(side.join(), "tp_mlp_shard_bwd: join");
     return ok();
 }
 
@@ -381,22 +420,23 @@ tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dty
     float* colp = (float*)(base + w.dO + w.D + w.dQKV + w.partWo + w.partWqkv);
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideStream* sd = nullptr;
-    HIP_TRY(side_stream(sd), "tp_attn_shard_bwd: side stream");
+    HIP_TRY(side_stream(stream, sd), "tp_attn_shard_bwd: side stream");
+    SideFork side(sd, stream);
     // side: dWo_r = O_r^T G (needs neither dO nor the attention backward), beside the dO GEMM
     // (whose 192 one-per-CU tiles leave room) and the attention kernels
-    HIP_TRY(stream_after(*sd, 0, stream, sd->s), "tp_attn_shard_bwd: fork");
+    HIP_TRY(side.fork(0), "tp_attn_shard_bwd: fork");
     // dO = G Wo_r^T
     GemmReq g = req(T, h_t, h, G, h, 0, Wo_r, h, 0, EPI_STORE, dO, h_t);
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_bwd: dO GEMM");
     g = req(h_t, h, T, O_r, h_t, 1, G, h, 1, EPI_STORE, dWo_r, h);
     g.accumulate = accumulate;
-    HIP_TRY(run_gemm(dt, g, true, partWo, sd->s), "tp_attn_shard_bwd: dWo GEMM");
+    HIP_TRY(run_gemm(dt, g, true, partWo, side.side()), "tp_attn_shard_bwd: dWo GEMM");
     if (T > 0)
         HIP_TRY(attn_bwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, dO, Dv, dQKV, dp, stream),
                 "tp_attn_shard_bwd: attention backward");
     // side: dbqkv = column sums of dQKV, beside the dWqkv GEMM
-    HIP_TRY(stream_after(*sd, 1, stream, sd->s), "tp_attn_shard_bwd: fork");
-    if (dbqkv_r) HIP_TRY(colsum(1, T, 3 * h_t, dQKV, dbqkv_r, accumulate, colp, sd->s), "tp_attn_shard_bwd: dbqkv");
+    HIP_TRY(side.fork(1), "tp_attn_shard_bwd: fork");
+    if (dbqkv_r) HIP_TRY(colsum(1, T, 3 * h_t, dQKV, dbqkv_r, accumulate, colp, side.side()), "tp_attn_shard_bwd: dbqkv");
     // dWqkv_r = Xn^T dQKV
     g = req(h, 3 * h_t, T, Xn, h, 1, dQKV, 3 * h_t, 1, EPI_STORE, dWqkv_r, 3 * h_t);
     g.accumulate = accumulate;
@@ -404,7 +444,7 @@ tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dty
     // dXn_r = dQKV Wqkv_r^T
     g = req(T, h, 3 * h_t, dQKV, 3 * h_t, 0, Wqkv_r, 3 * h_t, 0, EPI_STORE, dXn_r, h);
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_bwd: dXn GEMM");
-    HIP_TRY(stream_after(*sd, 2, sd->s, stream), "tp_attn_shard_bwd: join");
+    HIP_TRY(side.join(), "tp_attn_shard_bwd: join");
     return ok();
 }
 
