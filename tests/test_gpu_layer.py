@@ -1,5 +1,5 @@
-"""GPU parity of one whole pre-LN layer step, every rank of t = 2 on one device, through the
-C ABI (the LayerShard driver): the layer output, the input gradient and every parameter gradient
+"""GPU parity of one whole pre-LN layer step, every rank of t = 2 (small shapes) and of t = 4 (the
+2.5B shape at full size) on one device, through the C ABI (the LayerShard driver): the layer output, the input gradient and every parameter gradient
 of every rank against the float64 oracle's split layer ("Megatron-LM, annotated", §2.2 and §3.5).
 
 Tolerance: relative L2 <= 1e-2 (bf16 inputs, fp32 accumulation)."""
@@ -51,9 +51,9 @@ def host(a):
     return a.detach().double().cpu().numpy()
 
 
-@pytest.mark.parametrize("b,s,h,heads,ffn,t", [(2, 160, 384, 4, 1536, 2), (1, 96, 256, 4, 1024, 2)])
-def test_layer_step_every_output(b, s, h, heads, ffn, t):
-    p = tp_synth.layer_inputs(4242 + s, b, s, h, ffn, "bf16", bias_std=0.05, ln_random=True)
+def check_every_output(p, b, s, h, heads, ffn, t, tag):
+    """The layer output, the input gradient and every parameter gradient of every rank against the
+    oracle's split layer, rel-L2 <= 1e-2."""
     shards, x1, x2, dx1, dx = run_layer(p, b, s, h, heads, ffn, t)
     f = oracle.layer_split_fwd(p["x"], p, b, s, heads, t)
     g = oracle.layer_split_bwd(p["x"], p, f, p["G"], b, s, heads, t)
@@ -71,9 +71,24 @@ def test_layer_step_every_output(b, s, h, heads, ffn, t):
                 "dbqkv": g["attn"]["dbqkv"][qcols], "dWo": g["attn"]["dWo"][r * ht:(r + 1) * ht]}
         for k, ref in want.items():
             errs[f"{k}[{r}]"] = rel_l2(host(getattr(sh, k)), ref)
-    say(f"[layer] b={b} s={s} h={h} t={t}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    say(f"[layer] {tag} b={b} s={s} h={h} t={t}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     for k, e in errs.items():
         assert e <= 1e-2, (k, e)
+
+
+@pytest.mark.parametrize("b,s,h,heads,ffn,t", [(2, 160, 384, 4, 1536, 2), (1, 96, 256, 4, 1024, 2)])
+def test_layer_step_every_output(b, s, h, heads, ffn, t):
+    p = tp_synth.layer_inputs(4242 + s, b, s, h, ffn, "bf16", bias_std=0.05, ln_random=True)
+    check_every_output(p, b, s, h, heads, ffn, t, "small")
+
+
+def test_layer_2p5b_full_size_every_output():
+    """The 2.5B-shape layer at full size: 8 x 1024 tokens, h = 1920, 20 heads of 96, ffn 7680,
+    t = 4 (5 heads and 1920 MLP columns per rank), every rank, every output and gradient. The
+    oracle runs the whole split layer in float64 (~9 GB of host memory, tens of seconds)."""
+    b, s, h, heads, ffn, t = 8, 1024, 1920, 20, 7680, 4
+    p = tp_synth.layer_inputs(2525, b, s, h, ffn, "bf16", bias_std=0.05, ln_random=True)
+    check_every_output(p, b, s, h, heads, ffn, t, "2.5B full size")
 
 
 def test_layer_step_method_rank0():
