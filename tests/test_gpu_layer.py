@@ -83,12 +83,13 @@ def test_layer_step_every_output(b, s, h, heads, ffn, t):
 
 
 def test_layer_2p5b_full_size_every_output():
-    """The 2.5B-shape layer at full size: 8 x 1024 tokens, h = 1920, 20 heads of 96, ffn 7680,
-    t = 4 (5 heads and 1920 MLP columns per rank), every rank, every output and gradient. The
-    oracle runs the whole split layer in float64 (~9 GB of host memory, tens of seconds)."""
-    b, s, h, heads, ffn, t = 8, 1024, 1920, 20, 7680, 4
-    p = tp_synth.layer_inputs(2525, b, s, h, ffn, "bf16", bias_std=0.05, ln_random=True)
-    check_every_output(p, b, s, h, heads, ffn, t, "2.5B full size")
+    """The 2.5B-shape layer workload at full size, with its own inputs (biases 0, LayerNorm gain 1
+    and shift 0): 8 x 1024 tokens, h = 1920, 20 heads of 96, ffn 7680, t = 4 (5 heads and 1920
+    MLP columns per rank); every rank, every output and gradient. The oracle runs the whole split
+    layer in float64 (~9 GB of host memory)."""
+    w = tp_synth.WORKLOADS["layer_2p5b_t4"]
+    p = tp_synth.layer_inputs(w.seed, w.b, w.s, w.h, w.ffn, w.dtype)
+    check_every_output(p, w.b, w.s, w.h, w.heads, w.ffn, w.t, "2.5B full size")
 
 
 def test_layer_step_method_rank0():
