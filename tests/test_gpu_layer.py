@@ -92,11 +92,10 @@ def test_layer_2p5b_full_size_every_output():
     check_every_output(p, w.b, w.s, w.h, w.heads, w.ffn, w.t, "2.5B full size")
 
 
-def test_layer_step_method_rank0():
+def check_step_rank0(p, b, s, h, heads, ffn, t, tag):
     """LayerShard.step (the sequence bench.py times: fused g + LN2, pre-summed all-reduce inputs)
-    for rank 0 of t = 2 against the oracle."""
-    b, s, h, heads, ffn, t = 2, 128, 256, 4, 1024, 2
-    p = tp_synth.layer_inputs(4343, b, s, h, ffn, "bf16", bias_std=0.05, ln_random=True)
+    for rank 0 against the oracle's split layer: the layer output, the input gradient, the
+    replicated parameter gradients and rank 0's shards of the others."""
     shards, _x1, _x2, _dx1, _dx = run_layer(p, b, s, h, heads, ffn, t)   # sums every rank would receive
     dev = "cuda:0"
     T = b * s
@@ -111,16 +110,40 @@ def test_layer_step_method_rank0():
     shards[0].combine([sh.mlp_bwd(G) for sh in shards], None, None, dxn2_sum)
     dx1 = shards[0].ln2_bwd(dxn2_sum, G)
     shards[0].combine([sh.attn_bwd(dx1) for sh in shards], None, None, dxn1_sum)
-    x2, dx = shards[0].step(x, G, attn_sum, mlp_sum, dxn2_sum, dxn1_sum)
+    sh0 = shards[0]
+    del shards
+    x2, dx = sh0.step(x, G, attn_sum, mlp_sum, dxn2_sum, dxn1_sum)
     torch.cuda.synchronize()
     f = oracle.layer_split_fwd(p["x"], p, b, s, heads, t)
     g = oracle.layer_split_bwd(p["x"], p, f, p["G"], b, s, heads, t)
-    errs = {"x2": rel_l2(host(x2), f["x2"]), "dx": rel_l2(host(dx), g["dx"]),
-            "dln2_g": rel_l2(host(shards[0].dln2_g), g["dln2_g"]), "db2": rel_l2(host(shards[0].db2), g["mlp"]["db2"]),
-            "dA[0]": rel_l2(host(shards[0].dA), g["mlp"]["dA"][:, :ffn // t])}
-    say("[layer.step] " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    ht, Ft = h // t, ffn // t
+    qcols = np.concatenate([np.arange(i * h, i * h + ht) for i in range(3)])
+    want = {"dln1_g": g["dln1_g"], "dln1_b": g["dln1_b"], "dln2_g": g["dln2_g"], "dln2_b": g["dln2_b"],
+            "db2": g["mlp"]["db2"], "dbo": g["attn"]["dbo"], "dA": g["mlp"]["dA"][:, :Ft],
+            "db1": g["mlp"]["db1"][:Ft], "dB": g["mlp"]["dB"][:Ft], "dWqkv": g["attn"]["dWqkv"][:, qcols],
+            "dbqkv": g["attn"]["dbqkv"][qcols], "dWo": g["attn"]["dWo"][:ht]}
+    errs = {"x2": rel_l2(host(x2), f["x2"]), "dx": rel_l2(host(dx), g["dx"])}
+    for k, ref in want.items():
+        errs[k] = rel_l2(host(getattr(sh0, k)), ref)
+    say(f"[layer.step] {tag}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     for k, e in errs.items():
         assert e <= 1e-2, (k, e)
+
+
+def test_layer_step_method_rank0():
+    b, s, h, heads, ffn, t = 2, 128, 256, 4, 1024, 2
+    p = tp_synth.layer_inputs(4343, b, s, h, ffn, "bf16", bias_std=0.05, ln_random=True)
+    check_step_rank0(p, b, s, h, heads, ffn, t, "small")
+
+
+def test_layer_step_8p3b_full_size_rank0():
+    """The timed workload itself: the 8.3B-shape layer (8 x 1024 tokens, h = 3072, 32 heads of
+    96, ffn 12288, t = 8) with its own seeded inputs, rank 0's step in bench.py's launch sequence,
+    every output and rank-0 gradient against the whole float64 split layer (~18 GB of host
+    memory)."""
+    w = tp_synth.WORKLOADS["layer_8p3b_t8"]
+    p = tp_synth.layer_inputs(w.seed, w.b, w.s, w.h, w.ffn, w.dtype)
+    check_step_rank0(p, w.b, w.s, w.h, w.heads, w.ffn, w.t, "8.3B full size rank 0")
 
 
 DROP = {"p": 0.1, "seed": 0xC0FFEE1234, "resid_streams": (11, 12), "attn_streams": [100, 101]}
