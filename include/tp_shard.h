@@ -30,7 +30,8 @@
  *    failure reported by the HIP runtime returns TP_ERR_HIP. Forward calls with zero tokens
  *    return TP_OK and launch nothing; backward calls with zero tokens still write their weight
  *    and bias gradients (zeros, or unchanged when accumulating). Nothing aborts or throws
- *    across this boundary. Each GEMM operand must be smaller than 2032 MiB (TP_ERR_HIP otherwise).
+ *    across this boundary. Each bf16 or fp8 GEMM operand must be smaller than 2032 MiB
+ *    (TP_ERR_UNSUPPORTED otherwise, before anything is launched).
  *  - Determinism: fixed reduction orders, no floating-point atomics; repeated calls on the
  *    same inputs give identical bits.
  *  - Workspace: calls that need scratch memory take (ws, ws_bytes); the matching *_workspace

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 
@@ -150,6 +151,18 @@ tp_status check_mult8(const char* fn, const char* what, long v) {
 
 size_t al256(size_t b) { return (b + 255) / 256 * 256; }
 
+// bf16 and fp8 GEMM operands are addressed with 32-bit buffer offsets, and chunks outside an
+// operand are fetched at an offset of 2032 MiB, which must lie past its end: every operand must be
+// smaller. Checked before anything is launched.
+constexpr size_t kMaxOperandBytes = (size_t)2032 << 20;
+tp_status check_operands(const char* fn, size_t elem_bytes, std::initializer_list<size_t> elems) {
+    for (size_t n : elems)
+        if (n * elem_bytes >= kMaxOperandBytes)
+            return fail(TP_ERR_UNSUPPORTED, "%s: a GEMM operand of %zu bytes reaches the 2032 MiB limit", fn,
+                        n * elem_bytes);
+    return TP_OK;
+}
+
 // tp_dropout -> kernel parameters: thr = round(p * 65536), scale = 65536 / (65536 - thr). NULL or
 // p = 0 gives thr = 0 (no dropout).
 tp_status make_drop(const char* fn, const tp_dropout* d, DropParams& out) {
@@ -243,7 +256,10 @@ tp_status check_mlp(const char* fn, int T, int h, int ffn, int t, int r, tp_dtyp
     if (T < 0) return fail(TP_ERR_SHAPE, "%s: T=%d is negative", fn, T);
     if ((s = check_mult8(fn, "h", h)) != TP_OK) return s;
     if (ffn <= 0 || ffn % t != 0) return fail(TP_ERR_SHAPE, "%s: ffn=%d must be a positive multiple of t=%d", fn, ffn, t);
-    return check_mult8(fn, "ffn/t", ffn / t);
+    if ((s = check_mult8(fn, "ffn/t", ffn / t)) != TP_OK) return s;
+    if (dt != TP_BF16) return TP_OK;   // the fp32 GEMM indexes with 64-bit offsets
+    const size_t Tz = (size_t)T, hz = (size_t)h, Fz = (size_t)(ffn / t);
+    return check_operands(fn, 2, {Tz * hz, Tz * Fz, hz * Fz});
 }
 
 tp_status check_attn(const char* fn, int b, int s, int h, int heads, int t, int r, tp_dtype dt, int causal) {
@@ -261,7 +277,8 @@ tp_status check_attn(const char* fn, int b, int s, int h, int heads, int t, int 
     int d = h / heads;
     if (d != 64 && d != 96 && d != 128 && d != 192)
         return fail(TP_ERR_UNSUPPORTED, "%s: head width %d (supported: 64, 96, 128, 192)", fn, d);
-    return TP_OK;
+    const size_t Tz = (size_t)b * s, hz = (size_t)h, qz = (size_t)3 * (h / t);
+    return check_operands(fn, 2, {Tz * hz, Tz * qz, hz * qz});
 }
 
 tp_status check_vocab(const char* fn, int N, int h, int Vpad, int t, int r, tp_dtype dt) {
@@ -272,7 +289,8 @@ tp_status check_vocab(const char* fn, int N, int h, int Vpad, int t, int r, tp_d
     if (N < 0) return fail(TP_ERR_SHAPE, "%s: N=%d is negative", fn, N);
     if ((s = check_mult8(fn, "h", h)) != TP_OK) return s;
     if (Vpad <= 0 || Vpad % t != 0) return fail(TP_ERR_SHAPE, "%s: Vpad=%d must be a positive multiple of t=%d", fn, Vpad, t);
-    return check_mult8(fn, "Vpad/t", Vpad / t);
+    if ((s = check_mult8(fn, "Vpad/t", Vpad / t)) != TP_OK) return s;
+    return check_operands(fn, 2, {(size_t)N * h, (size_t)(Vpad / t) * h});
 }
 
 size_t xent_ws(int N, int h, int Vt) {
@@ -828,8 +846,8 @@ tp_status tp_gemm_fp8(int M, int N, int K, const uint8_t* A, int lda, const floa
         NEED(aux);
         if (bias) return fail(TP_ERR_ARG, "%s: TP_EPI_DGELU takes no bias", fn);
     }
-    if ((size_t)M * lda >= 0x7fff0000u || (size_t)N * ldb >= 0x7fff0000u)
-        return fail(TP_ERR_SHAPE, "%s: an operand is 2 GiB or larger", fn);
+    tp_status st = check_operands(fn, 1, {(size_t)M * lda, (size_t)N * ldb});
+    if (st != TP_OK) return st;
     if (M == 0 || N == 0) return ok();
     const size_t need = tp_gemm_fp8_workspace(M, N, K);
     const bool split_ok = epi == TP_EPI_STORE && ws && aligned16(ws) && ws_bytes >= need;

@@ -197,6 +197,8 @@ def test_gemm_fp8_argument_errors():
     assert call(epi=tp.TP_EPI_DGELU, aux=FAKE, bias=FAKE) == tp.TP_ERR_ARG
     assert call(sa=None) == tp.TP_ERR_ARG
     assert call(A=FAKE + 8) == tp.TP_ERR_ARG                   # misaligned operand
+    assert call(M=520192, K=4096, lda=4096, ldb=4096) == tp.TP_ERR_UNSUPPORTED   # A of exactly 2032 MiB
+    assert call(M=520191, N=520192, K=4096, lda=4096, ldb=4096, ldc=520192) == tp.TP_ERR_UNSUPPORTED   # B
     assert call(M=-1) == tp.TP_ERR_SHAPE
     assert "tp_gemm_fp8" in tp.tp_last_error()
 
@@ -218,3 +220,23 @@ def test_dropout_and_embedding_argument_errors():
     assert b(1000, 64, 128, 8, 1, tp.TP_BF16, FAKE, FAKE, FAKE, 0, FAKE, nb - 256, None) == tp.TP_ERR_WORKSPACE
     assert b(1000, 64, 128, 8, 1, tp.TP_BF16, FAKE, FAKE, FAKE, 2, FAKE, nb, None) == tp.TP_ERR_ARG
     assert "tp_embedding_shard_bwd" in tp.tp_last_error()
+
+
+def test_operand_size_limit():
+    """bf16 and fp8 GEMM operands must stay below 2032 MiB (32-bit buffer offsets, out-of-range
+    chunks fetched at that offset): refused on the host, before any launch, as unsupported. The
+    fp32 MLP path indexes with 64-bit offsets and has no such limit."""
+    T = (2032 << 20) // (2 * 3072)            # X = T x 3072 bf16 just below the limit
+    mlp = tp.lib.tp_mlp_shard_fwd
+    assert mlp(T + 8, 3072, 12288, 8, 0, tp.TP_BF16, *([FAKE] * 7), None) == tp.TP_ERR_UNSUPPORTED
+    assert "2032 MiB" in tp.tp_last_error()
+    # ffn/t columns make U and Y the largest operands
+    assert mlp(65536, 256, 16384 * 8, 8, 0, tp.TP_BF16, *([FAKE] * 7), None) == tp.TP_ERR_UNSUPPORTED
+    bwd = tp.lib.tp_mlp_shard_bwd
+    assert bwd(T + 8, 3072, 12288, 8, 0, tp.TP_BF16, *([FAKE] * 10), 0, FAKE, 1 << 40, None) == tp.TP_ERR_UNSUPPORTED
+    att = tp.lib.tp_attn_shard_fwd
+    assert att(T // 1024 + 1, 1024, 3072, 32, 8, 0, tp.TP_BF16, 1, *([FAKE] * 8), None, None) == tp.TP_ERR_UNSUPPORTED
+    xent = tp.lib.tp_vocab_xent_shard_fwd
+    assert xent(T + 8, 3072, 51200, 50257, 8, 0, tp.TP_BF16, 0, *([FAKE] * 7), FAKE, 1 << 40, None) == tp.TP_ERR_UNSUPPORTED
+    # E_r of 2032 MiB: Vpad / t rows of h
+    assert xent(16, 8192, 130048 * 8, 100, 8, 0, tp.TP_BF16, 0, *([FAKE] * 7), FAKE, 1 << 40, None) == tp.TP_ERR_UNSUPPORTED
