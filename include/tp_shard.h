@@ -16,10 +16,10 @@
  *    (0 = null stream), except that tp_mlp_shard_bwd and tp_attn_shard_bwd also run part of their
  *    work (column sums, split-K reductions, the dWo GEMM) on a second stream of the device's own,
  *    forked from the given stream by an event and joined back into it before they return: the
- *    given stream sees all of the call's work in order, and HIP graph capture records the fork
- *    and join. That stream and its events are created on the device's first such call; a first
- *    call made while the given stream is being captured creates nothing and runs all of its work
- *    on the given stream. Calls that use them are serialised on the host by a lock.
+ *    given stream sees all of the call's work in order. That stream and its events are created
+ *    on the device's first such call. While the given stream is being captured into a graph,
+ *    these calls fork nothing and run all of their work on the given stream. Calls that use the
+ *    second stream are serialised on the host by a lock.
  *  - Row-major, contiguous, 16-byte aligned. Tokens are rows: token = batch*s + position.
  *  - dt selects the element type of activations, weights, saved tensors and partials
  *    (TP_BF16: bfloat16 in, fp32 accumulate, bfloat16 out; TP_F32: fp32 throughout).

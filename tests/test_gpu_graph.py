@@ -1,6 +1,6 @@
 """The layer step captured into a HIP graph and replayed: every replay must reproduce the eager
-step bit for bit (the library launches only kernels, on the caller's stream or on its second
-stream forked from and joined back into it: no allocation, no memset, no synchronisation), with
+step bit for bit (under capture the library launches only kernels, all on the caller's stream:
+no allocation, no memset, no synchronisation, no fork onto its second stream), with
 eager work and synchronisations between the replays. Dropout is on, so the Philox draws and the
 attention keep-bit mask run under capture too."""
 import numpy as np
@@ -90,8 +90,8 @@ sys.exit(1 if bad else 0)
 def test_first_backward_call_under_capture():
     """A process whose first backward call is made while its stream is being captured: the call
     creates nothing and runs all of its work on the captured stream; the replay equals the eager
-    step run afterwards (which forks onto the second stream). Fresh process: the second stream is
-    per process and per device."""
+    step run afterwards (which creates the second stream and forks onto it). Fresh process: the
+    second stream is per process and per device."""
     import os
     import subprocess
     import sys
