@@ -79,9 +79,12 @@ __device__ __forceinline__ void read_frags8(const Gemm8State<C>& g, const char* 
     for (int j = 0; j < C::TN; ++j) g.ob.frag(Bs, j, s, bf[j]);
 }
 
+// One K step of MFMAs, issued at raised wave priority (s_setprio 1, restored to 0 after) so the
+// two waves sharing a SIMD fall out of phase instead of alternating MFMAs in lockstep.
 template <class C>
 __device__ __forceinline__ void mfma_step8(f32x16 (&acc)[C::TM][C::TN], const Frag8 (&af)[C::TM],
                                            const Frag8 (&bf)[C::TN]) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -91,6 +94,7 @@ __device__ __forceinline__ void mfma_step8(f32x16 (&acc)[C::TM][C::TN], const Fr
             // formats 0/0: E4M3 x E4M3; scale bytes 127 = 2^0 (E8M0) for both operands
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 127, 0, 127);
         }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 template <class C>
