@@ -474,10 +474,10 @@ __device__ __forceinline__ void gemm_tile(GemmState<C, LA, LB>& g, char* smem, f
     constexpr int NDW = (decltype(g.oa)::DMA ? 0 : 8) + (decltype(g.ob)::DMA ? 0 : 8);
     const bool more = kt + 1 < nk;
     // DMA of the next tile: issued behind the first MFMAs (which then start right after the
-    // barrier) when a register-staged operand is also in flight or the tile is 256x256; first
-    // thing in the tile otherwise (measured on MI355X: 256x192 and 128x128 tiles with both
-    // operands on DMA need the longer lead)
-    constexpr bool LATE = REG || (C::BM * C::BN >= 256 * 256);
+    // barrier) when a register-staged operand is also in flight; first thing in the tile when
+    // both operands go by DMA (measured on MI355X: those tiles need the longer lead; the 256x256
+    // vocabulary tiles too since their MFMAs issue at raised priority, 256 -> 248 us)
+    constexpr bool LATE = REG;
     // Barrier before the last k-step (see the end of the tile): not for the 256x256 tiles with two
     // register-staged operands (the extra live fragments spill) nor for the 256x192 and 128x128
     // tiles fed only by DMA (measured slower).
