@@ -24,8 +24,9 @@ Backward with G = dL/dx2: dx1 = G + LN2^T(sum_r dXn2_r), dx = dx1 + LN1^T(sum_r 
 where LN^T is the norm's backward applied to the f-summed partial.
 
 Pins: composition of the pinned blocks; split equals unsplit; float64 autograd and central
-finite differences on a tiny layer. End-to-end layer values are parity unpinned by the
-pages themselves (they print no layer-level number).
+finite differences on a tiny layer; the whole layer, forward and every gradient, against
+PyTorch's own pre-LN encoder layer (torch.nn.TransformerEncoderLayer, norm_first, erf GeLU, no
+dropout, causal mask) in float64. The pages print no layer-level number.
 """
 from .attention import attn_bwd, attn_fwd, attn_split_bwd, attn_split_fwd
 from .layernorm import layernorm_bwd, layernorm_fwd

@@ -92,6 +92,47 @@ def test_layer_against_torch_autograd():
         assert _rel(g["d" + k], T[k].grad.numpy()) < 1e-12, k
 
 
+def test_layer_against_torch_transformer_encoder_layer():
+    """The whole unsplit layer, forward and backward, against PyTorch's own pre-LN encoder layer
+    (torch.nn.TransformerEncoderLayer with norm_first, erf GeLU, no dropout, a causal mask) in
+    float64: a library composition of the block, independent of the oracle's."""
+    b, s, h, heads, ffn = 2, 6, 16, 4, 64
+    p = _layer_case(b, s, h, heads, ffn)
+    layer = torch.nn.TransformerEncoderLayer(h, heads, dim_feedforward=ffn, dropout=0.0, activation="gelu",
+                                             layer_norm_eps=1e-5, batch_first=True, norm_first=True,
+                                             dtype=torch.float64)
+    t64 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    with torch.no_grad():
+        layer.self_attn.in_proj_weight.copy_(t64(p["Wqkv"].T))
+        layer.self_attn.in_proj_bias.copy_(t64(p["bqkv"]))
+        layer.self_attn.out_proj.weight.copy_(t64(p["Wo"].T))
+        layer.self_attn.out_proj.bias.copy_(t64(p["bo"]))
+        layer.linear1.weight.copy_(t64(p["A"].T))
+        layer.linear1.bias.copy_(t64(p["b1"]))
+        layer.linear2.weight.copy_(t64(p["B"].T))
+        layer.linear2.bias.copy_(t64(p["b2"]))
+        for norm, k in ((layer.norm1, "ln1"), (layer.norm2, "ln2")):
+            norm.weight.copy_(t64(p[k + "_g"]))
+            norm.bias.copy_(t64(p[k + "_b"]))
+    x = t64(p["x"]).reshape(b, s, h).requires_grad_(True)
+    mask = torch.nn.Transformer.generate_square_subsequent_mask(s, dtype=torch.float64)
+    out = layer(x, src_mask=mask, is_causal=True)
+    (out * t64(p["G"]).reshape(b, s, h)).sum().backward()
+    f = oracle.layer_fwd(p["x"], p, b, s, heads)
+    g = oracle.layer_bwd(p["x"], p, f, p["G"], b, s, heads)
+    assert _rel(f["x2"], out.detach().reshape(b * s, h).numpy()) < 1e-13
+    assert _rel(g["dx"], x.grad.reshape(b * s, h).numpy()) < 1e-12
+    want = {("attn", "dWqkv"): layer.self_attn.in_proj_weight.grad.T, ("attn", "dbqkv"): layer.self_attn.in_proj_bias.grad,
+            ("attn", "dWo"): layer.self_attn.out_proj.weight.grad.T, ("attn", "dbo"): layer.self_attn.out_proj.bias.grad,
+            ("mlp", "dA"): layer.linear1.weight.grad.T, ("mlp", "db1"): layer.linear1.bias.grad,
+            ("mlp", "dB"): layer.linear2.weight.grad.T, ("mlp", "db2"): layer.linear2.bias.grad}
+    for (blk, k), ref in want.items():
+        assert _rel(g[blk][k], ref.numpy()) < 1e-12, k
+    for k, norm in (("ln1", layer.norm1), ("ln2", layer.norm2)):
+        assert _rel(g["d" + k + "_g"], norm.weight.grad.numpy()) < 1e-12, k
+        assert _rel(g["d" + k + "_b"], norm.bias.grad.numpy()) < 1e-12, k
+
+
 def test_layer_finite_differences_input():
     b, s, h, heads, ffn = 1, 4, 8, 2, 32
     p = _layer_case(b, s, h, heads, ffn)
