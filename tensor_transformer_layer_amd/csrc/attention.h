@@ -332,22 +332,32 @@ void attn_fwd_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int h
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ O,
                                                            int ld, int b, int s, int heads_t, float* __restrict__ Dv) {
-    size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    size_t total = (size_t)b * s * heads_t;
-    if (idx >= total) return;
-    int head = (int)(idx % heads_t);
-    size_t tok = idx / heads_t;
-    const bf16* a = dO + tok * ld + head * D;
-    const bf16* c = O + tok * ld + head * D;
+    // four lanes per (token, head) row, each taking every fourth 16-byte chunk of it: a wave's
+    // load covers 64 contiguous bytes of each of 16 rows; the four partial sums meet by shuffles
+    static_assert(D % 32 == 0, "head width must be a multiple of 32");
+    const size_t idx = ((size_t)blockIdx.x * 256 + threadIdx.x) >> 2;
+    const int part = threadIdx.x & 3;
+    const size_t total = (size_t)b * s * heads_t;
+    const bool live = idx < total;
     float acc = 0.f;
+    const int head = live ? (int)(idx % heads_t) : 0;
+    const size_t tok = live ? idx / heads_t : 0;
+    if (live) {
+        const bf16* a = dO + tok * ld + head * D;
+        const bf16* c = O + tok * ld + head * D;
 #pragma unroll
-    for (int k = 0; k < D; k += 8) {
-        bf16x8 x = *(const bf16x8*)(a + k), y = *(const bf16x8*)(c + k);
+        for (int k = part * 8; k < D; k += 32) {
+            bf16x8 x = *(const bf16x8*)(a + k), y = *(const bf16x8*)(c + k);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc += (float)x[e] * (float)y[e];
+            for (int e = 0; e < 8; ++e) acc += (float)x[e] * (float)y[e];
+        }
     }
-    int bi = (int)(tok / s), pos = (int)(tok % s);
-    Dv[((size_t)bi * heads_t + head) * s + pos] = acc;
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (live && part == 0) {
+        const int bi = (int)(tok / s), pos = (int)(tok % s);
+        Dv[((size_t)bi * heads_t + head) * s + pos] = acc;
+    }
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -24,7 +24,7 @@ static hipError_t bwd_d(int b, int s, int h_t, int heads_t, int causal, const vo
                         const float* lse, const void* dO, float* Dws, void* dQKV, const DropParams& dp,
                         hipStream_t st) {
     size_t rows = (size_t)b * s * heads_t;
-    hipLaunchKernelGGL((attn_bwd_dot_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL((attn_bwd_dot_kernel<D>), dim3((unsigned)((rows * 4 + 255) / 256)), dim3(256), 0, st,
                        (const bf16*)dO, (const bf16*)O, h_t, b, s, heads_t, Dws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
