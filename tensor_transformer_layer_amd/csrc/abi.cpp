@@ -57,7 +57,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 constexpr int kMaxDevices = 64;
 struct SideStream {
     hipStream_t s = nullptr;
-    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
 };
 std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
@@ -98,7 +98,7 @@ class SideFork {
     SideFork& operator=(const SideFork&) = delete;
     ~SideFork() { (void)join(); }
     hipStream_t side() const { return sd_ ? sd_->s : caller_; }
-    // the side stream waits for the caller's work so far (event slot 0 or 1)
+    // the side stream waits for the caller's work so far (event slot 0, 1 or 3)
     hipError_t fork(int slot) {
         if (!sd_) return hipSuccess;
         forked_ = true;
@@ -366,10 +366,16 @@ tp_status tp_mlp_shard_bwd(int T, int h, int ffn, int t, int r, tp_dtype dt, con
         HIP_TRY(gemm_splitk_reduce(g, plan_gemm_bf16(g.M, g.N, g.K, true), partB, side.side()),
                 "tp_mlp_shard_bwd: dB reduction");
     }
-    // dA_r = X^T dU
+    // dA_r = X^T dU; its split-K reduction on the side stream, beside the dX GEMM
     g = req(h, Ft, T, X, h, 1, dU, Ft, 1, EPI_STORE, dA_r, Ft);
     g.accumulate = accumulate;
+    g.defer_reduce = 1;
     HIP_TRY(run_gemm(dt, g, true, partA, stream), "tp_mlp_shard_bwd: dA GEMM");
+    if (dt == TP_BF16) {
+        HIP_TRY(side.fork(3), "tp_mlp_shard_bwd: fork");
+        HIP_TRY(gemm_splitk_reduce(g, plan_gemm_bf16(g.M, g.N, g.K, true), partA, side.side()),
+                "tp_mlp_shard_bwd: dA reduction");
+    }
     // dX_r = dU A_r^T
     g = req(T, h, Ft, dU, Ft, 0, A_r, Ft, 0, EPI_STORE, dX_r, h);
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_mlp_shard_bwd: dX GEMM");
