@@ -461,10 +461,14 @@ tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dty
     // side: dbqkv = column sums of dQKV, beside the dWqkv GEMM
     HIP_TRY(side.fork(1), "tp_attn_shard_bwd: fork");
     if (dbqkv_r) HIP_TRY(colsum(1, T, 3 * h_t, dQKV, dbqkv_r, accumulate, colp, side.side()), "tp_attn_shard_bwd: dbqkv");
-    // dWqkv_r = Xn^T dQKV
+    // dWqkv_r = Xn^T dQKV; its split-K reduction on the side stream, beside the dXn GEMM
     g = req(h, 3 * h_t, T, Xn, h, 1, dQKV, 3 * h_t, 1, EPI_STORE, dWqkv_r, 3 * h_t);
     g.accumulate = accumulate;
+    g.defer_reduce = 1;
     HIP_TRY(run_gemm(dt, g, true, partWqkv, stream), "tp_attn_shard_bwd: dWqkv GEMM");
+    HIP_TRY(side.fork(3), "tp_attn_shard_bwd: fork");
+    HIP_TRY(gemm_splitk_reduce(g, plan_gemm_bf16(g.M, g.N, g.K, true), partWqkv, side.side()),
+            "tp_attn_shard_bwd: dWqkv reduction");
     // dXn_r = dQKV Wqkv_r^T
     g = req(T, h, 3 * h_t, dQKV, 3 * h_t, 0, Wqkv_r, 3 * h_t, 0, EPI_STORE, dXn_r, h);
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_bwd: dXn GEMM");
