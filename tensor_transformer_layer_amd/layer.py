@@ -74,7 +74,6 @@ class LayerShard:
                             tp_attn_shard_bwd_workspace(b, s, h, heads, t, TP_BF16),
                             tp_layernorm_bwd_workspace(T, h, TP_BF16), tp_colsum_workspace(T, h, TP_BF16))
         self.ws = e((self.ws_bytes,), dtype=torch.uint8, device=device)
-        self.side = torch.cuda.Stream(device=device)   # default priority
         self.d_attn = self.d_res1 = self.d_res2 = None
         if drop is not None and drop["p"] > 0.0:
             self.mask = e((max(tp_attn_dropout_mask_bytes(b, s, heads, t) // 4, 1),), dtype=torch.int32, device=device)
@@ -164,22 +163,8 @@ class LayerShard:
         from the all-reduces (the sum over ranks of the partials, before bias and residual).
         recompute: run the forward again from x before the backward (activation checkpointing)."""
         self.attn_fwd(x)
-        p, T, h = self.p, self.T, self.h
-        tp_sum_partials_layernorm(T, h, 1, TP_BF16, [attn_sum], p["bo"], x, self.x1, EPS, p["ln2_g"], p["ln2_b"],
-                                  self.xn2, self.mean2, self.rstd2, drop=self.d_res1)
-        self.x1_in = self.x1
-        # The layer output x2 = x1 + D2(mlp_sum + b2) feeds nothing else in the step: outside a graph
-        # capture (and without recompute, which rewrites x1) it runs on a second stream beside the
-        # MLP GEMMs (memory-bound beside MFMA-bound) and is joined back before the step returns.
-        main = torch.cuda.current_stream()
-        fork = not recompute and not torch.cuda.is_current_stream_capturing()
-        if fork:
-            self.side.wait_stream(main)
-            with torch.cuda.stream(self.side):
-                self.combine_x2([mlp_sum])
-        else:
-            self.combine_x2([mlp_sum])
-        self._mlp(self.xn2)
+        self.combine_mlp_fwd([attn_sum], x)
+        self.combine_x2([mlp_sum])
         if recompute:
             self.attn_fwd(x)
             self.combine_mlp_fwd([attn_sum], x)
@@ -187,8 +172,6 @@ class LayerShard:
         self.ln2_bwd(dxn2_sum, G)
         self.attn_bwd(self.dx1)
         self.ln1_bwd(x, dxn1_sum, self.dx1)
-        if fork:
-            main.wait_stream(self.side)
         return self.x2, self.dx
 
 
