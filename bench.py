@@ -1,18 +1,18 @@
 """Throughput of one GPU's share of the 8.3B-shape tensor-parallel layer (t = 8, rank 0) on MI355X.
 
-One step = the whole hot path of rank 0 over one batch of 8 x 1024 synthetic tokens:
-  * the pre-LN layer shard, forward + backward (h=3072, 32 heads of 96 -> 4 per rank,
-    ffn=12288 -> 1536 columns per rank): LN1, QKV GEMM, causal attention, output projection,
-    residual, LN2, MLP GEMM1 + bias + GeLU, GEMM2, residual; the backward with dgrad/wgrad GEMMs,
-    the attention backward, both LN backwards and the bias column sums;
-  * the vocabulary-parallel fused logits GEMM + cross-entropy statistics of the same model
-    (vocabulary 50,257 padded to 51,200 -> 6,400 rows per rank) and the loss merge.
-The all-reduce results rank 0 would receive (g forward, f backward, the loss statistics of the
-other ranks) are computed once before timing by running all 8 ranks, then handed to rank 0's
+One step = rank 0's pre-LN layer shard, forward + backward, over one batch of 8 x 1024 synthetic
+tokens (h=3072, 32 heads of 96 -> 4 per rank, ffn=12288 -> 1536 columns per rank): LN1, QKV GEMM,
+causal attention, output projection, residual, LN2, MLP GEMM1 + bias + GeLU, GEMM2, residual;
+the backward with the input- and weight-gradient GEMMs, the attention backward, both LN
+backwards and the bias column sums. The all-reduce results rank 0 would receive (g forward,
+f backward) are computed once before timing by running all 8 ranks, then handed to rank 0's
 step: no collective runs inside the timed region.
 
-value = algorithmic FLOP of the step / measured step time (TFLOP/s), FLOPs counted 2 per
-multiply-add, backward = 2x forward, causal attention over the visible pairs only.
+value = the layer's algorithmic FLOP / the layer step's time (TFLOP/s), FLOPs counted 2 per
+multiply-add, backward = 2x forward, causal attention over the visible pairs only. The rest of
+the hot path, rank 0's vocabulary shard (fused logits GEMM + cross-entropy statistics and the
+loss merge over 8 ranks, vocabulary 50,257 padded to 51,200), is timed on its own and reported
+in "vocab_xent". "roofline" is the layer's dominant GEMM, timed live in isolation.
 Prints ONE JSON line.
 """
 import argparse
@@ -34,6 +34,7 @@ PEAK_BF16 = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12         # bytes/s
 COPY_PROBE_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "vocab_xent_gemm_8p3b.md")
+DOMINANT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_dominant_gemm_8p3b.md")
 KERNEL_SOURCES = ["common.h", "gemm.h", "gemm_dispatch.h", "gemm_plan.cpp", "xent.h"]
 FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp8_layer_gemms_8p3b.md")
 FP8_KERNEL_SOURCES = ["common.h", "gemm.h", "gemm_fp8.hip"]
@@ -96,7 +97,7 @@ def stage_inputs():
 
 
 def cpu_baseline(p, xe, seqs=8, heads=HEADS):
-    """The float64 oracle on rank 0's work for `seqs` sequences (the same step, fewer tokens)."""
+    """The float64 oracle on rank 0's layer step for `seqs` sequences (the same step, fewer tokens)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -120,7 +121,7 @@ def cpu_baseline(p, xe, seqs=8, heads=HEADS):
         run()
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
-    flops = layer_flops(seqs, S, H, heads, FFN, TP) + xent_flops(T, H, Vt)
+    flops = layer_flops(seqs, S, H, heads, FFN, TP)
     try:
         cores = len(os.sched_getaffinity(0))
     except Exception:
@@ -132,7 +133,7 @@ def cpu_baseline(p, xe, seqs=8, heads=HEADS):
     except Exception:
         pass
     return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"rank 0 step (layer fwd+bwd + vocab-shard statistics) on {seqs} of {B} sequences "
+            "sample": f"rank 0's layer step (fwd+bwd) on {seqs} of {B} sequences "
                       f"({T} tokens), float64 NumPy, median of 3 runs ({', '.join(f'{t:.1f}' for t in times)} s); "
                       f"{cores} cores in the affinity mask, {blas}"}
 
@@ -149,7 +150,6 @@ def _oracle_step(oracle, p, xe, x, G, Wqkv_r, bq, Wo_r, A_r, b1_r, B_r, seqs, he
     dx1 = G + b2["dx"]
     ga = oracle.attn_shard_bwd(l1["y"], Wqkv_r, Wo_r, fa, dx1, seqs, S, heads // TP)
     oracle.layernorm_bwd(x, p["ln1_g"], l1["mean"], l1["rstd"], ga["dXn"])
-    oracle.xent_shard_stats(xe["X"][:T], xe["E0"], xe["targets"][:T], TP, 0, VOCAB)
 
 
 def main():
@@ -254,60 +254,64 @@ def main():
     stream = torch.cuda.current_stream()
     if args.vocab_bwd:
         return bench_vocab_bwd(args, tp, torch, T, Vt, Xv, E0, tg, peers, stream)
-    xev = []
     if args.copy_probe:
         copy_probe(torch, dev)
 
-    step_ev = []
-
-    def step(record):
-        if record:
-            s0 = torch.cuda.Event(enable_timing=True)
-            s0.record(stream)
+    def layer_step():
         if args.embedding:
             tp.tp_embedding_shard_fwd(T, H, VOCAB_PAD, TP, 0, tp.TP_BF16, tg, E0, emb_out)
         rank0.step(x, G, attn_sum, mlp_sum, dxn2_sum, dxn1_sum, recompute=args.recompute)
         if args.embedding:
             tp.tp_embedding_shard_bwd(T, H, VOCAB_PAD, TP, 0, tp.TP_BF16, tg, rank0.dx, dE0, 0, emb_ws, emb_ws_bytes)
-        if record:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+
+    def vocab_step():
         tp.tp_vocab_xent_shard_fwd(T, H, VOCAB_PAD, VOCAB, TP, 0, tp.TP_BF16, 0, Xv, E0, tg, mx, se, tv, am, xws,
                                    xws_bytes)
-        if record:
-            e1.record(stream)
-            xev.append((e0, e1))
         tp.tp_vocab_xent_combine(T, TP, [q[0] for q in peers], [q[1] for q in peers], [q[2] for q in peers], loss, mean)
-        if record:
-            s1 = torch.cuda.Event(enable_timing=True)
-            s1.record(stream)
-            step_ev.append((s0, s1))
+
+    def step():
+        layer_step()
+        vocab_step()
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     if args.graph:
         return bench_graph(args, torch, step, heads, stream)
-    # the timed steps carry no per-step events (each record leaves a ~5 us gap in the stream); a
-    # second pass of as many steps records them for the breakdown, the roofline kernel's time
-    # and the per-step spread
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
+
+    def timed(fn, n):
+        """Mean time of fn() over n back-to-back calls, one pair of HIP events around all of them."""
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b_) / n
+
+    # the timed region: K layer steps with no events inside (each record leaves a gap in the stream)
+    ms = timed(layer_step, args.steps)
+    # the rest of the hot path, timed on its own: the vocabulary shard's fused logits GEMM + CE
+    # statistics and the loss merge
+    xent_ms = timed(vocab_step, args.steps)
+    # per-step spread: a second pass of as many layer steps, each bracketed by its own events
+    per_step = []
     for _ in range(args.steps):
-        step(False)
-    end.record(stream)
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        layer_step()
+        b_.record(stream)
+        per_step.append((a, b_))
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b_) for a, b_ in per_step])
+    clock = sample_sclk(lambda: [layer_step() for _ in range(max(1, int(1500 / max(ms, 1e-3))))], torch)
+    roof = dominant_gemm_roofline(args, tp, torch, rank0, G, stream)
+
     fl_layer = layer_flops(B, S, H, heads, FFN, TP)
     fl_xent = xent_flops(T, H, Vt)
-    value = (fl_layer + fl_xent) / (ms * 1e-3) / 1e12
-    xent_ms = float(np.mean([a.elapsed_time(b_) for a, b_ in xev]))
-    xent_achieved = fl_xent / (xent_ms * 1e-3) / 1e12
-    per_step = np.array([a.elapsed_time(b_) for a, b_ in step_ev])
-
+    value = fl_layer / (ms * 1e-3) / 1e12
+    xent_tf = fl_xent / (xent_ms * 1e-3) / 1e12
+    peak_info = rocminfo_peak()
     out = {
         "metric": "layer-shard TFLOP/s fwd+bwd (% bf16 MFMA peak), 8.3B shape t=8, 1 GPU",
         "value": round(value, 2),
@@ -320,40 +324,132 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, uniform targets)",
-        "config": {"workload": "8.3B-shape layer shard t=8 rank 0 fwd+bwd + vocab-parallel xent shard"
+        "data": "synthetic (seeded N(0,1) activations and gradients, N(0,0.02^2) weights, uniform targets)",
+        "config": {"workload": f"8.3B-shape layer shard, tp=8, rank 0, forward + backward: {B} x {S} tokens, "
+                               f"hidden {H}, {heads} heads of {H // heads} ({heads // TP} per rank), ffn {FFN} "
+                               f"({FFN // TP} columns per rank)"
                                + (" + input-embedding lookup fwd+bwd" if args.embedding else "")
                                + (f", dropout {args.dropout}" if args.dropout else "")
                                + (", activation recompute" if args.recompute else ""),
                    "batch": B, "seq_len": S, "hidden": H, "heads": heads, "ffn": FFN, "tp": TP,
-                   "vocab_padded": VOCAB_PAD, "parallelism": "one rank of tp8 (sums pre-staged)",
+                   "parallelism": "one rank of tp8 (all-reduce results pre-staged)",
                    "dropout": args.dropout, "recompute": args.recompute, "embedding": args.embedding},
         "pct_bf16_peak": round(100 * value * 1e12 / PEAK_BF16, 2),
+        "layer_gflop": round(fl_layer / 1e9, 2),
         "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
-        "breakdown": {"layer_gflop": round(fl_layer / 1e9, 2), "xent_gflop": round(fl_xent / 1e9, 2),
-                      "xent_ms": round(xent_ms, 4),
-                      "layer_ms": round(ms - xent_ms, 4),
-                      "layer_tflops": round(fl_layer / ((ms - xent_ms) * 1e-3) / 1e12, 2)},
-        "roofline": {"bound": "mfma", "kernel": "fused vocab logits GEMM + CE statistics (gemm_bf16_kernel "
-                     "with EpiXent in two launches: 256x256 tiles over vocabulary rows 0-6143, 64x64 tiles over "
-                     "6144-6399; plus its per-token tile merge)",
-                     "achieved": round(xent_achieved, 2), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                     "frac": round(xent_achieved * 1e12 / PEAK_BF16, 4), "traffic": measured_traffic(),
-                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
+        "vocab_xent": {"what": "rank 0's vocabulary shard (6400 of 51,200 rows): fused logits GEMM + per-token "
+                               "max / sum-exp / target / argmax, then the loss merge over 8 ranks; timed on its own",
+                       "ms": round(xent_ms, 4), "gflop": round(fl_xent / 1e9, 2), "tflops": round(xent_tf, 2),
+                       "frac": round(xent_tf * 1e12 / PEAK_BF16, 4),
+                       "traffic": measured_traffic(),
+                       "traffic_unit": "HBM bytes per call of the fused GEMM (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                       "copy-calibrated), from the committed counter summary; null once stale"},
+        "hot_path_ms": round(ms + xent_ms, 4),
+        "roofline": roof,
+        "clock": {"sclk_mhz_under_load": clock, "rocminfo": peak_info},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, xe, heads=heads)
     print(json.dumps(out), flush=True)
 
 
+def rocminfo_peak():
+    """Compute units and maximum engine clock of the gfx950 agent as rocminfo reports them, and
+    the dense bf16 MFMA peak they imply (4096 FLOP per clock per CU)."""
+    import subprocess
+    try:
+        text = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except Exception:
+        return None
+    for agent in text.split("Agent ")[1:]:
+        if "gfx950" not in agent:
+            continue
+        cu = re.search(r"Compute Unit:\s*(\d+)", agent)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s*(\d+)", agent)
+        if cu and mhz:
+            cus, f = int(cu.group(1)), int(mhz.group(1))
+            return {"compute_units": cus, "max_clock_mhz": f,
+                    "bf16_dense_peak_tflops": round(cus * f * 1e6 * 4096 / 1e12, 1)}
+    return None
+
+
+def sample_sclk(run, torch):
+    """Median shader clock (MHz) that rocm-smi reports while run() keeps the GPU busy with layer
+    steps for about a second and a half; None if the tool is unavailable."""
+    import subprocess
+    import threading
+    vals, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+                m = re.search(r"sclk clock level:\s*\d+:?\s*\((\d+)Mhz\)", r.stdout)
+                if m:
+                    vals.append(int(m.group(1)))
+            except Exception:
+                return
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    run()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30)
+    return int(np.median(vals)) if vals else None
+
+
+# The layer's dominant GEMM, the weight gradient dB_r = Y_r^T G of the MLP (1536 x 3072 x 8192,
+# both operands MN-contiguous): name, M, N, K, flops.
+DOMINANT = ("MLP weight gradient dB_r = Y_r^T G (gemm_bf16_kernel 256x256 TN, 3 K splits, + split-K reduction)",
+            FFN // TP, H, B * S)
+
+
+def dominant_gemm_roofline(args, tp, torch, rank0, G, stream):
+    """Average launch time of the layer's dominant GEMM, measured live: the same call the step
+    makes (same shape, plan, operands and stream) through tp_gemm_bf16, each launch bracketed by
+    HIP events, with a 320 MB write before each so that its operands come from HBM as they do
+    inside the step (the MALL holds 256 MB)."""
+    name, M, N, K = DOMINANT
+    nb = tp.tp_gemm_bf16_workspace(M, N, K)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    flush = torch.empty(80 << 20, dtype=torch.float32, device="cuda:0")
+
+    def call():
+        tp.tp_gemm_bf16(M, N, K, rank0.Y, M, 1, G, N, 1, tp.TP_EPI_STORE, out, None, N, None, None, 0, ws, nb)
+
+    for _ in range(3):
+        call()
+    ev = []
+    for i in range(args.steps):
+        flush.fill_(float(i))
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b_.record(stream)
+        ev.append((a, b_))
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b_) for a, b_ in ev])) * 1e3
+    fl = 2.0 * M * N * K
+    ach = fl / (us * 1e-6) / 1e12
+    return {"bound": "mfma", "kernel": name, "M_N_K": [M, N, K], "gflop_per_launch": round(fl / 1e9, 2),
+            "avg_launch_us": round(us, 2), "achieved": round(ach, 2), "peak": PEAK_BF16 / 1e12,
+            "unit": "TFLOP/s", "frac": round(ach * 1e12 / PEAK_BF16, 4),
+            "traffic": measured_traffic(DOMINANT_TRAFFIC_FILE, KERNEL_SOURCES),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated), from the "
+                            "committed counter summary; null once the kernel sources have changed"}
+
+
 def bench_graph(args, torch, step, heads, stream):
-    """The same step captured once into a HIP graph (every call is a kernel launch on the captured
-    stream) and replayed; each replay is bracketed by events outside the graph."""
+    """The whole hot path (layer step + vocabulary shard) captured once into a HIP graph (every
+    call is a kernel launch on the captured stream) and replayed; each replay is bracketed by
+    events outside the graph."""
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.graph(graph, stream=side):
-        step(False)
+        step()
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         graph.replay()
@@ -371,11 +467,12 @@ def bench_graph(args, torch, step, heads, stream):
     fl = layer_flops(B, S, H, heads, FFN, TP) + xent_flops(B * S, H, VOCAB_PAD // TP)
     value = fl / (ms * 1e-3) / 1e12
     print(json.dumps({
-        "metric": "layer-shard TFLOP/s fwd+bwd (% bf16 MFMA peak), 8.3B shape t=8, 1 GPU, HIP graph replay",
+        "metric": "hot-path TFLOP/s (layer shard fwd+bwd + vocabulary shard xent), 8.3B shape t=8, 1 GPU, "
+                  "HIP graph replay",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, uniform targets)",
-        "config": {"workload": "the default step (layer shard fwd+bwd + vocab-parallel xent shard) as one graph",
+        "config": {"workload": "layer shard fwd+bwd + vocab-parallel xent shard, one graph per step",
                    "dropout": args.dropout, "recompute": args.recompute, "embedding": args.embedding},
         "pct_bf16_peak": round(100 * value * 1e12 / PEAK_BF16, 2),
         "step_ms_p10_p50_p90": [round(float(np.percentile(per, q)), 4) for q in (10, 50, 90)]}), flush=True)

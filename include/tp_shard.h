@@ -12,14 +12,10 @@
  *
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers owned by the caller. The library never allocates
- *    device memory, frees or synchronises with the host. It launches on the stream it is given
- *    (0 = null stream), except that tp_mlp_shard_bwd and tp_attn_shard_bwd also run part of their
- *    work (column sums, split-K reductions, the dWo GEMM) on a second stream of the device's own,
- *    forked from the given stream by an event and joined back into it before they return: the
- *    given stream sees all of the call's work in order. That stream and its events are created
- *    on the device's first such call. While the given stream is being captured into a graph,
- *    these calls fork nothing and run all of their work on the given stream. Calls that use the
- *    second stream are serialised on the host by a lock.
+ *    device memory, frees or synchronises with the host, and keeps no state between calls
+ *    apart from the thread-local error text: it creates no streams or events and takes no locks.
+ *    Every kernel of a call is launched on the stream it is given (0 = null stream), in order, so
+ *    calls on distinct streams are independent and a call can be captured into a graph.
  *  - Row-major, contiguous, 16-byte aligned. Tokens are rows: token = batch*s + position.
  *  - dt selects the element type of activations, weights, saved tensors and partials
  *    (TP_BF16: bfloat16 in, fp32 accumulate, bfloat16 out; TP_F32: fp32 throughout).
@@ -189,9 +185,12 @@ tp_status tp_vocab_xent_shard_fwd(int N, int h, int Vpad, int Vreal, int t, int 
                                   const int32_t* targets, float* max_r, float* sumexp_r, float* tgt_r,
                                   int32_t* argmax_r, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* The rank's fp32 logits [N, V_t], computed by the same GEMM kernel as tp_vocab_xent_shard_fwd
- * (same tiles, same accumulation order, hence the same bits). For verification of the fused
- * statistics; not on the hot path. */
+/* The rank's fp32 logits [N, V_t], stored. For verification of the fused statistics; not on the
+ * hot path. It runs the same bf16 MFMA main loop as tp_vocab_xent_shard_fwd but with the
+ * library's ordinary tile plan for the shape, not the fused call's tiles. Every tile shape sums
+ * each logit over k in the same order (64-deep K tiles in increasing k, the same MFMA
+ * instruction and k-steps inside a tile, no K split), so the stored logits carry exactly the
+ * bits the fused epilogue reduces. */
 tp_status tp_vocab_logits_shard(int N, int h, int Vpad, int t, int r, tp_dtype dt, const void* X,
                                 const void* E_r, float* logits, hipStream_t stream);
 
@@ -311,18 +310,41 @@ tp_status tp_colsum(int T, int n, tp_dtype dt, const void* G, void* out, int acc
                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
- * fp8 GEMMs for the layer shard (8-bit E4M3 operands, fp32 accumulation, bf16 outputs).
- * The pages train in 16-bit floating point with dynamic loss scaling ("Megatron-LM, annotated",
- * §4.2 Training optimization and hyperparameters) and define no 8-bit format; the scheme here is
- * this library's own. Format: OCP E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits;
- * largest finite 448; 0x7F/0xFF are NaN; no infinities).
- * ------------------------------------------------------------------------------------------- */
+ * The bf16 GEMM the shard calls are built from, exposed on its own: the column-parallel linear
+ * layer (replicated input times the rank's column block, bias and GeLU fused) and the
+ * row-parallel one (sharded input times the rank's row block, a full-size partial) of
+ * "Megatron-LM ..." digest §3.4, and their input and weight gradients ("Tensor and pipeline
+ * parallelism ..." §3, Proposition proof steps 4-5), as one call each.
+ *   P[M, N] = sum_k A(m, k) B(k, n), bf16 operands, fp32 accumulation, then the epilogue `epi`
+ *   (tp_epilogue) into bf16 C [M, ldc] (and C2 for TP_EPI_BIAS_GELU).
+ * Operand layouts: a_mn = 0: A(m, k) = A[m * lda + k] (K-contiguous); a_mn = 1:
+ * A(m, k) = A[k * lda + m] (MN-contiguous); likewise b_mn for B(k, n) = B[n * ldb + k] or
+ * B[k * ldb + n]. Implemented: (a_mn, b_mn) = (0, 0) input gradients G W^T, (0, 1) forward
+ * products X W, (1, 1) weight gradients X^T G; (1, 0) returns TP_ERR_UNSUPPORTED.
+ * N % 8 == 0; lda, ldb, ldc multiples of 8 and at least the contiguous extent; every operand
+ * below 2032 MiB. accumulate (0/1) only with TP_EPI_STORE; bias bf16 [N] or NULL (not with
+ * TP_EPI_DGELU, whose aux is U [M, ldc]). ws: with TP_EPI_STORE and ws_bytes >=
+ * tp_gemm_bf16_workspace(...) the call may split K (fp32 partials in ws, summed in a fixed
+ * order); otherwise ws is unused and may be NULL. M, N or K = 0: C is written as the epilogue of
+ * a zero product (K = 0), or nothing happens (M or N = 0). */
 typedef enum tp_epilogue {
     TP_EPI_STORE = 0,      /* C = P (+ bias[n]) (+ C if accumulate) */
     TP_EPI_BIAS_GELU = 1,  /* C = P (+ bias[n]) (the pre-activation U), C2 = GeLU(C) (erf form) */
     TP_EPI_DGELU = 2       /* C = P * GeLU'(aux[m, n]) (aux = U, row stride ldc) */
 } tp_epilogue;
 
+size_t tp_gemm_bf16_workspace(int M, int N, int K);
+tp_status tp_gemm_bf16(int M, int N, int K, const void* A, int lda, int a_mn, const void* B, int ldb,
+                       int b_mn, int epi, void* C, void* C2, int ldc, const void* bias, const void* aux,
+                       int accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * fp8 GEMMs for the layer shard (8-bit E4M3 operands, fp32 accumulation, bf16 outputs).
+ * The pages train in 16-bit floating point with dynamic loss scaling ("Megatron-LM, annotated",
+ * §4.2 Training optimization and hyperparameters) and define no 8-bit format; the scheme here is
+ * this library's own. Format: OCP E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * largest finite 448; 0x7F/0xFF are NaN; no infinities).
+ * ------------------------------------------------------------------------------------------- */
 /* Per-tensor quantisation of x [rows, cols] (row stride ldx, dt = TP_BF16 or TP_F32):
  *   amax = max |x|; e = the largest integer with amax * 2^e <= 448 (0 when amax is 0 or not
  *   finite), clamped to [-126, 126]; code = E4M3(x * 2^e), round to nearest even, saturating

@@ -74,7 +74,7 @@ def xent_shard_stats(X, E_r, targets, t, r, Vreal, mask_padding=False):
     owned = (local >= 0) & (local < Vt)
     n = np.arange(X.shape[0])
     tgt = np.where(owned, y[n, np.clip(local, 0, Vt - 1)], 0.0)
-    return {"max": m, "sumexp": s, "tgt": tgt, "argmax": y.argmax(axis=1) + col0}
+    return {"max": m, "sumexp": s, "tgt": tgt, "argmax": y.argmax(axis=1) + col0, "logits": y}
 
 
 def xent_combine(maxes, sumexps, tgts):

@@ -84,6 +84,8 @@ SIGNATURES = {
     "tp_layernorm_bwd": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
     "tp_colsum_workspace": (_z, [_i, _i, _i]),
     "tp_colsum": (_i, [_i, _i, _i, _p, _p, _i, _p, _z, _p]),
+    "tp_gemm_bf16_workspace": (_z, [_i, _i, _i]),
+    "tp_gemm_bf16": (_i, [_i, _i, _i, _p, _i, _i, _p, _i, _i, _i, _p, _p, _i, _p, _p, _i, _p, _z, _p]),
     "tp_fp8_quantize_workspace": (_z, [_i, _i]),
     "tp_fp8_quantize": (_i, [_i, _i, _i, _p, _i, _p, _i, _p, _i, _p, _p, _p, _z, _p]),
     "tp_gemm_fp8_workspace": (_z, [_i, _i, _i]),
@@ -272,6 +274,16 @@ def tp_colsum_workspace(T, n, dt):
 
 def tp_colsum(T, n, dt, G, out, accumulate, ws, ws_bytes, stream=None):
     _check(lib.tp_colsum(T, n, _dt(dt), _ptr(G), _ptr(out), accumulate, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tp_gemm_bf16_workspace(M, N, K):
+    return lib.tp_gemm_bf16_workspace(M, N, K)
+
+
+def tp_gemm_bf16(M, N, K, A, lda, a_mn, B, ldb, b_mn, epi, C_, C2, ldc, bias, aux, accumulate, ws, ws_bytes,
+                 stream=None):
+    _check(lib.tp_gemm_bf16(M, N, K, _ptr(A), lda, a_mn, _ptr(B), ldb, b_mn, epi, _ptr(C_), _ptr(C2), ldc,
+                            _ptr(bias), _ptr(aux), accumulate, _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def tp_fp8_quantize_workspace(rows, cols):

@@ -9,7 +9,6 @@
 #include <algorithm>
 #include <cmath>
 #include <initializer_list>
-#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -43,83 +42,6 @@ tp_status ok() {
     } while (0)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-// A second stream per device for work that can run beside the caller's stream inside one call
-// (column sums, split-K reductions and a weight-gradient GEMM next to GEMMs that leave CUs idle).
-// Default priority. Work goes to it after an event recorded on the caller's stream (fork), and the
-// caller's stream waits for an event recorded after the last of it (join) before the call
-// returns, so every entry point keeps single-stream semantics; both steps are an event record and
-// a stream wait. The stream and its events are created on a device's first such call. While the
-// caller's stream is being captured into a graph, nothing is forked: the call runs all of its work
-// on the caller's stream (graph replays of the forked form measured ~60 us slower per layer step
-// than eager launches; the single-stream form replays at eager speed). Calls that use the second
-// stream are serialised on the host by a mutex (the events are reused).
-constexpr int kMaxDevices = 64;
-struct SideStream {
-    hipStream_t s = nullptr;
-    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
-};
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
-
-// The current device's side stream, created on first use; nullptr while `caller` is capturing.
-hipError_t side_stream(hipStream_t caller, SideStream*& out) {
-    out = nullptr;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(caller, &cs) != hipSuccess) {
-        (void)hipGetLastError();   // a query refused during a capture: stay on the caller's stream
-        return hipSuccess;
-    }
-    if (cs != hipStreamCaptureStatusNone) return hipSuccess;
-    SideStream& sd = g_side[dev];
-    if (!sd.s) {
-        if ((e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking)) != hipSuccess) return e;
-        for (hipEvent_t& ev : sd.ev)
-            // device-scope fences only: both streams run on this device (a system-scope fence,
-            // the default, costs a cache writeback at every fork and join)
-            if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence)) != hipSuccess)
-                return e;
-    }
-    out = &sd;
-    return hipSuccess;
-}
-
-// Fork/join of the side stream within one call. side() is where side work goes: the side stream
-// once forked, else the caller's stream. A call that returns early after a fork (an error) still
-// joins, so a graph capture is never left with an unjoined branch.
-class SideFork {
-  public:
-    SideFork(SideStream* sd, hipStream_t caller) : sd_(sd), caller_(caller) {}
-    SideFork(const SideFork&) = delete;
-    SideFork& operator=(const SideFork&) = delete;
-    ~SideFork() { (void)join(); }
-    hipStream_t side() const { return sd_ ? sd_->s : caller_; }
-    // the side stream waits for the caller's work so far (event slot 0, 1 or 3)
-    hipError_t fork(int slot) {
-        if (!sd_) return hipSuccess;
-        forked_ = true;
-        return after(slot, caller_, sd_->s);
-    }
-    // the caller's stream waits for all side work
-    hipError_t join() {
-        if (!forked_) return hipSuccess;
-        forked_ = false;
-        return after(2, sd_->s, caller_);
-    }
-
-  private:
-    hipError_t after(int slot, hipStream_t from, hipStream_t to) {
-        hipError_t e = hipEventRecord(sd_->ev[slot], from);
-        return e != hipSuccess ? e : hipStreamWaitEvent(to, sd_->ev[slot], 0);
-    }
-    SideStream* sd_;
-    hipStream_t caller_;
-    bool forked_ = false;
-};
 
 // required pointer: non-null and 16-byte aligned
 #define NEED(p)                                                                                      \
@@ -345,41 +267,23 @@ tp_status tp_mlp_shard_bwd(int T, int h, int ffn, int t, int r, tp_dtype dt, con
     void* partB = base + w.dU;
     void* partA = base + w.dU + w.partB;
     float* colp = (float*)(base + w.dU + w.partB + w.partA);
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream* sd = nullptr;
-    HIP_TRY(side_stream(stream, sd), "tp_mlp_shard_bwd: side stream");
-    SideFork side(sd, stream);
     // dU = (G B_r^T) * GeLU'(U_r)
     GemmReq g = req(T, Ft, h, G, h, 0, B_r, h, 0, EPI_DGELU, dU, Ft);
     g.aux = U_r;
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_mlp_shard_bwd: dU GEMM");
-    // side: db1 = column sums of dU, beside the dB GEMM (whose 216 tiles leave CUs free)
-    HIP_TRY(side.fork(0), "tp_mlp_shard_bwd: fork");
-    if (db1_r) HIP_TRY(colsum(dt == TP_BF16, T, Ft, dU, db1_r, accumulate, colp, side.side()), "tp_mlp_shard_bwd: db1");
-    // dB_r = Y_r^T G; its split-K reduction on the side stream, beside the dA GEMM
+    // db1 = column sums of dU
+    if (db1_r) HIP_TRY(colsum(dt == TP_BF16, T, Ft, dU, db1_r, accumulate, colp, stream), "tp_mlp_shard_bwd: db1");
+    // dB_r = Y_r^T G
     g = req(Ft, h, T, Y_r, Ft, 1, G, h, 1, EPI_STORE, dB_r, h);
     g.accumulate = accumulate;
-    g.defer_reduce = 1;
     HIP_TRY(run_gemm(dt, g, true, partB, stream), "tp_mlp_shard_bwd: dB GEMM");
-    if (dt == TP_BF16) {
-        HIP_TRY(side.fork(1), "tp_mlp_shard_bwd: fork");
-        HIP_TRY(gemm_splitk_reduce(g, plan_gemm_bf16(g.M, g.N, g.K, true), partB, side.side()),
-                "tp_mlp_shard_bwd: dB reduction");
-    }
-    // dA_r = X^T dU; its split-K reduction on the side stream, beside the dX GEMM
+    // dA_r = X^T dU
     g = req(h, Ft, T, X, h, 1, dU, Ft, 1, EPI_STORE, dA_r, Ft);
     g.accumulate = accumulate;
-    g.defer_reduce = 1;
     HIP_TRY(run_gemm(dt, g, true, partA, stream), "tp_mlp_shard_bwd: dA GEMM");
-    if (dt == TP_BF16) {
-        HIP_TRY(side.fork(3), "tp_mlp_shard_bwd: fork");
-        HIP_TRY(gemm_splitk_reduce(g, plan_gemm_bf16(g.M, g.N, g.K, true), partA, side.side()),
-                "tp_mlp_shard_bwd: dA reduction");
-    }
     // dX_r = dU A_r^T
     g = req(T, h, Ft, dU, Ft, 0, A_r, Ft, 0, EPI_STORE, dX_r, h);
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_mlp_shard_bwd: dX GEMM");
-    HIP_TRY(side.join(), "tp_mlp_shard_bwd: join");
     return ok();
 }
 
@@ -442,37 +346,25 @@ tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dty
     void* partWo = base + w.dO + w.D + w.dQKV;
     void* partWqkv = base + w.dO + w.D + w.dQKV + w.partWo;
     float* colp = (float*)(base + w.dO + w.D + w.dQKV + w.partWo + w.partWqkv);
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream* sd = nullptr;
-    HIP_TRY(side_stream(stream, sd), "tp_attn_shard_bwd: side stream");
-    SideFork side(sd, stream);
-    // side: dWo_r = O_r^T G (needs neither dO nor the attention backward), beside the dO GEMM
-    // (whose 192 one-per-CU tiles leave room) and the attention kernels
-    HIP_TRY(side.fork(0), "tp_attn_shard_bwd: fork");
     // dO = G Wo_r^T
     GemmReq g = req(T, h_t, h, G, h, 0, Wo_r, h, 0, EPI_STORE, dO, h_t);
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_bwd: dO GEMM");
+    // dWo_r = O_r^T G
     g = req(h_t, h, T, O_r, h_t, 1, G, h, 1, EPI_STORE, dWo_r, h);
     g.accumulate = accumulate;
-    HIP_TRY(run_gemm(dt, g, true, partWo, side.side()), "tp_attn_shard_bwd: dWo GEMM");
+    HIP_TRY(run_gemm(dt, g, true, partWo, stream), "tp_attn_shard_bwd: dWo GEMM");
     if (T > 0)
         HIP_TRY(attn_bwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, dO, Dv, dQKV, dp, stream),
                 "tp_attn_shard_bwd: attention backward");
-    // side: dbqkv = column sums of dQKV, beside the dWqkv GEMM
-    HIP_TRY(side.fork(1), "tp_attn_shard_bwd: fork");
-    if (dbqkv_r) HIP_TRY(colsum(1, T, 3 * h_t, dQKV, dbqkv_r, accumulate, colp, side.side()), "tp_attn_shard_bwd: dbqkv");
-    // dWqkv_r = Xn^T dQKV; its split-K reduction on the side stream, beside the dXn GEMM
+    // dbqkv = column sums of dQKV
+    if (dbqkv_r) HIP_TRY(colsum(1, T, 3 * h_t, dQKV, dbqkv_r, accumulate, colp, stream), "tp_attn_shard_bwd: dbqkv");
+    // dWqkv_r = Xn^T dQKV
     g = req(h, 3 * h_t, T, Xn, h, 1, dQKV, 3 * h_t, 1, EPI_STORE, dWqkv_r, 3 * h_t);
     g.accumulate = accumulate;
-    g.defer_reduce = 1;
     HIP_TRY(run_gemm(dt, g, true, partWqkv, stream), "tp_attn_shard_bwd: dWqkv GEMM");
-    HIP_TRY(side.fork(3), "tp_attn_shard_bwd: fork");
-    HIP_TRY(gemm_splitk_reduce(g, plan_gemm_bf16(g.M, g.N, g.K, true), partWqkv, side.side()),
-            "tp_attn_shard_bwd: dWqkv reduction");
     // dXn_r = dQKV Wqkv_r^T
     g = req(T, h, 3 * h_t, dQKV, 3 * h_t, 0, Wqkv_r, 3 * h_t, 0, EPI_STORE, dXn_r, h);
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_bwd: dXn GEMM");
-    HIP_TRY(side.join(), "tp_attn_shard_bwd: join");
     return ok();
 }
 
@@ -560,6 +452,8 @@ tp_status tp_vocab_xent_shard_bwd(int N, int h, int Vpad, int Vreal, int t, int 
     if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
     if (need > 0) NEED(ws);
     const int ldd = (int)xent_bwd_ld(N);
+    // the two copies of the logits gradient are GEMM operands too (steps 2 and 3)
+    if ((st = check_operands(fn, 2, {(size_t)N * Vt, (size_t)Vt * ldd})) != TP_OK) return st;
     void* D = ws;
     void* DT = (char*)ws + al256((size_t)Vt * ldd * 2);
     GemmReq g;
@@ -793,6 +687,51 @@ tp_status tp_embedding_shard_bwd(int N, int h, int Vpad, int t, int r, tp_dtype 
     if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
     NEED(ws);
     HIP_TRY(embedding_bwd(dt == TP_BF16, N, h, Vpad / t, r, ids, dX, dE_r, accumulate, ws, stream), fn);
+    return ok();
+}
+
+/* ---- the bf16 GEMM on its own ---- */
+
+size_t tp_gemm_bf16_workspace(int M, int N, int K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return al256(split_ws_bytes(plan_gemm_bf16(M, N, K, true), M, N));
+}
+
+tp_status tp_gemm_bf16(int M, int N, int K, const void* A, int lda, int a_mn, const void* B, int ldb, int b_mn,
+                       int epi, void* C, void* C2, int ldc, const void* bias, const void* aux, int accumulate,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "tp_gemm_bf16";
+    if (M < 0 || N < 0 || K < 0) return fail(TP_ERR_SHAPE, "%s: M=%d N=%d K=%d must be >= 0", fn, M, N, K);
+    if (N % 8 != 0) return fail(TP_ERR_SHAPE, "%s: N=%d must be a multiple of 8", fn, N);
+    if ((a_mn != 0 && a_mn != 1) || (b_mn != 0 && b_mn != 1))
+        return fail(TP_ERR_ARG, "%s: a_mn=%d, b_mn=%d must be 0 or 1", fn, a_mn, b_mn);
+    if (a_mn && !b_mn) return fail(TP_ERR_UNSUPPORTED, "%s: A MN-contiguous with B K-contiguous", fn);
+    const int a_ext = a_mn ? M : K, b_ext = b_mn ? N : K;
+    if (lda < a_ext || lda % 8 != 0 || ldb < b_ext || ldb % 8 != 0)
+        return fail(TP_ERR_SHAPE, "%s: lda=%d, ldb=%d must be multiples of 8 and >= %d, %d", fn, lda, ldb, a_ext, b_ext);
+    if (ldc < N || ldc % 8 != 0) return fail(TP_ERR_SHAPE, "%s: ldc=%d must be >= N and a multiple of 8", fn, ldc);
+    if (epi != TP_EPI_STORE && epi != TP_EPI_BIAS_GELU && epi != TP_EPI_DGELU)
+        return fail(TP_ERR_ARG, "%s: unknown epilogue %d", fn, epi);
+    // epilogues per layout: the forward products carry bias + GeLU, the input gradients GeLU'
+    if ((epi == TP_EPI_BIAS_GELU && !(!a_mn && b_mn)) || (epi == TP_EPI_DGELU && !(!a_mn && !b_mn)))
+        return fail(TP_ERR_UNSUPPORTED, "%s: epilogue %d with layout (a_mn=%d, b_mn=%d)", fn, epi, a_mn, b_mn);
+    if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_ARG, "%s: accumulate=%d must be 0 or 1", fn, accumulate);
+    if (accumulate && epi != TP_EPI_STORE) return fail(TP_ERR_ARG, "%s: accumulate needs TP_EPI_STORE", fn);
+    NEED(A); NEED(B); NEED(C); OPT(bias);
+    if (epi == TP_EPI_BIAS_GELU) NEED(C2);
+    if (epi == TP_EPI_DGELU) {
+        NEED(aux);
+        if (bias) return fail(TP_ERR_ARG, "%s: TP_EPI_DGELU takes no bias", fn);
+    }
+    tp_status st = check_operands(fn, 2, {(size_t)(a_mn ? K : M) * lda, (size_t)(b_mn ? K : N) * ldb});
+    if (st != TP_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    const size_t need = tp_gemm_bf16_workspace(M, N, K);
+    const bool split_ok = epi == TP_EPI_STORE && need > 0 && ws && aligned16(ws) && ws_bytes >= need;
+    GemmReq g = req(M, N, K, A, lda, a_mn, B, ldb, b_mn,
+                    epi == TP_EPI_STORE ? EPI_STORE : epi == TP_EPI_BIAS_GELU ? EPI_BIAS_GELU : EPI_DGELU, C, ldc);
+    g.out2 = C2; g.bias = bias; g.aux = aux; g.accumulate = accumulate;
+    HIP_TRY(gemm_bf16(g, plan_gemm_bf16(M, N, K, split_ok), split_ok ? ws : nullptr, stream), fn);
     return ok();
 }
 

@@ -61,7 +61,7 @@ static hipError_t gemm_run(const GemmReq& r, const GemmPlan& p, void* ws, hipStr
             if (r.epi != EPI_STORE || ws == nullptr) return hipErrorInvalidValue;
             EpiPartial e{(float*)ws, r.N, (size_t)r.M * r.N, 0};
             hipError_t err = launch_plan<LA, LB>(r, p, e, st);
-            if (err != hipSuccess || r.defer_reduce) return err;
+            if (err != hipSuccess) return err;
             return launch_splitk_reduce(r, p, ws, st);
         }
         return hipErrorInvalidValue;

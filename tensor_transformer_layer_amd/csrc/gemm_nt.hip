@@ -6,7 +6,4 @@ hipError_t gemm_bf16_nt(const GemmReq& r, const GemmPlan& p, void* ws, hipStream
                     (1 << EPI_STORE) | (1 << EPI_DGELU) | (1 << EPI_STORE_T) | (1 << EPI_XENT) |
                         (1 << EPI_XENT_GRAD)>(r, p, ws, st);
 }
-hipError_t gemm_splitk_reduce(const GemmReq& r, const GemmPlan& p, const void* ws, hipStream_t st) {
-    return launch_splitk_reduce(r, p, ws, st);
-}
 }  // namespace tp

@@ -34,9 +34,6 @@ struct GemmReq {
     const float* stat_m; const float* stat_s; const float* dloss; int ld2;
     // fp8 GEMM: device pointers to the per-tensor descales of A and B
     const float* descale_a; const float* descale_b;
-    // split-K plans: 1 = leave the fp32 partials in the workspace; gemm_splitk_reduce() finishes
-    // them (possibly on another stream)
-    int defer_reduce;
 };
 
 struct GemmPlan {
@@ -55,9 +52,6 @@ size_t split_ws_bytes(const GemmPlan& p, int M, int N);
 // Launch one bf16 GEMM (+ split-K reduction if the plan has splits). ws must hold
 // split_ws_bytes(plan) bytes when plan.splits > 1.
 hipError_t gemm_bf16(const GemmReq& r, const GemmPlan& plan, void* ws, hipStream_t st);
-// The split-K reduction of a deferred request: out = sum of the plan's partials in ws (+ bias)
-// (+ out if accumulate), bf16. No-op for plans without splits.
-hipError_t gemm_splitk_reduce(const GemmReq& r, const GemmPlan& plan, const void* ws, hipStream_t st);
 // Launch one fp32 SIMT GEMM.
 hipError_t gemm_f32(const GemmReq& r, hipStream_t st);
 

@@ -240,3 +240,14 @@ def test_operand_size_limit():
     assert xent(T + 8, 3072, 51200, 50257, 8, 0, tp.TP_BF16, 0, *([FAKE] * 7), FAKE, 1 << 40, None) == tp.TP_ERR_UNSUPPORTED
     # E_r of 2032 MiB: Vpad / t rows of h
     assert xent(16, 8192, 130048 * 8, 100, 8, 0, tp.TP_BF16, 0, *([FAKE] * 7), FAKE, 1 << 40, None) == tp.TP_ERR_UNSUPPORTED
+
+
+def test_vocab_bwd_logits_gradient_size_limit():
+    """The backward's two copies of the logits gradient ([N, V_t] and [V_t, N] bf16) are GEMM
+    operands too: a shard whose X and E_r are small but whose N x V_t gradient reaches 2032 MiB is
+    refused on the host before any launch."""
+    b = tp.lib.tp_vocab_xent_shard_bwd
+    N, h, Vt, t = 8128, 8, 131072, 8          # N * V_t * 2 bytes = 2032 MiB exactly
+    args = (h, Vt * t, 100, t, 0, tp.TP_BF16, 0, *([FAKE] * 8), 0, FAKE, 1 << 40, None)
+    assert b(N, *args) == tp.TP_ERR_UNSUPPORTED
+    assert "2032 MiB" in tp.tp_last_error()

@@ -14,7 +14,7 @@ import torch
 import oracle
 import oracle.fp8 as f8
 import tp_synth
-from tests.gpu_util import DEV, dev, empty, host, rel_l2, say, ws
+from tests.gpu_util import DEV, dev, empty, host, rel_l2, within, say, ws
 
 pytestmark = pytest.mark.gpu
 tp = pytest.importorskip("tensor_transformer_layer_amd")
@@ -150,7 +150,7 @@ def test_gemm_fp8_store(M, N, K):
     got = run_gemm(ca, da, cb, db, M, N, K, tp.TP_EPI_STORE)
     e = rel_l2(got, ref)
     say(f"  rel_l2={e:.2e}")
-    assert e <= TOL
+    assert within(e, TOL)
     # bias + accumulate into a padded output
     bias = tp_synth.normal(901, 1, (N,), 0.5, "bf16")
     C0 = np.zeros((M, N + 8))
@@ -158,7 +158,7 @@ def test_gemm_fp8_store(M, N, K):
     got = run_gemm(ca, da, cb, db, M, N, K, tp.TP_EPI_STORE, bias=bias, C0=C0, accumulate=1, ldc=N + 8)
     e = rel_l2(got, ref + bias[None, :] + C0[:, :N])
     say(f"  bias+accumulate rel_l2={e:.2e}")
-    assert e <= TOL
+    assert within(e, TOL)
 
 
 def test_gemm_fp8_epilogues():
@@ -170,12 +170,12 @@ def test_gemm_fp8_epilogues():
     say("[fp8] gemm bias+gelu")
     U, Y = run_gemm(ca, da, cb, db, M, N, K, tp.TP_EPI_BIAS_GELU, bias=bias)
     Uref = P + bias[None, :]
-    assert rel_l2(U, Uref) <= TOL
-    assert rel_l2(Y, oracle.gelu(Uref)) <= TOL
+    assert within(rel_l2(U, Uref), TOL)
+    assert within(rel_l2(Y, oracle.gelu(Uref)), TOL)
     say("[fp8] gemm dgelu")
     aux = tp_synth.normal(912, 1, (M, N), 1.0, "bf16")
     dU = run_gemm(ca, da, cb, db, M, N, K, tp.TP_EPI_DGELU, aux=aux)
-    assert rel_l2(dU, P * oracle.gelu_grad(aux)) <= TOL
+    assert within(rel_l2(dU, P * oracle.gelu_grad(aux)), TOL)
 
 
 def test_gemm_fp8_split_k_matches_unsplit_and_is_deterministic():
@@ -190,7 +190,7 @@ def test_gemm_fp8_split_k_matches_unsplit_and_is_deterministic():
     b = run_gemm(ca, da, cb, db, M, N, K, tp.TP_EPI_STORE, use_ws=True)
     c = run_gemm(ca, da, cb, db, M, N, K, tp.TP_EPI_STORE, use_ws=False)
     assert np.array_equal(a, b)
-    assert rel_l2(a, ref) <= TOL and rel_l2(c, ref) <= TOL
+    assert within(rel_l2(a, ref) <= TOL and rel_l2(c, ref), TOL)
 
 
 def test_gemm_fp8_zero_k_and_empty():
@@ -237,4 +237,4 @@ def test_gemm_fp8_full_size_sampled(name, M, N, K, epi):
         ref = oracle.gelu(ref + bias[None, :])
     e = rel_l2(out[rows], ref)
     say(f"  sampled rel_l2={e:.2e}")
-    assert e <= TOL
+    assert within(e, TOL)

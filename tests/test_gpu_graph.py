@@ -1,6 +1,6 @@
 """The layer step captured into a HIP graph and replayed: every replay must reproduce the eager
-step bit for bit (under capture the library launches only kernels, all on the caller's stream:
-no allocation, no memset, no synchronisation, no fork onto its second stream), with
+step bit for bit (the library launches only kernels, all on the caller's stream: no
+allocation, no memset, no synchronisation, no stream or event of its own), with
 eager work and synchronisations between the replays. Dropout is on, so the Philox draws and the
 attention keep-bit mask run under capture too."""
 import numpy as np
@@ -79,7 +79,7 @@ graph.replay()
 torch.cuda.synchronize()
 names = %r
 got = {k: getattr(sh, k).clone() for k in names}
-sh.step(x, G, *sums)           # eager: creates and uses the second stream
+sh.step(x, G, *sums)           # eager, after the replay
 torch.cuda.synchronize()
 bad = [k for k in names if not torch.equal(getattr(sh, k), got[k])]
 print("mismatch:", bad, flush=True)
@@ -88,10 +88,9 @@ sys.exit(1 if bad else 0)
 
 
 def test_first_backward_call_under_capture():
-    """A process whose first backward call is made while its stream is being captured: the call
-    creates nothing and runs all of its work on the captured stream; the replay equals the eager
-    step run afterwards (which creates the second stream and forks onto it). Fresh process: the
-    second stream is per process and per device."""
+    """A process whose first backward call is made while its stream is being captured: the
+    library keeps no per-process state that a first call would have to create, so the replay
+    equals the eager step run afterwards. Fresh process, so that no earlier call has run."""
     import os
     import subprocess
     import sys

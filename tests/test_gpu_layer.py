@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import tp_synth
-from tests.gpu_util import rel_l2, say
+from tests.gpu_util import rel_l2, within, say
 
 pytestmark = pytest.mark.gpu
 tp = pytest.importorskip("tensor_transformer_layer_amd")
@@ -73,7 +73,7 @@ def check_every_output(p, b, s, h, heads, ffn, t, tag):
             errs[f"{k}[{r}]"] = rel_l2(host(getattr(sh, k)), ref)
     say(f"[layer] {tag} b={b} s={s} h={h} t={t}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     for k, e in errs.items():
-        assert e <= 1e-2, (k, e)
+        assert within(e, 1e-2), (k, e)
 
 
 @pytest.mark.parametrize("b,s,h,heads,ffn,t", [(2, 160, 384, 4, 1536, 2), (1, 96, 256, 4, 1024, 2)])
@@ -127,7 +127,7 @@ def check_step_rank0(p, b, s, h, heads, ffn, t, tag):
         errs[k] = rel_l2(host(getattr(sh0, k)), ref)
     say(f"[layer.step] {tag}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     for k, e in errs.items():
-        assert e <= 1e-2, (k, e)
+        assert within(e, 1e-2), (k, e)
 
 
 def test_layer_step_method_rank0():
@@ -173,7 +173,7 @@ def test_layer_step_dropout_every_output():
             errs[f"{k}[{r}]"] = rel_l2(host(getattr(sh, k)), ref)
     say("[layer+drop] " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     for k, e in errs.items():
-        assert e <= 1e-2, (k, e)
+        assert within(e, 1e-2), (k, e)
 
 
 @pytest.mark.parametrize("drop", [None, DROP])

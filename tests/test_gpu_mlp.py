@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import tp_synth
-from tests.gpu_util import TP_DT, dev, empty, host, rel_l2, say, ws
+from tests.gpu_util import TP_DT, dev, empty, host, rel_l2, within, say, ws
 
 pytestmark = pytest.mark.gpu
 tp = pytest.importorskip("tensor_transformer_layer_amd")
@@ -70,7 +70,7 @@ def check_mlp(inp, t, dtype, label):
     errs = {k: rel_l2(got[k], want[k]) for k in want}
     say(f"[mlp] {label}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for k, e in errs.items():
-        assert e <= tol, (label, k, e)
+        assert within(e, tol), (label, k, e)
     return ranks, sums
 
 
@@ -171,4 +171,4 @@ def test_mlp_8p3b_shape_rank0_sampled():
     errs["dB"] = rel_l2(host(dB)[ib], oracle.gelu(X @ A_r[:, ib]).T @ G)
     say("[mlp] 8.3B rank 0: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for k, e in errs.items():
-        assert e <= 1e-2, (k, e)
+        assert within(e, 1e-2), (k, e)
