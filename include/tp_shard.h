@@ -185,6 +185,24 @@ tp_status tp_vocab_xent_shard_fwd(int N, int h, int Vpad, int Vreal, int t, int 
                                   const int32_t* targets, float* max_r, float* sumexp_r, float* tgt_r,
                                   int32_t* argmax_r, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* tp_vocab_xent_shard_fwd without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * kernels and results, with the per-(tile, token) partials in a library-owned scratch array of
+ * TP_XENT_NOALLOC_SCRATCH_BYTES per device (allocated with the library's code object on a device's
+ * first use, held until the process ends). The call itself allocates nothing. A shape whose
+ * partials need more (tp_vocab_xent_shard_fwd_workspace bytes) is refused with
+ * TP_ERR_UNSUPPORTED before any launch: 8 MiB holds e.g. N = 8192 tokens at V_t = 6400 (3.7 MB)
+ * and up to ~18,000 tokens at that V_t. Every call on a device shares that device's array, which
+ * keeps the last call's contents; calls that overlap in time on one device (on different streams
+ * or host threads) race on it and must be serialised by the caller. */
+#define TP_XENT_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+size_t tp_vocab_xent_shard_fwd_noalloc_max_bytes(void);
+tp_status tp_vocab_xent_shard_fwd_noalloc(int N, int h, int Vpad, int Vreal, int t, int r,
+                                          tp_dtype dt, int mask_padding, const void* X,
+                                          const void* E_r, const int32_t* targets, float* max_r,
+                                          float* sumexp_r, float* tgt_r, int32_t* argmax_r,
+                                          hipStream_t stream);
+
 /* The rank's fp32 logits [N, V_t], stored. For verification of the fused statistics; not on the
  * hot path. It runs the same bf16 MFMA main loop as tp_vocab_xent_shard_fwd but with the
  * library's ordinary tile plan for the shape, not the fused call's tiles. Every tile shape sums

@@ -68,6 +68,8 @@ SIGNATURES = {
                                _p, _z, _p]),
     "tp_vocab_xent_shard_fwd_workspace": (_z, [_i, _i, _i, _i, _i]),
     "tp_vocab_xent_shard_fwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _z, _p]),
+    "tp_vocab_xent_shard_fwd_noalloc_max_bytes": (_z, []),
+    "tp_vocab_xent_shard_fwd_noalloc": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
     "tp_vocab_logits_shard": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p]),
     "tp_vocab_xent_combine": (_i, [_i, _i, _pp, _pp, _pp, _p, _p, _p, _p, _p]),
     "tp_vocab_xent_shard_bwd_workspace": (_z, [_i, _i, _i, _i, _i]),
@@ -191,6 +193,17 @@ def tp_vocab_xent_shard_fwd(N, h, Vpad, Vreal, t, r, dt, mask_padding, X, E_r, t
     _check(lib.tp_vocab_xent_shard_fwd(N, h, Vpad, Vreal, t, r, _dt(dt), mask_padding, _ptr(X), _ptr(E_r),
                                        _ptr(targets), _ptr(max_r), _ptr(sumexp_r), _ptr(tgt_r), _ptr(argmax_r),
                                        _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tp_vocab_xent_shard_fwd_noalloc_max_bytes():
+    return lib.tp_vocab_xent_shard_fwd_noalloc_max_bytes()
+
+
+def tp_vocab_xent_shard_fwd_noalloc(N, h, Vpad, Vreal, t, r, dt, mask_padding, X, E_r, targets, max_r, sumexp_r,
+                                    tgt_r, argmax_r, stream=None):
+    _check(lib.tp_vocab_xent_shard_fwd_noalloc(N, h, Vpad, Vreal, t, r, _dt(dt), mask_padding, _ptr(X), _ptr(E_r),
+                                               _ptr(targets), _ptr(max_r), _ptr(sumexp_r), _ptr(tgt_r),
+                                               _ptr(argmax_r), _stream(stream)))
 
 
 def tp_vocab_logits_shard(N, h, Vpad, t, r, dt, X, E_r, logits, stream=None):

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <initializer_list>
 #include <string>
@@ -375,25 +376,26 @@ size_t tp_vocab_xent_shard_fwd_workspace(int N, int h, int Vpad, int t, tp_dtype
     return xent_ws(N, h, Vpad / t);
 }
 
-tp_status tp_vocab_xent_shard_fwd(int N, int h, int Vpad, int Vreal, int t, int r, tp_dtype dt, int mask_padding,
-                                  const void* X, const void* E_r, const int32_t* targets, float* max_r,
-                                  float* sumexp_r, float* tgt_r, int32_t* argmax_r, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
-    const char* fn = "tp_vocab_xent_shard_fwd";
+// Argument checks shared by the two forms of the fused vocabulary call (workspace / library scratch).
+static tp_status check_xent_fwd(const char* fn, int N, int h, int Vpad, int Vreal, int t, int r, tp_dtype dt,
+                                int mask_padding, const void* X, const void* E_r, const int32_t* targets, float* max_r,
+                                float* sumexp_r, float* tgt_r, int32_t* argmax_r) {
     tp_status st = check_vocab(fn, N, h, Vpad, t, r, dt);
     if (st != TP_OK) return st;
     if (Vreal <= 0 || Vreal > Vpad) return fail(TP_ERR_SHAPE, "%s: Vreal=%d must be in [1, Vpad=%d]", fn, Vreal, Vpad);
     if (mask_padding != 0 && mask_padding != 1) return fail(TP_ERR_ARG, "%s: mask_padding=%d must be 0 or 1", fn, mask_padding);
     NEED(X); NEED(E_r); NEED(targets); NEED(max_r); NEED(sumexp_r); NEED(tgt_r); OPT(argmax_r);
-    const int Vt = Vpad / t;
-    size_t need = xent_ws(N, h, Vt);
-    if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
-    if (need > 0) NEED(ws);
-    if (N == 0) return ok();
-    // rows [0, main_rows) and [main_rows, Vt) of the shard; the tail's partials follow the main
-    // part's tile rows, so the merge reads the tiles in row order
+    return TP_OK;
+}
+
+// The fused logits GEMM over rows [0, main_rows) and [main_rows, Vt) of the shard, then the tile
+// merge; the tile partials go to `part` (xent_ws bytes). The tail's partials follow the main
+// part's tile rows, so the merge reads the tiles in row order.
+static tp_status launch_xent_fwd(const char* fn, int N, int h, int Vt, int Vreal, int r, int mask_padding,
+                                 const void* X, const void* E_r, const int32_t* targets, float* max_r, float* sumexp_r,
+                                 float* tgt_r, int32_t* argmax_r, void* part, hipStream_t stream) {
     const VocabPlan vp = plan_vocab(Vt, N, h);
-    GemmReq g = req(vp.main_rows, N, h, E_r, h, 0, X, h, 0, EPI_XENT, ws, 0);
+    GemmReq g = req(vp.main_rows, N, h, E_r, h, 0, X, h, 0, EPI_XENT, part, 0);
     g.targets = targets;
     g.col0 = r * Vt;
     g.Vreal = Vreal;
@@ -403,14 +405,86 @@ tp_status tp_vocab_xent_shard_fwd(int N, int h, int Vpad, int Vreal, int t, int 
         const int main_tiles = vp.main_rows / vp.main.bm;
         g.M = Vt - vp.main_rows;
         g.A = (const char*)E_r + (size_t)vp.main_rows * h * 2;
-        g.out = (char*)ws + (size_t)main_tiles * N * 16;
+        g.out = (char*)part + (size_t)main_tiles * N * 16;
         g.col0 = r * Vt + vp.main_rows;
         g.row0 = vp.main_rows;
         HIP_TRY(gemm_bf16(g, vp.tail, nullptr, stream), "tp_vocab_xent_shard_fwd: fused logits GEMM (last rows)");
     }
-    HIP_TRY(xent_merge(ws, vp.tiles_m, N, r * Vt, max_r, sumexp_r, tgt_r, argmax_r, stream),
+    HIP_TRY(xent_merge(part, vp.tiles_m, N, r * Vt, max_r, sumexp_r, tgt_r, argmax_r, stream),
             "tp_vocab_xent_shard_fwd: tile merge");
+    (void)fn;
     return ok();
+}
+
+tp_status tp_vocab_xent_shard_fwd(int N, int h, int Vpad, int Vreal, int t, int r, tp_dtype dt, int mask_padding,
+                                  const void* X, const void* E_r, const int32_t* targets, float* max_r,
+                                  float* sumexp_r, float* tgt_r, int32_t* argmax_r, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+    const char* fn = "tp_vocab_xent_shard_fwd";
+    tp_status st = check_xent_fwd(fn, N, h, Vpad, Vreal, t, r, dt, mask_padding, X, E_r, targets, max_r, sumexp_r,
+                                  tgt_r, argmax_r);
+    if (st != TP_OK) return st;
+    const int Vt = Vpad / t;
+    size_t need = xent_ws(N, h, Vt);
+    if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    if (need > 0) NEED(ws);
+    if (N == 0) return ok();
+    return launch_xent_fwd(fn, N, h, Vt, Vreal, r, mask_padding, X, E_r, targets, max_r, sumexp_r, tgt_r, argmax_r, ws,
+                           stream);
+}
+
+}  // extern "C"
+
+// Library-owned scratch for tp_vocab_xent_shard_fwd_noalloc: one copy per device, allocated with the
+// code object when the library is first used on that device and kept until the process ends. Host
+// code must not pass `tp_xent_scratch` itself to a kernel (in host code the name is a stand-in,
+// not a device address): the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char tp_xent_scratch[TP_XENT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_xent_scratch[kMaxDevices];
+
+// The current device's address of tp_xent_scratch (resolved on the first call on that device; a
+// race between two first calls resolves the same address twice).
+tp_status xent_scratch(const char* fn, void*& out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(TP_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+    void* p = g_xent_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(tp_xent_scratch)), "hipGetSymbolAddress(tp_xent_scratch)");
+        if (!p) return fail(TP_ERR_HIP, "%s: hipGetSymbolAddress returned NULL", fn);
+        g_xent_scratch[dev].store(p, std::memory_order_release);
+    }
+    out = p;
+    return TP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t tp_vocab_xent_shard_fwd_noalloc_max_bytes(void) { return TP_XENT_NOALLOC_SCRATCH_BYTES; }
+
+tp_status tp_vocab_xent_shard_fwd_noalloc(int N, int h, int Vpad, int Vreal, int t, int r, tp_dtype dt,
+                                          int mask_padding, const void* X, const void* E_r, const int32_t* targets,
+                                          float* max_r, float* sumexp_r, float* tgt_r, int32_t* argmax_r,
+                                          hipStream_t stream) {
+    const char* fn = "tp_vocab_xent_shard_fwd_noalloc";
+    tp_status st = check_xent_fwd(fn, N, h, Vpad, Vreal, t, r, dt, mask_padding, X, E_r, targets, max_r, sumexp_r,
+                                  tgt_r, argmax_r);
+    if (st != TP_OK) return st;
+    const int Vt = Vpad / t;
+    const size_t need = xent_ws(N, h, Vt);
+    if (need > TP_XENT_NOALLOC_SCRATCH_BYTES)
+        return fail(TP_ERR_UNSUPPORTED, "%s: the tile partials need %zu bytes, beyond the %zu-byte scratch (use "
+                    "tp_vocab_xent_shard_fwd with a workspace)", fn, need, (size_t)TP_XENT_NOALLOC_SCRATCH_BYTES);
+    if (N == 0) return ok();
+    void* part = nullptr;
+    if ((st = xent_scratch(fn, part)) != TP_OK) return st;
+    // every partial the merge reads is written by the GEMM of this call: nothing needs clearing
+    return launch_xent_fwd(fn, N, h, Vt, Vreal, r, mask_padding, X, E_r, targets, max_r, sumexp_r, tgt_r, argmax_r,
+                           part, stream);
 }
 
 tp_status tp_vocab_logits_shard(int N, int h, int Vpad, int t, int r, tp_dtype dt, const void* X, const void* E_r,

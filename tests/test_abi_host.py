@@ -251,3 +251,13 @@ def test_vocab_bwd_logits_gradient_size_limit():
     args = (h, Vt * t, 100, t, 0, tp.TP_BF16, 0, *([FAKE] * 8), 0, FAKE, 1 << 40, None)
     assert b(N, *args) == tp.TP_ERR_UNSUPPORTED
     assert "2032 MiB" in tp.tp_last_error()
+
+
+def test_xent_noalloc_refuses_beyond_scratch():
+    """The allocation-free vocabulary call refuses, before any launch, a shape whose tile partials
+    exceed its fixed scratch array (8 MiB): 65,536 tokens at V_t = 6400 need ~26 MB."""
+    assert tp.tp_vocab_xent_shard_fwd_noalloc_max_bytes() == 8 << 20
+    f = tp.lib.tp_vocab_xent_shard_fwd_noalloc
+    st = f(65536, 3072, 51200, 50257, 8, 0, tp.TP_BF16, 0, *([FAKE] * 7), None)
+    assert st == tp.TP_ERR_UNSUPPORTED and "scratch" in tp.tp_last_error()
+    assert f(64, 3072, 51200, 50257, 8, 9, tp.TP_BF16, 0, *([FAKE] * 7), None) == tp.TP_ERR_ARG   # r >= t
