@@ -158,6 +158,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the shader-clock sample (about 1.5 s of extra steps; for profiler runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="copy 512 MiB device-to-device once before the steps (calibrates HBM byte counters)")
     ap.add_argument("--vocab-bwd", action="store_true",
@@ -304,7 +306,8 @@ def main():
         per_step.append((a, b_))
     torch.cuda.synchronize()
     per_step = np.array([a.elapsed_time(b_) for a, b_ in per_step])
-    clock = sample_sclk(lambda: [layer_step() for _ in range(max(1, int(1500 / max(ms, 1e-3))))], torch)
+    clock = None if args.no_clock else sample_sclk(
+        lambda: [layer_step() for _ in range(max(1, int(1500 / max(ms, 1e-3))))], torch)
     roof = dominant_gemm_roofline(args, tp, torch, rank0, G, stream)
 
     fl_layer = layer_flops(B, S, H, heads, FFN, TP)
