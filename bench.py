@@ -178,6 +178,11 @@ def main():
                     help="add rank 0's vocabulary-parallel input-embedding lookup and its backward to the step")
     ap.add_argument("--graph", action="store_true",
                     help="capture the step into a HIP graph and time its replays (prints its own JSON line)")
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5],
+                    help="workload: 4 = the 8.3B layer shard (the metric, default); 1 = the fp32 MLP block (t=2), "
+                         "2 = the 1.2B attention shard (t=2), 3 = the 2.5B layer shard (t=4), 5 = the 8.3B "
+                         "vocabulary-parallel cross-entropy shard (t=8): rank 0's share, timed, with the worst "
+                         "element-wise error against the float64 oracle and the oracle's time in cpu_baseline")
     ap.add_argument("--heads", type=int, default=HEADS,
                     help="attention heads of the layer (the pages' 8.3B head-count sweep uses 16, 24, 32; the "
                          "FLOPs and all other shapes are unchanged, heads per rank = heads / 8)")
@@ -193,6 +198,8 @@ def main():
 
     if args.fp8:
         return bench_fp8(args, tp, torch)
+    if args.config != 4:
+        return bench_config(args, tp, torch)
     dev = "cuda:0"
     T = B * S
     Vt = VOCAB_PAD // TP
@@ -296,6 +303,21 @@ def main():
     # the rest of the hot path, timed on its own: the vocabulary shard's fused logits GEMM + CE
     # statistics and the loss merge
     xent_ms = timed(vocab_step, args.steps)
+    # the unfused form of the vocabulary statistics: a pass over rank 0's materialised fp32 logits
+    # (written once here, 210 MB), timed on its own (HBM-bound)
+    logits = torch.empty((T, Vt), dtype=torch.float32, device=dev)
+    tp.tp_vocab_logits_shard(T, H, VOCAB_PAD, TP, 0, tp.TP_BF16, Xv, E0, logits)
+    ux = tuple(torch.empty(T, dtype=torch.float32, device=dev) for _ in range(3))
+    uam = torch.empty(T, dtype=torch.int32, device=dev)
+
+    def stats_pass():
+        tp.tp_vocab_xent_stats_from_logits(T, VOCAB_PAD, VOCAB, TP, 0, 0, logits, Vt, tg, *ux, uam)
+
+    stats_pass()
+    pass_us = timed(stats_pass, args.steps) * 1e3
+    pass_bytes = T * Vt * 4 + T * 16
+    del logits
+    torch.cuda.empty_cache()
     # per-step spread: a second pass of as many layer steps, each bracketed by its own events
     per_step = []
     for _ in range(args.steps):
@@ -346,7 +368,13 @@ def main():
                        "frac": round(xent_tf * 1e12 / PEAK_BF16, 4),
                        "traffic": measured_traffic(),
                        "traffic_unit": "HBM bytes per call of the fused GEMM (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
-                                       "copy-calibrated), from the committed counter summary; null once stale"},
+                                       "copy-calibrated), from the committed counter summary; null once stale",
+                       "unfused_stats_pass": {
+                           "what": "the same per-token statistics from the materialised fp32 logits [8192 x 6400] "
+                                   "(tp_vocab_xent_stats_from_logits): one HBM pass, the form the fusion avoids",
+                           "us": round(pass_us, 2), "bytes": pass_bytes,
+                           "GB_per_s": round(pass_bytes / (pass_us * 1e-6) / 1e9, 1),
+                           "frac_of_8TB_per_s": round(pass_bytes / (pass_us * 1e-6) / PEAK_HBM, 4)}},
         "hot_path_ms": round(ms + xent_ms, 4),
         "roofline": roof,
         "clock": {"sclk_mhz_under_load": clock, "rocminfo": peak_info},
@@ -442,6 +470,202 @@ def dominant_gemm_roofline(args, tp, torch, rank0, G, stream):
             "traffic": measured_traffic(DOMINANT_TRAFFIC_FILE, KERNEL_SOURCES),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated), from the "
                             "committed counter summary; null once the kernel sources have changed"}
+
+
+def _timed_calls(torch, fn, warmup, steps):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b_.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b_) / steps
+
+
+def _cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except Exception:
+        return os.cpu_count()
+
+
+def _worst(pairs):
+    """Largest of (relative L2, max|err|/max|ref|) over the named (got, ref) pairs: (name, value)."""
+    worst = ("", 0.0)
+    for name, got, ref in pairs:
+        got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+        d = got - ref
+        e = max(float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300)),
+                float(np.abs(d).max() / max(np.abs(ref).max(), 1e-300)))
+        if e > worst[1]:
+            worst = (name, e)
+    return {"output": worst[0], "value": float(f"{worst[1]:.3g}")}
+
+
+def bench_config(args, tp, torch):
+    """Rank 0's share of one of the other workloads, timed like the default step (warm-up, then
+    HIP events around K back-to-back calls), reported on its own JSON line. The oracle leg (unless
+    --no-cpu-baseline) times the float64 oracle on the same work on the host cores and reports the
+    worst element-wise error of the timed call's outputs against it."""
+    import tp_synth
+    dev = "cuda:0"
+
+    def d(a, dt=torch.bfloat16):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+
+    n = args.config
+    t0 = time.perf_counter
+    out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "data": "synthetic (seeded, the workload's distributions)"}
+    if n == 1:
+        w = tp_synth.WORKLOADS["mlp_fp32_t2"]
+        inp = tp_synth.mlp_inputs(w.seed, w.T, w.h, w.ffn, "f32")
+        T, h, ffn, t = w.T, w.h, w.ffn, w.t
+        Ft = ffn // t
+        f32 = torch.float32
+        X, G = d(inp["X"], f32), d(inp["G"], f32)
+        A0, b0, B0 = d(inp["A"][:, :Ft], f32), d(inp["b1"][:Ft], f32), d(inp["B"][:Ft], f32)
+        U, Y, Z = (torch.empty((T, n_), dtype=f32, device=dev) for n_ in (Ft, Ft, h))
+        dX, dA, db1, dB = (torch.empty(sh, dtype=f32, device=dev) for sh in ((T, h), (h, Ft), (Ft,), (Ft, h)))
+        nb = tp.tp_mlp_shard_bwd_workspace(T, h, ffn, t, tp.TP_F32)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+
+        def call():
+            tp.tp_mlp_shard_fwd(T, h, ffn, t, 0, tp.TP_F32, X, A0, b0, B0, U, Y, Z)
+            tp.tp_mlp_shard_bwd(T, h, ffn, t, 0, tp.TP_F32, X, A0, B0, U, Y, G, dX, dA, db1, dB, 0, ws, nb)
+
+        fl = 3 * 2.0 * 2 * T * h * Ft
+        dtype, name = "f32", "MLP block shard (fp32), T=128, h=256, ffn=1024, t=2, rank 0, fwd+bwd"
+
+        def oracle_run():
+            import oracle
+            f = oracle.mlp_shard_fwd(inp["X"], inp["A"][:, :Ft], inp["b1"][:Ft], inp["B"][:Ft])
+            g = oracle.mlp_shard_bwd(inp["X"], inp["A"][:, :Ft], inp["B"][:Ft], f["U"], f["Y"], inp["G"])
+            return [("U", U, f["U"]), ("Y", Y, f["Y"]), ("Z_0", Z, f["Z"]), ("dX_0", dX, g["dX"]),
+                    ("dA_0", dA, g["dA"]), ("db1_0", db1, g["db1"]), ("dB_0", dB, g["dB"])]
+    elif n == 2:
+        w = tp_synth.WORKLOADS["attn_1p2b_t2"]
+        inp = tp_synth.attn_inputs(w.seed, w.b, w.s, w.h, "bf16")
+        b, s, h, heads, t = w.b, w.s, w.h, w.heads, w.t
+        T, ht = b * s, h // t
+        Xn, G = d(inp["Xn"]), d(inp["G"])
+        # rank 0's [Wq | Wk | Wv] columns of its heads and its rows of Wo
+        qcols = np.concatenate([np.arange(i * h, i * h + ht) for i in range(3)])
+        Wq, bq, Wo = d(inp["Wqkv"][:, qcols]), d(inp["bqkv"][qcols]), d(inp["Wo"][:ht])
+        QKV, O, Z = (torch.empty(sh, dtype=torch.bfloat16, device=dev) for sh in ((T, 3 * ht), (T, ht), (T, h)))
+        lse = torch.empty((b, heads // t, s), dtype=torch.float32, device=dev)
+        dXn, dWqkv, dbqkv, dWo = (torch.empty(sh, dtype=torch.bfloat16, device=dev)
+                                  for sh in ((T, h), (h, 3 * ht), (3 * ht,), (ht, h)))
+        nb = tp.tp_attn_shard_bwd_workspace(b, s, h, heads, t, tp.TP_BF16)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+        def call():
+            tp.tp_attn_shard_fwd(b, s, h, heads, t, 0, tp.TP_BF16, 1, Xn, Wq, bq, Wo, QKV, O, lse, Z)
+            tp.tp_attn_shard_bwd(b, s, h, heads, t, 0, tp.TP_BF16, 1, Xn, Wq, Wo, QKV, O, lse, G, dXn, dWqkv, dbqkv,
+                                 dWo, 0, ws, nb)
+
+        d_ = h // heads
+        fl = 3 * (2.0 * T * h * 3 * ht + 2.0 * T * ht * h + 4.0 * d_ * (s * (s + 1) // 2) * b * (heads // t))
+        dtype, name = "bf16", "1.2B-shape attention shard, t=2, rank 0, fwd+bwd (8 x 1024 tokens, 8 heads of 96)"
+
+        def oracle_run():
+            import oracle
+            Wq_, bq_, Wo_ = (oracle.qkv_shard(inp["Wqkv"], heads, t, 0), oracle.qkv_shard(inp["bqkv"], heads, t, 0),
+                             oracle.wo_shard(inp["Wo"], heads, t, 0))
+            f = oracle.attn_shard_fwd(inp["Xn"], Wq_, bq_, Wo_, b, s, heads // t)
+            g = oracle.attn_shard_bwd(inp["Xn"], Wq_, Wo_, f, inp["G"], b, s, heads // t)
+            return [("QKV", QKV, f["QKV"]), ("O", O, f["O"]), ("lse", lse, f["lse"]), ("Z_0", Z, f["Z"]),
+                    ("dXn_0", dXn, g["dXn"]), ("dWqkv_0", dWqkv, g["dWqkv"]), ("dbqkv_0", dbqkv, g["dbqkv"]),
+                    ("dWo_0", dWo, g["dWo"])]
+    elif n == 3:
+        from tensor_transformer_layer_amd.layer import LayerShard, rank_params
+        w = tp_synth.WORKLOADS["layer_2p5b_t4"]
+        p = tp_synth.layer_inputs(w.seed, w.b, w.s, w.h, w.ffn, "bf16")
+        b, s, h, heads, ffn, t = w.b, w.s, w.h, w.heads, w.ffn, w.t
+        T = b * s
+        x, G = d(p["x"]), d(p["G"])
+        shards = [LayerShard(b, s, h, heads, ffn, t, r, rank_params(p, heads, t, r, dev), dev) for r in range(t)]
+        sums = [torch.empty((T, h), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+        attn_sum, mlp_sum, dxn2_sum, dxn1_sum = sums
+        sh0 = shards[0]
+        sh0.combine([sh.attn_fwd(x) for sh in shards], None, None, attn_sum)
+        x1 = torch.empty_like(attn_sum)
+        sh0.combine([attn_sum], sh0.p["bo"], x, x1)
+        sh0.combine([sh.mlp_fwd(x1) for sh in shards], None, None, mlp_sum)
+        sh0.combine([sh.mlp_bwd(G) for sh in shards], None, None, dxn2_sum)
+        dx1 = sh0.ln2_bwd(dxn2_sum, G)
+        sh0.combine([sh.attn_bwd(dx1) for sh in shards], None, None, dxn1_sum)
+        torch.cuda.synchronize()
+        del shards
+        torch.cuda.empty_cache()
+
+        def call():
+            sh0.step(x, G, attn_sum, mlp_sum, dxn2_sum, dxn1_sum)
+
+        fl = layer_flops(b, s, h, heads, ffn, t)
+        fl_oracle = t * fl   # the oracle leg runs the whole split layer (every rank) to check rank 0's outputs
+        dtype, name = "bf16", "2.5B-shape layer shard, t=4, rank 0, fwd+bwd (8 x 1024 tokens, 5 heads of 96, 1920 MLP columns)"
+
+        def oracle_run():
+            import oracle
+            f = oracle.layer_split_fwd(p["x"], p, b, s, heads, t)
+            gr = oracle.layer_split_bwd(p["x"], p, f, p["G"], b, s, heads, t)
+            ht, Ft = h // t, ffn // t
+            qcols = np.concatenate([np.arange(i * h, i * h + ht) for i in range(3)])
+            return [("x2", sh0.x2, f["x2"]), ("dx", sh0.dx, gr["dx"]), ("dA_0", sh0.dA, gr["mlp"]["dA"][:, :Ft]),
+                    ("dB_0", sh0.dB, gr["mlp"]["dB"][:Ft]), ("db1_0", sh0.db1, gr["mlp"]["db1"][:Ft]),
+                    ("dWqkv_0", sh0.dWqkv, gr["attn"]["dWqkv"][:, qcols]), ("dWo_0", sh0.dWo, gr["attn"]["dWo"][:ht]),
+                    ("dln1_g", sh0.dln1_g, gr["dln1_g"]), ("dln2_g", sh0.dln2_g, gr["dln2_g"])]
+    else:
+        w = tp_synth.WORKLOADS["xent_8p3b_t8"]
+        inp = tp_synth.xent_inputs(w.seed, w.T, w.h, w.vocab, w.vocab_pad, "bf16")
+        N, h, Vpad, Vreal, t = w.T, w.h, w.vocab_pad, w.vocab, w.t
+        Vt = Vpad // t
+        X, E0 = d(inp["X"]), d(inp["E"][:Vt])
+        tg = torch.from_numpy(inp["targets"]).to(dev)
+        mx, se, tv = (torch.empty(N, dtype=torch.float32, device=dev) for _ in range(3))
+        am = torch.empty(N, dtype=torch.int32, device=dev)
+        nb = tp.tp_vocab_xent_shard_fwd_workspace(N, h, Vpad, t, tp.TP_BF16)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+        def call():
+            tp.tp_vocab_xent_shard_fwd(N, h, Vpad, Vreal, t, 0, tp.TP_BF16, 0, X, E0, tg, mx, se, tv, am, ws, nb)
+
+        fl = xent_flops(N, h, Vt)
+        dtype, name = "bf16", "8.3B vocabulary shard, t=8, rank 0: fused logits GEMM + per-token max/sum-exp/target/argmax (N=8192, h=3072, V_t=6400)"
+
+        def oracle_run():
+            import oracle
+            st = oracle.xent_shard_stats(inp["X"], inp["E"][:Vt], inp["targets"], t, 0, Vreal)
+            return [("max", mx, st["max"]), ("sumexp", se, st["sumexp"]), ("tgt", tv, st["tgt"])]
+    fl_oracle = locals().get("fl_oracle", fl)
+    ms = _timed_calls(torch, call, args.warmup, args.steps)
+    value = fl / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16 if dtype == "bf16" else 157.3e12
+    out.update({"metric": f"config {n} shard TFLOP/s, 1 GPU", "value": round(value, 3), "unit": "TFLOP/s",
+                "ms_per_step": round(ms, 4), "dtype": dtype, "config": {"workload": name},
+                "gflop": round(fl / 1e9, 3), "pct_peak": round(100 * value * 1e12 / peak, 2),
+                "peak_tflops": peak / 1e12})
+    if not args.no_cpu_baseline:
+        call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(3):
+            a = t0()
+            pairs = oracle_run()
+            times.append(t0() - a)
+        dt = float(np.median(times))
+        out["worst_error_vs_oracle"] = _worst([(k, g.detach().float().cpu().numpy(), r) for k, g, r in pairs])
+        what = ("the whole t-way split layer (every rank's work, to check rank 0's outputs)" if fl_oracle != fl
+                else "the same rank-0 work")
+        out["cpu_baseline"] = {"value": round(fl_oracle / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(_cores()),
+                               "kind": "oracle", "sample": f"{what} in float64 NumPy, median of 3 runs "
+                                                           f"({', '.join(f'{x:.2f}' for x in times)} s)"}
+    print(json.dumps(out), flush=True)
 
 
 def bench_graph(args, torch, step, heads, stream):

@@ -212,6 +212,20 @@ tp_status tp_vocab_xent_shard_fwd_noalloc(int N, int h, int Vpad, int Vreal, int
 tp_status tp_vocab_logits_shard(int N, int h, int Vpad, int t, int r, tp_dtype dt, const void* X,
                                 const void* E_r, float* logits, hipStream_t stream);
 
+/* The same per-token statistics as tp_vocab_xent_shard_fwd (max, sum of exponentials relative to
+ * it, target logit, argmax as a global index), computed from the rank's materialised fp32 logits
+ * [N, ld] (row n = token n, column v = the rank's vocabulary row v, as tp_vocab_logits_shard writes
+ * them): the unfused form that the pages contrast the fused call with ("Megatron-LM ..." digest
+ * §3.4, output embedding parallelism: gathering the b*s*v logits instead of b*s scalars). A pass
+ * over HBM: N * V_t * 4 bytes read, 16 bytes per token written. Max, argmax (lowest column on ties)
+ * and target logit are exact functions of the logits; the sum of exponentials is summed in its own
+ * order (within fp32 rounding of the fused call's). mask_padding as for the fused call.
+ * ld >= V_t, ld % 4 == 0; argmax_r may be NULL. */
+tp_status tp_vocab_xent_stats_from_logits(int N, int Vpad, int Vreal, int t, int r, int mask_padding,
+                                          const float* logits, int ld, const int32_t* targets,
+                                          float* max_r, float* sumexp_r, float* tgt_r, int32_t* argmax_r,
+                                          hipStream_t stream);
+
 /* Merge of t ranks' statistics into per-token losses, standing in for the cross-entropy's
  * all-reduces on one device: M = max_r max_r; S = sum_r sumexp_r exp(max_r - M);
  * loss = M + log S - sum_r tgt_r. max_r/sumexp_r/tgt_r are HOST arrays of t device pointers.

@@ -71,6 +71,7 @@ SIGNATURES = {
     "tp_vocab_xent_shard_fwd_noalloc_max_bytes": (_z, []),
     "tp_vocab_xent_shard_fwd_noalloc": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
     "tp_vocab_logits_shard": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p]),
+    "tp_vocab_xent_stats_from_logits": (_i, [_i, _i, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p]),
     "tp_vocab_xent_combine": (_i, [_i, _i, _pp, _pp, _pp, _p, _p, _p, _p, _p]),
     "tp_vocab_xent_shard_bwd_workspace": (_z, [_i, _i, _i, _i, _i]),
     "tp_vocab_xent_shard_bwd": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
@@ -204,6 +205,13 @@ def tp_vocab_xent_shard_fwd_noalloc(N, h, Vpad, Vreal, t, r, dt, mask_padding, X
     _check(lib.tp_vocab_xent_shard_fwd_noalloc(N, h, Vpad, Vreal, t, r, _dt(dt), mask_padding, _ptr(X), _ptr(E_r),
                                                _ptr(targets), _ptr(max_r), _ptr(sumexp_r), _ptr(tgt_r),
                                                _ptr(argmax_r), _stream(stream)))
+
+
+def tp_vocab_xent_stats_from_logits(N, Vpad, Vreal, t, r, mask_padding, logits, ld, targets, max_r, sumexp_r,
+                                    tgt_r, argmax_r, stream=None):
+    _check(lib.tp_vocab_xent_stats_from_logits(N, Vpad, Vreal, t, r, mask_padding, _ptr(logits), ld, _ptr(targets),
+                                               _ptr(max_r), _ptr(sumexp_r), _ptr(tgt_r), _ptr(argmax_r),
+                                               _stream(stream)))
 
 
 def tp_vocab_logits_shard(N, h, Vpad, t, r, dt, X, E_r, logits, stream=None):

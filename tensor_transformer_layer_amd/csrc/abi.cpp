@@ -501,6 +501,26 @@ tp_status tp_vocab_logits_shard(int N, int h, int Vpad, int t, int r, tp_dtype d
     return ok();
 }
 
+tp_status tp_vocab_xent_stats_from_logits(int N, int Vpad, int Vreal, int t, int r, int mask_padding,
+                                          const float* logits, int ld, const int32_t* targets, float* max_r,
+                                          float* sumexp_r, float* tgt_r, int32_t* argmax_r, hipStream_t stream) {
+    const char* fn = "tp_vocab_xent_stats_from_logits";
+    tp_status st;
+    if ((st = check_rank(fn, t, r)) != TP_OK) return st;
+    if (N < 0) return fail(TP_ERR_SHAPE, "%s: N=%d is negative", fn, N);
+    if (Vpad <= 0 || Vpad % t != 0) return fail(TP_ERR_SHAPE, "%s: Vpad=%d must be a positive multiple of t=%d", fn, Vpad, t);
+    if ((st = check_mult8(fn, "Vpad/t", Vpad / t)) != TP_OK) return st;
+    if (Vreal <= 0 || Vreal > Vpad) return fail(TP_ERR_SHAPE, "%s: Vreal=%d must be in [1, Vpad=%d]", fn, Vreal, Vpad);
+    if (mask_padding != 0 && mask_padding != 1) return fail(TP_ERR_ARG, "%s: mask_padding=%d must be 0 or 1", fn, mask_padding);
+    const int Vt = Vpad / t;
+    if (ld < Vt || ld % 4 != 0) return fail(TP_ERR_SHAPE, "%s: ld=%d must be >= V_t=%d and a multiple of 4", fn, ld, Vt);
+    NEED(logits); NEED(targets); NEED(max_r); NEED(sumexp_r); NEED(tgt_r); OPT(argmax_r);
+    if (N == 0) return ok();
+    HIP_TRY(xent_stats_from_logits(logits, ld, N, Vt, r * Vt, Vreal, mask_padding, targets, max_r, sumexp_r, tgt_r,
+                                   argmax_r, stream), fn);
+    return ok();
+}
+
 // dlogits copies: vocab-major [Vt][ldd] (ldd = N rounded up to 8) and token-major [N][Vt]
 static size_t xent_bwd_ld(int N) { return ((size_t)N + 7) / 8 * 8; }
 size_t tp_vocab_xent_shard_bwd_workspace(int N, int h, int Vpad, int t, tp_dtype dt) {

@@ -93,6 +93,10 @@ VocabPlan plan_vocab(int Vt, int N, int K);
 // Cross-entropy merge / combine
 hipError_t xent_merge(const void* part, int tiles_m, int N, int col0, float* mx, float* se, float* tg,
                       int32_t* am, hipStream_t st);
+// Per-token statistics (the fused call's outputs) from materialised fp32 logits [N][ld]
+hipError_t xent_stats_from_logits(const float* logits, int ld, int N, int Vt, int col0, int Vreal, int mask,
+                                  const int32_t* targets, float* mx, float* se, float* tg, int32_t* am,
+                                  hipStream_t st);
 hipError_t xent_combine(int N, int t, const float* const* mx, const float* const* se, const float* const* tg,
                         float* loss, float* mean, float* max_all, float* sumexp_all, hipStream_t st);
 

@@ -121,6 +121,92 @@ __global__ __launch_bounds__(1024) void mean_kernel(const float* __restrict__ x,
 }
 
 
+// ---------------------------------------------------------------------------------------------
+// Per-token statistics of materialised fp32 logits (the unfused form: the logits are in memory).
+// One wave per token row; lane l takes 4-column chunks l, l+64, ... (each load instruction of a
+// wave reads 1 KB of the row), U chunks in flight per lane. A lane keeps a running max (strict >,
+// so the lowest column wins a tie among its own columns, which it visits in increasing order), its
+// column, and the sum of exp(y - max) rescaled when a chunk raises the max; the 64 lanes' triples
+// are merged by a butterfly (ties to the lower column). The target logit is read directly.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void xent_row_merge(float& m, float& s, int& a, float m2, float s2, int a2) {
+    const float mn = fmaxf(m, m2);
+    const bool take = m2 > m || (m2 == m && a2 < a);
+    if (mn == -INFINITY) {
+        s = 0.f;
+    } else {
+        s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (m2 == -INFINITY ? 0.f : s2 * __expf(m2 - mn));
+    }
+    if (take) a = a2;
+    m = mn;
+}
+
+template <int U>
+__global__ __launch_bounds__(256) void xent_rows_kernel(const float* __restrict__ logits, int ld, int N, int Vt,
+                                                        int col0, int vend, const int32_t* __restrict__ targets,
+                                                        float* __restrict__ max_r, float* __restrict__ sumexp_r,
+                                                        float* __restrict__ tgt_r, int32_t* __restrict__ argmax_r) {
+    const int lane = threadIdx.x & 63;
+    const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (n >= N) return;
+    const float* row = logits + (size_t)n * ld;
+    const int nch = (vend + 3) >> 2;
+    float m = -INFINITY, s = 0.f;
+    int a = INT_MAX;
+    for (int j0 = 0; j0 < nch; j0 += 64 * U) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + 64 * u + lane;
+            v[u] = j < nch ? *(const f32x4*)(row + 4 * j) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c0 = 4 * (j0 + 64 * u + lane);
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = c0 + e < vend ? v[u][e] : -INFINITY;
+            float cm = y[0];
+            int ca = c0;
+#pragma unroll
+            for (int e = 1; e < 4; ++e)
+                if (y[e] > cm) { cm = y[e]; ca = c0 + e; }
+            if (cm > m) {
+                s = (m == -INFINITY) ? 0.f : s * __expf(m - cm);
+                m = cm;
+                a = ca;
+            }
+            if (m != -INFINITY) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s += (y[e] == -INFINITY) ? 0.f : __expf(y[e] - m);
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+        const int a2 = __shfl_xor(a, o);
+        xent_row_merge(m, s, a, m2, s2, a2);
+    }
+    if (lane == 0) {
+        const int local = targets[n] - col0;
+        max_r[n] = m;
+        sumexp_r[n] = s;
+        tgt_r[n] = (local >= 0 && local < Vt) ? row[local] : 0.f;
+        if (argmax_r) argmax_r[n] = (a == INT_MAX) ? -1 : col0 + a;
+    }
+}
+
+hipError_t xent_stats_from_logits(const float* logits, int ld, int N, int Vt, int col0, int Vreal, int mask,
+                                  const int32_t* targets, float* mx, float* se, float* tg, int32_t* am,
+                                  hipStream_t st) {
+    if (N == 0) return hipSuccess;
+    const int vend = mask ? max(0, min(Vt, Vreal - col0)) : Vt;
+    hipLaunchKernelGGL(xent_rows_kernel<4>, dim3((N + 3) / 4), dim3(256), 0, st, logits, ld, N, Vt, col0, vend, targets,
+                       mx, se, tg, am);
+    return hipGetLastError();
+}
+
 hipError_t xent_merge(const void* part, int tiles_m, int N, int col0, float* mx, float* se, float* tg,
                       int32_t* am, hipStream_t st) {
     if (N == 0) return hipSuccess;

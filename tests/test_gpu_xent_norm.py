@@ -49,6 +49,45 @@ def check_bitexact_from_logits(o, r, Vt, Vreal, mask, targets):
     assert np.array_equal(o["tgt"].cpu().numpy(), want_t)
 
 
+def check_stats_pass(o, N, Vpad, Vreal, t, r, mask, tg):
+    """The statistics pass over the stored logits against the fused call's outputs: max, argmax and
+    target logit bit for bit; the sum of exponentials (a different summation order) to 1e-5
+    element-wise relative (fp32 sums of up to V_t terms in either order)."""
+    Vt = Vpad // t
+    mx, se, tv = empty((N,), "f32"), empty((N,), "f32"), empty((N,), "f32")
+    am = torch.full((N,), -7, dtype=torch.int32, device="cuda:0")
+    tp.tp_vocab_xent_stats_from_logits(N, Vpad, Vreal, t, r, mask, o["logits"], Vt, tg, mx, se, tv, am)
+    torch.cuda.synchronize()
+    assert torch.equal(mx, o["max"]) and torch.equal(am, o["argmax"]) and torch.equal(tv, o["tgt"]), r
+    a, b = host(se), host(o["sumexp"])
+    fin = b > 0
+    assert np.array_equal(a[~fin], b[~fin])
+    rel = np.abs(a[fin] - b[fin]) / b[fin]
+    assert rel.size == 0 or rel.max() <= 1e-5, (r, rel.max())
+    return float(rel.max()) if rel.size else 0.0
+
+
+@pytest.mark.parametrize("Vreal,t,r,mask", [(1000, 4, 1, 0), (1000, 4, 3, 1), (560, 4, 3, 1), (1021, 1, 0, 1)])
+def test_xent_stats_pass_small(Vreal, t, r, mask):
+    """The statistics pass over materialised logits on ragged shapes (N = 300 tokens, h = 200,
+    V_t = 256, 192 or 1024), with and without the padding mask; (560, t=4, r=3, mask) is a rank whose
+    every column is padding: max -inf, sum 0, argmax -1, target 0."""
+    N, h = 300, 200
+    Vpad = oracle.pad_vocab(Vreal, t, multiple=64 if t > 1 else 1024)
+    inp = tp_synth.xent_inputs(90 + Vreal + r, N, h, Vreal, Vpad, "bf16", e_std=0.2)
+    say(f"[xent] stats pass N={N} Vpad={Vpad} Vreal={Vreal} t={t} r={r} mask={mask}")
+    o = run_xent(inp, N, h, Vpad, Vreal, t, [r], mask)[r]
+    rel = check_stats_pass(o, N, Vpad, Vreal, t, r, mask, dev_i32(inp["targets"]))
+    st = oracle.xent_shard_stats(inp["X"], oracle.vocab_shard(inp["E"], t, r), inp["targets"], t, r, Vreal, bool(mask))
+    if mask and r * (Vpad // t) >= Vreal:
+        assert np.all(host(o["max"]) == -np.inf) and np.all(host(o["argmax"]) == -1)
+        assert np.all(host(o["sumexp"]) == 0) and np.all(host(o["tgt"]) == 0)
+    else:
+        for k in ("max", "sumexp", "tgt"):
+            assert within(rel_l2(host(o[k]), st[k]), 1e-2), k
+    say(f"[xent] stats pass: max/argmax/target equal to the fused call; sumexp max rel diff {rel:.1e}")
+
+
 @pytest.mark.parametrize("mask", [0, 1])
 def test_xent_small_ragged(mask):
     """N=300 tokens, h=200, Vreal=1000 padded to 1024 for t=4 (V_t=256), all ranks + merge."""
@@ -126,10 +165,12 @@ def xent_8p3b():
     say("[xent] 8.3B workload: all 8 ranks on the device")
     out = run_xent(inp, w.T, w.h, w.vocab_pad, w.vocab, w.t, range(w.t), 0)
     host_out = {}
+    tg = dev_i32(inp["targets"])
     for r in range(w.t):
         o = out[r]
         host_out[r] = {k: o[k].cpu().numpy() for k in ("max", "sumexp", "tgt", "argmax")}
         check_bitexact_from_logits(o, r, w.vocab_pad // w.t, w.vocab, 0, inp["targets"])
+        check_stats_pass(o, w.T, w.vocab_pad, w.vocab, w.t, r, 0, tg)
     loss = empty((w.T,), "f32")
     mean = empty((1,), "f32")
     tp.tp_vocab_xent_combine(w.T, w.t, [out[r]["max"] for r in range(w.t)], [out[r]["sumexp"] for r in range(w.t)],
