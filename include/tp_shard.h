@@ -156,7 +156,9 @@ size_t tp_attn_dropout_mask_bytes(int b, int s, int heads, int t);
  * dWo_r [h_t, h]. accumulate as in tp_mlp_shard_bwd (dXn_r always overwritten).
  * With the forward's attention dropout (drop with the same p and the mask it wrote): dV = P~^T dO
  * and dS = P * ((dO V^T) * keep * scale - D), P~ = P * keep * scale; D = rowsum(dO * O) holds as
- * is because O = P~ V. */
+ * is because O = P~ V.
+ * The workspace holds dO, D, dQKV, split-K partials and dS in bf16 (b * heads/t * ceil(s/64)^2
+ * blocks of 64 x 64; the dK/dV pass writes it, the dQ pass reads it). */
 size_t tp_attn_shard_bwd_workspace(int b, int s, int h, int heads, int t, tp_dtype dt);
 tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dtype dt, int causal,
                             const void* Xn, const void* Wqkv_r, const void* Wo_r, const void* QKV_r,

@@ -155,9 +155,9 @@ MlpWs mlp_ws(int T, int h, int Ft, tp_dtype dt) {
     return w;
 }
 
-// dO | D | dQKV | dWo split partials | dWqkv split partials | dbqkv column-sum partials
+// dO | D | dQKV | dWo split partials | dWqkv split partials | dbqkv column-sum partials | dS blocks
 struct AttnWs {
-    size_t dO, D, dQKV, partWo, partWqkv, col, total;
+    size_t dO, D, dQKV, partWo, partWqkv, col, dS, total;
 };
 AttnWs attn_ws(int b, int s, int h, int heads_t, int h_t) {
     long T = (long)b * s;
@@ -168,7 +168,8 @@ AttnWs attn_ws(int b, int s, int h, int heads_t, int h_t) {
     w.partWo = al256(wgrad_split_ws(TP_BF16, h_t, h, (int)T));
     w.partWqkv = al256(wgrad_split_ws(TP_BF16, h, 3 * h_t, (int)T));
     w.col = al256(colsum_ws((int)T, 3 * h_t));
-    w.total = w.dO + w.D + w.dQKV + w.partWo + w.partWqkv + w.col;
+    w.dS = al256(attn_bwd_ds_bytes(b, s, heads_t));
+    w.total = w.dO + w.D + w.dQKV + w.partWo + w.partWqkv + w.col + w.dS;
     return w;
 }
 
@@ -347,6 +348,7 @@ tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dty
     void* partWo = base + w.dO + w.D + w.dQKV;
     void* partWqkv = base + w.dO + w.D + w.dQKV + w.partWo;
     float* colp = (float*)(base + w.dO + w.D + w.dQKV + w.partWo + w.partWqkv);
+    void* dSw = base + w.dO + w.D + w.dQKV + w.partWo + w.partWqkv + w.col;
     // dO = G Wo_r^T
     GemmReq g = req(T, h_t, h, G, h, 0, Wo_r, h, 0, EPI_STORE, dO, h_t);
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_bwd: dO GEMM");
@@ -355,7 +357,7 @@ tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dty
     g.accumulate = accumulate;
     HIP_TRY(run_gemm(dt, g, true, partWo, stream), "tp_attn_shard_bwd: dWo GEMM");
     if (T > 0)
-        HIP_TRY(attn_bwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, dO, Dv, dQKV, dp, stream),
+        HIP_TRY(attn_bwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, dO, Dv, dSw, dQKV, dp, stream),
                 "tp_attn_shard_bwd: attention backward");
     // dbqkv = column sums of dQKV
     if (dbqkv_r) HIP_TRY(colsum(1, T, 3 * h_t, dQKV, dbqkv_r, accumulate, colp, stream), "tp_attn_shard_bwd: dbqkv");

@@ -24,18 +24,22 @@
 // tiles are staged through registers: the next step's global loads are in flight while the
 // current step's tiles are used.
 //
-// Backward: D = rowsum(dO * O); the dK/dV kernel owns 64 keys per block and loops over query
-// tiles; the dQ kernel owns 64 queries per block and loops over key tiles. Both recompute P from
-// lse. No atomics: every output element is written by exactly one lane.
+// Backward: D = rowsum(dO * O); the dK/dV kernel owns 64 keys per block, loops over query tiles,
+// recomputes P from lse and forms dS = P (dP - D); it also stores dS (bf16, the values its dK
+// product uses) as one 64 x 64 block per (key tile, query tile) pair it visits, each block in the
+// order the waves' accumulators hold it, so every store instruction writes a whole kilobyte. The
+// dQ kernel owns 64 queries per block, turns those blocks into [key][query] LDS tiles as it
+// stages them and computes dQ = dS K: no second pass over S, P and dP. No atomics: every output
+// element is written by exactly one lane.
 //
 // Dropout on the attention weights (DROP = true; "Megatron-LM ..." paper digest, §3.4: drawn per
 // rank): the forward draws each lane's keep bits with Philox (rng.h; the element mapping puts a
 // lane's 16 keys of a 32-key tile in two calls), applies P~ = P * keep * scale before P V while
 // the row sums l use the undropped P, and stores the bits as a query-major bitmap, one 32-bit word
 // per (query, 32-key tile). The backward reads the bits instead of drawing again: dV = P~^T dO,
-// dP = (dO V^T) * keep * scale, dS = P (dP - D) with D = rowsum(dO * O) unchanged. The dQ kernel
-// has the forward's lane layout and reads one word per tile; the dK/dV kernel (one key and 16
-// queries per lane) stages the query tile's words in LDS with lse and D.
+// dP = (dO V^T) * keep * scale, dS = P (dP - D) with D = rowsum(dO * O) unchanged. The dK/dV
+// kernel (one key and 16 queries per lane) stages the query tile's words in LDS with lse and D;
+// the dQ kernel reads dS and so needs no bits.
 #pragma once
 #include "common.h"
 #include "rng.h"
@@ -360,6 +364,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(const bf16* __restric
     }
 }
 
+// dS blocks of one (sequence, head): one per (key tile kt, query tile qt) pair with a visible key,
+// i.e. qt >= kt under the causal mask (ordered by kt, then qt), every pair otherwise.
+__host__ __device__ __forceinline__ int ds_pairs(int nq, int causal) { return causal ? nq * (nq + 1) / 2 : nq * nq; }
+__device__ __forceinline__ int ds_pair(int kt, int qt, int nq, int causal) {
+    return causal ? kt * nq - kt * (kt - 1) / 2 + (qt - kt) : kt * nq + qt;
+}
+
 // ---------------------------------------------------------------------------------------------
 // dK, dV. grid = (b * heads_t, key tiles), key tile kt = blockIdx.y (heavy first under the causal
 // mask). Wave w: key group g = w & 1 (keys kt*64 + 32g ..), query half q = w >> 1 of each query
@@ -373,7 +384,7 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(D <= 96 
 void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int heads_t,
                           const bf16* __restrict__ dO, int ld_do, const float* __restrict__ lse,
                           const float* __restrict__ Dv, float scale_log2, float scale, int causal,
-                          bf16* __restrict__ dQKV, int ld_dq, DropParams dp) {
+                          bf16* __restrict__ dQKV, int ld_dq, bf16* __restrict__ dSb, DropParams dp) {
     __shared__ __attribute__((aligned(16))) bf16 smem[4 * ATT_B * D];   // Q tile | dO tile | K | V
     __shared__ float lse_s[ATT_B], D_s[ATT_B];
     __shared__ uint32_t mk_s[ATT_B][2];   // dropout keep words of the query tile x the block's two key groups
@@ -433,12 +444,17 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
     };
     if (qt0 < nqt) { fetch(qt0 * ATT_B); stash(); }
     __syncthreads();
-    for (int qt = qt0; qt < nqt; ++qt) {
+    // this wave's two 1 KB chunks (kk = 0, 1) of dS block (kt, qt), in the accumulator's own order
+    bf16* dsw = dSb + ((size_t)(bi * heads_t + head) * ds_pairs(nqt, causal) + ds_pair(kt, qt0, nqt, causal)) * (ATT_B * ATT_B) +
+                (grp * 2 + qh) * 2 * 512 + lane * 8;
+    for (int qt = qt0; qt < nqt; ++qt, dsw += ATT_B * ATT_B) {
         const bool more = qt + 1 < nqt;
         if (more) fetch((qt + 1) * ATT_B);
         const int q0 = qt * ATT_B;
         const int qs0 = q0 + qh * 32;
-        if (!(causal && qs0 + 31 < kw0)) {   // some query of this half sees some key of this wave
+        u32x4 dsv[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};   // this step's dS, stored at its end
+        if (causal && qs0 + 31 < kw0) {   // no query of this half sees a key of this wave: dS = 0
+        } else {
             const bool need_mask = (causal && qs0 < kw0 + 31) || (qs0 + 32 > s) || (kw0 + 32 > s);
             f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
@@ -468,6 +484,7 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 bf16x8 pb = pack8(sacc, 8 * kk), dsb = pack8(dpacc, 8 * kk);
+                dsv[kk] = __builtin_bit_cast(u32x4, dsb);
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) {
                     dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<D>(Gb, qh * 32 + 16 * kk, dt * 32, lane),
@@ -480,6 +497,10 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
         __syncthreads();
         if (more) stash();
         __syncthreads();
+        // dS for the dQ kernel, issued after the stash's wait for the next tile's loads so that the
+        // stores drain during the next step instead of holding up that wait
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) *(u32x4*)(dsw + 512 * kk) = dsv[kk];
     }
     // merge: the second query half's waves hand dK, dV to the first half's wave of the same key
     // group, through the tile buffers (in two rounds, dK then dV, when both do not fit at once)
@@ -556,115 +577,106 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
 }
 
 // ---------------------------------------------------------------------------------------------
-// dQ. grid = (b * heads_t, query tiles), qt = last - blockIdx.y (heavy first). Wave w: row group
-// g = w & 1 (32 queries), key-tile parity kp = w >> 1; K and V tiles two per step.
-//   S^T = K Q^T, P^T = exp2(S^T*c - lse2), dP^T = V dO^T, dS^T = P^T (dP^T - D); dQ^T += K^T dS^T
+// dQ = scale * dS K from the dK/dV kernel's dS blocks. grid = (b * heads_t, query tiles), qt = last
+// - blockIdx.y (heavy first). Wave w: row group g = w & 1 (32 queries), key-tile parity kp = w >> 1;
+// per step the block stages two key tiles and their dS blocks (register-staged, the next pair's
+// loads in flight while the current pair is multiplied):
+//   dQ^T (D x 32 queries) += K^T (D x 64 keys) dS^T (64 keys x 32 queries)
+// both operands read with the transposing LDS load from the row-major K tile and the [key][query]
+// dS block, in the same k order. The two parities' sums are added at the end.
 // ---------------------------------------------------------------------------------------------
-template <int D, bool DROP>
-__global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(D <= 96 ? 2 : 1)))
+template <int D>
+__global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void attn_bwd_dq_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int heads_t,
-                        const bf16* __restrict__ dO, int ld_do, const float* __restrict__ lse,
-                        const float* __restrict__ Dv, float scale_log2, float scale, int causal,
-                        bf16* __restrict__ dQKV, int ld_dq, DropParams dp) {
-    __shared__ __attribute__((aligned(16))) bf16 smem[4 * ATT_B * D];   // K tiles [2] | V tiles [2]
-    __shared__ __attribute__((aligned(16))) bf16 QGs[2 * ATT_B * D];    // the block's queries | their dO
-    bf16* Kb = smem;
-    bf16* Vb = smem + 2 * ATT_B * D;
+                        const bf16* __restrict__ dSb, float scale, int causal, bf16* __restrict__ dQKV, int ld_dq) {
+    __shared__ __attribute__((aligned(16))) bf16 Kb[2 * ATT_B * D];          // key tiles of parity 0 | 1
+    __shared__ __attribute__((aligned(16))) bf16 Sb[2 * ATT_B * ATT_B];      // their dS blocks
     const int head = blockIdx.x % heads_t, bi = blockIdx.x / heads_t, qt = gridDim.y - 1 - blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const int grp = wave & 1, kp = wave >> 1;
     const size_t tok0 = (size_t)bi * s;
-    const bf16* Qp = QKV + tok0 * ld + head * D;
     const bf16* Kp = QKV + tok0 * ld + h_t + head * D;
-    const bf16* Vp = QKV + tok0 * ld + 2 * h_t + head * D;
-    const bf16* dOp = dO + tok0 * ld_do + head * D;
-    const bf16* Qs = QGs;
-    const bf16* Gs = QGs + ATT_B * D;
-    const int q0w = qt * ATT_B + grp * 32;
-    const int myq = q0w + l32;
-    const float lse2 = (myq < s) ? lse[((size_t)bi * heads_t + head) * s + myq] * kLog2e : INFINITY;
-    const float Dq = (myq < s) ? Dv[((size_t)bi * heads_t + head) * s + myq] : 0.f;
-
-    load_tile<D>(Qp, ld, qt * ATT_B, s, QGs, tid);
-    load_tile<D>(dOp, ld_do, qt * ATT_B, s, QGs + ATT_B * D, tid);
+    const int nq = (s + ATT_B - 1) / ATT_B;
+    const bf16* dSh = dSb + (size_t)(bi * heads_t + head) * ds_pairs(nq, causal) * (ATT_B * ATT_B);
+    const int myq = qt * ATT_B + grp * 32 + l32;
     f32x16 dq[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) dq[dt] = zero16();
 
-    const int kv_end = causal ? min(s, (qt + 1) * ATT_B) : s;
-    const int ntiles = (kv_end + ATT_B - 1) / ATT_B;
+    const int ntiles = causal ? qt + 1 : nq;
     const int niter = (ntiles + 1) / 2;
-    AttTileRegs<D> kr, vr;
-    const auto krs = att_rsrc<D>(Kp, ld, s), vrs = att_rsrc<D>(Vp, ld, s);
+    AttTileRegs<D> kr;
+    const auto krs = att_rsrc<D>(Kp, ld, s);
+    // The dS blocks of key tiles 2it, 2it + 1, four 16-byte chunks per thread (a block past the last
+    // key tile reads zeros). Chunk c = ((g*2 + qh)*2 + kk)*64 + 32h + k of a block holds key 32g + k
+    // and queries 32qh + 16kk + 4h + 0..3 and + 8 .. + 11 (the dK/dV kernel's accumulator order);
+    // it goes to the [key][query] tile as two 8-byte pieces. Pass u = 4j + wave covers block u/8,
+    // key group (u/4)%2, keys 8(u%4) .. + 7; lane = key%8 + 8 (h + 2kk + 4qh), so a wave reads
+    // whole 128-byte lines and each LDS write puts two dwords on every bank.
+    u32x4 sr[4];
+    auto ds_coords = [&](int j, int& blk, int& key, int& q0, int& c) {
+        const int u = 4 * j + wave, g = (u >> 2) & 1, k = (u & 3) * 8 + (lane & 7), cb = lane >> 3;
+        const int hh = cb & 1, kk = (cb >> 1) & 1, qh = cb >> 2;
+        blk = u >> 3;
+        key = g * 32 + k;
+        q0 = qh * 32 + 16 * kk + 4 * hh;
+        c = ((g * 2 + qh) * 2 + kk) * 64 + 32 * hh + k;
+    };
+    auto fetch_ds = [&](int it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int blk, key, q0, c;
+            ds_coords(j, blk, key, q0, c);
+            const int kt = 2 * it + blk;
+            sr[j] = kt < ntiles ? *(const u32x4*)(dSh + (size_t)ds_pair(kt, qt, nq, causal) * (ATT_B * ATT_B) + c * 8)
+                                : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto stash_ds = [&]() {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int blk, key, q0, c;
+            ds_coords(j, blk, key, q0, c);
+            bf16* t = Sb + blk * ATT_B * ATT_B;
+            *(u32x2*)(t + att_off<ATT_B>(key, q0)) = u32x2{sr[j][0], sr[j][1]};
+            *(u32x2*)(t + att_off<ATT_B>(key, q0 + 8)) = u32x2{sr[j][2], sr[j][3]};
+        }
+    };
     if (niter > 0) {
         kr.load(krs, ld, 0, s, tid);
-        vr.load(vrs, ld, 0, s, tid);
+        fetch_ds(0);
         kr.store(Kb, tid);
-        vr.store(Vb, tid);
+        stash_ds();
     }
     __syncthreads();
     for (int it = 0; it < niter; ++it) {
         const bool more = it + 1 < niter;
         if (more) {
             kr.load(krs, ld, (it + 1) * 2 * ATT_B, s, tid);
-            vr.load(vrs, ld, (it + 1) * 2 * ATT_B, s, tid);
+            fetch_ds(it + 1);
         }
-        const int kt = 2 * it + kp, k0 = kt * ATT_B;
-        if (kt < ntiles) {
+        if (2 * it + kp < ntiles) {
             const bf16* K = Kb + kp * ATT_B * D;
-            const bf16* V = Vb + kp * ATT_B * D;
+            const bf16* S = Sb + kp * ATT_B * ATT_B;
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-                const int ks0 = k0 + sub * 32;
-                if (causal && ks0 > q0w + 31) continue;
-                const bool need_mask = (causal && ks0 + 31 > q0w) || (ks0 + 32 > s);
-                uint32_t keepw = 0;
-                if constexpr (DROP) {
-                    const int n32 = (s + 31) >> 5, kt32 = ks0 >> 5;
-                    if (myq < s && kt32 < n32) keepw = dp.mask[((size_t)(bi * heads_t + head) * s + myq) * n32 + kt32];
-                }
-                f32x16 sacc = zero16(), dpacc = zero16();
+            for (int ks = 0; ks < ATT_B / 16; ++ks) {
+                const bf16x8 dsf = frag_cols<ATT_B>(S, 16 * ks, grp * 32, lane);
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(K, sub * 32, ks * 16, lane),
-                                                                   frag_rows<D>(Qs, grp * 32, ks * 16, lane), sacc, 0, 0, 0);
-                    dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(V, sub * 32, ks * 16, lane),
-                                                                    frag_rows<D>(Gs, grp * 32, ks * 16, lane), dpacc, 0, 0, 0);
-                }
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    float pv = fast_exp2(fmaf(sacc[v], scale_log2, -lse2));
-                    if (need_mask) {
-                        int key = ks0 + 8 * (v >> 2) + 4 * h + (v & 3);
-                        if ((causal && key > myq) || key >= s) pv = 0.f;
-                    }
-                    if constexpr (DROP) {
-                        const bool kb = (keepw >> (8 * (v >> 2) + 4 * h + (v & 3))) & 1u;
-                        dpacc[v] = pv * ((kb ? dpacc[v] * dp.scale : 0.0f) - Dq);
-                    } else {
-                        dpacc[v] = pv * (dpacc[v] - Dq);
-                    }
-                }
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    bf16x8 dsb = pack8(dpacc, 8 * kk);
-#pragma unroll
-                    for (int dt = 0; dt < D / 32; ++dt)
-                        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<D>(K, sub * 32 + 16 * kk, dt * 32, lane),
-                                                                         dsb, dq[dt], 0, 0, 0);
-                }
+                for (int dt = 0; dt < D / 32; ++dt)
+                    dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<D>(K, 16 * ks, dt * 32, lane), dsf, dq[dt],
+                                                                     0, 0, 0);
             }
         }
         __syncthreads();
         if (more) {
             kr.store(Kb, tid);
-            vr.store(Vb, tid);
+            stash_ds();
         }
         __syncthreads();
     }
     constexpr int NV = D / 2;
-    float* xch = (float*)smem;
-    static_assert(2 * NV * 64 * 4 <= 4 * ATT_B * D * 2, "exchange exceeds the tile buffers");
+    float* xch = (float*)Kb;
+    static_assert(2 * NV * 64 * 4 <= 2 * ATT_B * D * 2, "exchange exceeds the tile buffers");
     if (kp == 1) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)

@@ -71,11 +71,15 @@ hipError_t gemm_bf16_nt(const GemmReq& r, const GemmPlan& p, void* ws, hipStream
 hipError_t gemm_bf16_tn(const GemmReq& r, const GemmPlan& p, void* ws, hipStream_t st);   // both MN-contig
 
 // Attention (bf16, head width d)
-// dp.thr = 0: no dropout; otherwise attention dropout with dp.mask written by attn_fwd, read by attn_bwd
+// dp.thr = 0: no dropout; otherwise attention dropout with dp.mask written by attn_fwd, read by attn_bwd.
+// attn_bwd's dSws holds the bf16 score gradients between its two passes: attn_bwd_ds_bytes(b, s, heads_t)
+// bytes (every 64 x 64 block of every head; a causal mask uses a little over half).
 hipError_t attn_fwd(int b, int s, int h_t, int heads_t, int d, int causal, const void* QKV, void* O, float* lse,
                     const DropParams& dp, hipStream_t st);
 hipError_t attn_bwd(int b, int s, int h_t, int heads_t, int d, int causal, const void* QKV, const void* O,
-                    const float* lse, const void* dO, float* Dws, void* dQKV, const DropParams& dp, hipStream_t st);
+                    const float* lse, const void* dO, float* Dws, void* dSws, void* dQKV, const DropParams& dp,
+                    hipStream_t st);
+size_t attn_bwd_ds_bytes(int b, int s, int heads_t);
 
 // Fused logits GEMM of a vocabulary shard (Vt rows x N tokens, depth K), in two launches: 256x256
 // tiles over rows [0, main_rows) -- as many whole rounds of tiles over the 256 CUs as the shape
