@@ -150,7 +150,9 @@ MlpWs mlp_ws(int T, int h, int Ft, tp_dtype dt) {
     w.dU = al256((size_t)T * Ft * esize(dt));
     w.partB = al256(wgrad_split_ws(dt, Ft, h, T));
     w.partA = al256(wgrad_split_ws(dt, h, Ft, T));
-    w.col = al256(colsum_ws(T, Ft));
+    // db1 partials: the column-sum pass's row blocks, or one row per 64 or more tokens (the dU
+    // GEMM's tile rows), whichever is larger
+    w.col = al256(std::max(colsum_ws(T, Ft), (size_t)((T + 63) / 64) * Ft * sizeof(float)));
     w.total = w.dU + w.partB + w.partA + w.col;
     return w;
 }
@@ -167,7 +169,8 @@ AttnWs attn_ws(int b, int s, int h, int heads_t, int h_t) {
     w.dQKV = al256((size_t)T * 3 * h_t * 2);
     w.partWo = al256(wgrad_split_ws(TP_BF16, h_t, h, (int)T));
     w.partWqkv = al256(wgrad_split_ws(TP_BF16, h, 3 * h_t, (int)T));
-    w.col = al256(colsum_ws((int)T, 3 * h_t));
+    // dbqkv partials: one row per 64-token tile of each sequence (at least the column-sum pass's)
+    w.col = al256(std::max(colsum_ws((int)T, 3 * h_t), (size_t)b * ((s + 63) / 64) * 3 * h_t * sizeof(float)));
     w.dS = al256(attn_bwd_ds_bytes(b, s, heads_t));
     w.total = w.dO + w.D + w.dQKV + w.partWo + w.partWqkv + w.col + w.dS;
     return w;
@@ -269,12 +272,20 @@ tp_status tp_mlp_shard_bwd(int T, int h, int ffn, int t, int r, tp_dtype dt, con
     void* partB = base + w.dU;
     void* partA = base + w.dU + w.partB;
     float* colp = (float*)(base + w.dU + w.partB + w.partA);
-    // dU = (G B_r^T) * GeLU'(U_r)
+    // dU = (G B_r^T) * GeLU'(U_r); in bf16 its epilogue also writes the column sums of dU per tile
+    // row, which db1 = column sums of dU then adds up
     GemmReq g = req(T, Ft, h, G, h, 0, B_r, h, 0, EPI_DGELU, dU, Ft);
     g.aux = U_r;
+    const bool fused_db1 = db1_r && dt == TP_BF16;
+    if (fused_db1) g.colpart = colp;
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_mlp_shard_bwd: dU GEMM");
-    // db1 = column sums of dU
-    if (db1_r) HIP_TRY(colsum(dt == TP_BF16, T, Ft, dU, db1_r, accumulate, colp, stream), "tp_mlp_shard_bwd: db1");
+    if (fused_db1) {
+        const int bm = plan_gemm_bf16(T, Ft, h, false).bm;
+        HIP_TRY(colsum_reduce(1, T > 0 ? (T + bm - 1) / bm : 0, Ft, colp, db1_r, accumulate, stream),
+                "tp_mlp_shard_bwd: db1");
+    } else if (db1_r) {
+        HIP_TRY(colsum(0, T, Ft, dU, db1_r, accumulate, colp, stream), "tp_mlp_shard_bwd: db1");
+    }
     // dB_r = Y_r^T G
     g = req(Ft, h, T, Y_r, Ft, 1, G, h, 1, EPI_STORE, dB_r, h);
     g.accumulate = accumulate;
@@ -357,10 +368,13 @@ tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dty
     g.accumulate = accumulate;
     HIP_TRY(run_gemm(dt, g, true, partWo, stream), "tp_attn_shard_bwd: dWo GEMM");
     if (T > 0)
-        HIP_TRY(attn_bwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, dO, Dv, dSw, dQKV, dp, stream),
+        HIP_TRY(attn_bwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, dO, Dv, dSw, dQKV, dbqkv_r ? colp : nullptr,
+                         dp, stream),
                 "tp_attn_shard_bwd: attention backward");
-    // dbqkv = column sums of dQKV
-    if (dbqkv_r) HIP_TRY(colsum(1, T, 3 * h_t, dQKV, dbqkv_r, accumulate, colp, stream), "tp_attn_shard_bwd: dbqkv");
+    // dbqkv = column sums of dQKV, from the attention backward's per-tile sums
+    if (dbqkv_r)
+        HIP_TRY(colsum_reduce(1, T > 0 ? b * ((s + 63) / 64) : 0, 3 * h_t, colp, dbqkv_r, accumulate, stream),
+                "tp_attn_shard_bwd: dbqkv");
     // dWqkv_r = Xn^T dQKV
     g = req(h, 3 * h_t, T, Xn, h, 1, dQKV, 3 * h_t, 1, EPI_STORE, dWqkv_r, 3 * h_t);
     g.accumulate = accumulate;

@@ -364,6 +364,37 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(const bf16* __restric
     }
 }
 
+// Column sums over a block's 64 rows (tokens) of D columns held in MFMA accumulator layout by two
+// waves (rows 32g + lane % 32, column dt*32 + 8(v/4) + 4(lane/32) + v%4 of acc[dt][v]): the values
+// as rounded to bf16 (zeros for rows past the sequence) go through an fp32 LDS buffer [64][D + 4]
+// and D threads add their column's rows in order; out[d] = sum. Called by all threads of the block
+// after the buffer's previous contents are no longer needed by any wave.
+template <int D, int NDT>
+__device__ __forceinline__ void tile_colsum(const f32x16 (&acc)[NDT], bool holder, bool valid, int row, int lane, int tid,
+                                            float* buf, float* __restrict__ out) {
+    constexpr int LDC = D + 4;
+    const int h = lane >> 5;
+    __syncthreads();
+    if (holder) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = valid ? (float)(bf16)acc[dt][4 * i + e] : 0.f;
+                *(f32x4*)(buf + row * LDC + dt * 32 + 8 * i + 4 * h) = w;
+            }
+    }
+    __syncthreads();
+    for (int d = tid; d < D; d += ATT_NT) {
+        float sum = 0.f;
+#pragma unroll 8
+        for (int r = 0; r < ATT_B; ++r) sum += buf[r * LDC + d];
+        out[d] = sum;
+    }
+}
+
 // dS blocks of one (sequence, head): one per (key tile kt, query tile qt) pair with a visible key,
 // i.e. qt >= kt under the causal mask (ordered by kt, then qt), every pair otherwise.
 __host__ __device__ __forceinline__ int ds_pairs(int nq, int causal) { return causal ? nq * (nq + 1) / 2 : nq * nq; }
@@ -384,7 +415,8 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(D <= 96 
 void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int heads_t,
                           const bf16* __restrict__ dO, int ld_do, const float* __restrict__ lse,
                           const float* __restrict__ Dv, float scale_log2, float scale, int causal,
-                          bf16* __restrict__ dQKV, int ld_dq, bf16* __restrict__ dSb, DropParams dp) {
+                          bf16* __restrict__ dQKV, int ld_dq, bf16* __restrict__ dSb, float* __restrict__ colpart,
+                          DropParams dp) {
     __shared__ __attribute__((aligned(16))) bf16 smem[4 * ATT_B * D];   // Q tile | dO tile | K | V
     __shared__ float lse_s[ATT_B], D_s[ATT_B];
     __shared__ uint32_t mk_s[ATT_B][2];   // dropout keep words of the query tile x the block's two key groups
@@ -557,22 +589,30 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
                 for (int v = 0; v < 16; ++v) dv[dt][v] += xch_get<NH>(xch, grp, dt * 16 + v, lane);
         }
     }
-    if (qh == 0 && mykey < s) {
+    if (qh == 0) {
         bf16* kp_ = dQKV + (tok0 + mykey) * ld_dq + h_t + head * D;
         bf16* vp_ = dQKV + (tok0 + mykey) * ld_dq + 2 * h_t + head * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) dk[dt][v] *= scale;
+            if (mykey < s) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int d = dt * 32 + 8 * i + 4 * h;
-                *(u32x2*)(kp_ + d) = u32x2{pack_bf16x2(dk[dt][4 * i], dk[dt][4 * i + 1]),
-                                           pack_bf16x2(dk[dt][4 * i + 2], dk[dt][4 * i + 3])};
-                *(u32x2*)(vp_ + d) = u32x2{pack_bf16x2(dv[dt][4 * i], dv[dt][4 * i + 1]),
-                                           pack_bf16x2(dv[dt][4 * i + 2], dv[dt][4 * i + 3])};
+                for (int i = 0; i < 4; ++i) {
+                    int d = dt * 32 + 8 * i + 4 * h;
+                    *(u32x2*)(kp_ + d) = u32x2{pack_bf16x2(dk[dt][4 * i], dk[dt][4 * i + 1]),
+                                               pack_bf16x2(dk[dt][4 * i + 2], dk[dt][4 * i + 3])};
+                    *(u32x2*)(vp_ + d) = u32x2{pack_bf16x2(dv[dt][4 * i], dv[dt][4 * i + 1]),
+                                               pack_bf16x2(dv[dt][4 * i + 2], dv[dt][4 * i + 3])};
+                }
             }
         }
+    }
+    static_assert(ATT_B * (D + 4) * 4 <= sizeof(smem), "column-sum buffer exceeds the tile buffers");
+    if (colpart) {
+        float* cp = colpart + (size_t)(bi * nqt + kt) * (3 * h_t) + head * D;
+        tile_colsum<D, D / 32>(dk, qh == 0, mykey < s, grp * 32 + l32, lane, tid, (float*)smem, cp + h_t);
+        tile_colsum<D, D / 32>(dv, qh == 0, mykey < s, grp * 32 + l32, lane, tid, (float*)smem, cp + 2 * h_t);
     }
 }
 
@@ -588,9 +628,11 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
 template <int D>
 __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void attn_bwd_dq_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int heads_t,
-                        const bf16* __restrict__ dSb, float scale, int causal, bf16* __restrict__ dQKV, int ld_dq) {
-    __shared__ __attribute__((aligned(16))) bf16 Kb[2 * ATT_B * D];          // key tiles of parity 0 | 1
-    __shared__ __attribute__((aligned(16))) bf16 Sb[2 * ATT_B * ATT_B];      // their dS blocks
+                        const bf16* __restrict__ dSb, float scale, int causal, bf16* __restrict__ dQKV, int ld_dq,
+                        float* __restrict__ colpart) {
+    __shared__ __attribute__((aligned(16))) bf16 sm[2 * ATT_B * D + 2 * ATT_B * ATT_B];
+    bf16* Kb = sm;                      // key tiles of parity 0 | 1
+    bf16* Sb = sm + 2 * ATT_B * D;      // their dS blocks
     const int head = blockIdx.x % heads_t, bi = blockIdx.x / heads_t, qt = gridDim.y - 1 - blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const int grp = wave & 1, kp = wave >> 1;
@@ -684,20 +726,25 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, in
             for (int v = 0; v < 16; ++v) xch_put<NV>(xch, grp, dt * 16 + v, lane, dq[dt][v]);
     }
     __syncthreads();
-    if (kp == 0 && myq < s) {
+    if (kp == 0) {
         bf16* qp_ = dQKV + (tok0 + myq) * ld_dq + head * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) dq[dt][v] = (dq[dt][v] + xch_get<NV>(xch, grp, dt * 16 + v, lane)) * scale;
+            if (myq < s) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int d = dt * 32 + 8 * i + 4 * h;
-                *(u32x2*)(qp_ + d) = u32x2{pack_bf16x2(dq[dt][4 * i], dq[dt][4 * i + 1]),
-                                           pack_bf16x2(dq[dt][4 * i + 2], dq[dt][4 * i + 3])};
+                for (int i = 0; i < 4; ++i) {
+                    int d = dt * 32 + 8 * i + 4 * h;
+                    *(u32x2*)(qp_ + d) = u32x2{pack_bf16x2(dq[dt][4 * i], dq[dt][4 * i + 1]),
+                                               pack_bf16x2(dq[dt][4 * i + 2], dq[dt][4 * i + 3])};
+                }
             }
         }
     }
+    static_assert(ATT_B * (D + 4) * 4 <= sizeof(sm), "column-sum buffer exceeds the tile buffers");
+    if (colpart) tile_colsum<D, D / 32>(dq, kp == 0, myq < s, grp * 32 + l32, lane, tid, (float*)sm,
+                                        colpart + (size_t)(bi * nq + qt) * (3 * h_t) + head * D);
 }
 
 }  // namespace tp

@@ -21,8 +21,8 @@ static hipError_t fwd_d(int b, int s, int h_t, int heads_t, int causal, const vo
 
 template <int D>
 static hipError_t bwd_d(int b, int s, int h_t, int heads_t, int causal, const void* QKV, const void* O,
-                        const float* lse, const void* dO, float* Dws, void* dSws, void* dQKV, const DropParams& dp,
-                        hipStream_t st) {
+                        const float* lse, const void* dO, float* Dws, void* dSws, void* dQKV, float* colpart,
+                        const DropParams& dp, hipStream_t st) {
     size_t rows = (size_t)b * s * heads_t;
     hipLaunchKernelGGL((attn_bwd_dot_kernel<D>), dim3((unsigned)((rows * 4 + 255) / 256)), dim3(256), 0, st,
                        (const bf16*)dO, (const bf16*)O, h_t, b, s, heads_t, Dws);
@@ -34,14 +34,14 @@ static hipError_t bwd_d(int b, int s, int h_t, int heads_t, int causal, const vo
 #define TP_ATT_BWD(DR)                                                                                           \
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, DR>), grid, dim3(ATT_NT), 0, st, (const bf16*)QKV, 3 * h_t, h_t, s, \
                        heads_t, (const bf16*)dO, h_t, lse, (const float*)Dws, scale_log2, scale, causal,            \
-                       (bf16*)dQKV, 3 * h_t, (bf16*)dSws, dp)
+                       (bf16*)dQKV, 3 * h_t, (bf16*)dSws, colpart, dp)
     if (dp.thr) TP_ATT_BWD(true);
     else TP_ATT_BWD(false);
 #undef TP_ATT_BWD
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), grid, dim3(ATT_NT), 0, st, (const bf16*)QKV, 3 * h_t, h_t, s, heads_t,
-                       (const bf16*)dSws, scale, causal, (bf16*)dQKV, 3 * h_t);
+                       (const bf16*)dSws, scale, causal, (bf16*)dQKV, 3 * h_t, colpart);
     return hipGetLastError();
 }
 
@@ -62,13 +62,13 @@ hipError_t attn_fwd(int b, int s, int h_t, int heads_t, int d, int causal, const
 }
 
 hipError_t attn_bwd(int b, int s, int h_t, int heads_t, int d, int causal, const void* QKV, const void* O,
-                    const float* lse, const void* dO, float* Dws, void* dSws, void* dQKV, const DropParams& dp,
-                    hipStream_t st) {
+                    const float* lse, const void* dO, float* Dws, void* dSws, void* dQKV, float* colpart,
+                    const DropParams& dp, hipStream_t st) {
     switch (d) {
-        case 64: return bwd_d<64>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dSws, dQKV, dp, st);
-        case 96: return bwd_d<96>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dSws, dQKV, dp, st);
-        case 128: return bwd_d<128>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dSws, dQKV, dp, st);
-        case 192: return bwd_d<192>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dSws, dQKV, dp, st);
+        case 64: return bwd_d<64>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dSws, dQKV, colpart, dp, st);
+        case 96: return bwd_d<96>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dSws, dQKV, colpart, dp, st);
+        case 128: return bwd_d<128>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dSws, dQKV, colpart, dp, st);
+        case 192: return bwd_d<192>(b, s, h_t, heads_t, causal, QKV, O, lse, dO, Dws, dSws, dQKV, colpart, dp, st);
     }
     return hipErrorInvalidValue;
 }

@@ -265,6 +265,77 @@ __device__ __forceinline__ void apply_staged(const Op& op, f32x16 (&acc)[C::TM][
     }
 }
 
+// apply_staged that also sums, per column, the values the op stores (rounded to its output type
+// OutT) over the tile's rows, and writes those sums as row m0 / BM of colpart [tiles_m][N]. After
+// a strip's op8 calls each wave writes the stored values back over its slab and its lanes add the
+// slab's columns (32 rows, in row order); the WGM waves sharing a column block are then added in
+// wave-row order through LDS. Rows past M and columns past N count as zeros.
+template <class C, class Op>
+__device__ __forceinline__ void apply_staged_colsum(const Op& op, f32x16 (&acc)[C::TM][C::TN], int m0, int n0, int mw0,
+                                                    int nw0, int lane, int wave, int M, int N, char* smem,
+                                                    float* __restrict__ colpart) {
+    typedef Staging<C> S;
+    typedef typename Op::OutT OutT;
+    constexpr int NCL = (C::WN + 63) / 64;   // slab columns per lane in the column pass
+    static_assert(C::WGM * C::BN * 4 <= C::LDS, "column-sum exchange exceeds the tile buffers");
+    float* slab = (float*)smem + wave * S::SLAB;
+    const int h = lane >> 5, l32 = lane & 31;
+    float cs[NCL];
+#pragma unroll
+    for (int j = 0; j < NCL; ++j) cs[j] = 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) slab[(8 * (v >> 2) + 4 * h + (v & 3)) * S::LD + j * 32 + l32] = acc[i][j][v];
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < S::CHUNKS / 64; ++q) {
+            const int c = q * 64 + lane, r = c / S::CPR, cc = c - r * S::CPR;
+            float* p = slab + r * S::LD + cc * 8;
+            f32x4 lo = *(const f32x4*)p, hi = *(const f32x4*)(p + 4);
+            float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const int row = mw0 + i * 32 + r, col = nw0 + cc * 8;
+            if (row < M && col < N) {
+                op.op8(row, col, v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = to_f32(from_f32<OutT>(v[e]));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = 0.f;
+            }
+            // a wave's LDS accesses complete in order: the column pass below reads these values
+            *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
+            *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        }
+#pragma unroll
+        for (int j = 0; j < NCL; ++j) {
+            const int col = lane + 64 * j;
+            if (col < C::WN) {
+#pragma unroll 8
+                for (int r = 0; r < 32; ++r) cs[j] += slab[r * S::LD + col];
+            }
+        }
+        __syncthreads();
+    }
+    const int wm = wave / C::WGN, wn = wave % C::WGN;
+    float* red = (float*)smem;   // [WGM][BN]
+#pragma unroll
+    for (int j = 0; j < NCL; ++j) {
+        const int col = lane + 64 * j;
+        if (col < C::WN) red[wm * C::BN + wn * C::WN + col] = cs[j];
+    }
+    __syncthreads();
+    for (int c = (int)threadIdx.x; c < C::BN; c += C::NT) {
+        float sum = red[c];
+#pragma unroll
+        for (int w = 1; w < C::WGM; ++w) sum += red[w * C::BN + c];
+        if (n0 + c < N) colpart[(size_t)(m0 / C::BM) * N + n0 + c] = sum;
+    }
+}
+
 // Elementwise form, straight from the MFMA layout (used by the transposed store).
 template <class C, class Op>
 __device__ __forceinline__ void apply_elementwise(const Op& op, f32x16 (&acc)[C::TM][C::TN], int mw0, int nw0,
@@ -364,11 +435,14 @@ template <typename T> struct EpiBiasGelu {
     TP_STAGED_APPLY
 };
 
-// dU = v * GeLU'(U)
+// dU = v * GeLU'(U); with colpart, also the column sums of the stored dU per tile row
+// (apply_staged_colsum)
 template <typename T> struct EpiDGelu {
     static constexpr bool kVec8 = true;
+    typedef T OutT;
     __device__ __forceinline__ void set_split(int) {}
     T* dU; const T* U; int ld;
+    float* colpart = nullptr;
     __device__ __forceinline__ void operator()(int r, int c, float v) const {
         size_t o = (size_t)r * ld + c;
         dU[o] = from_f32<T>(v * gelu_grad_f(to_f32(U[o])));
@@ -381,7 +455,13 @@ template <typename T> struct EpiDGelu {
         for (int e = 0; e < 8; ++e) v[e] *= gelu_grad_f(u[e]);
         store8(dU + o, v);
     }
-    TP_STAGED_APPLY
+    template <class C>
+    __device__ __forceinline__ void apply(f32x16 (&acc)[C::TM][C::TN], int m0, int n0, int mw0, int nw0, int lane,
+                                          int M, int N, char* smem) const {
+        const int wave = (int)(threadIdx.x >> 6);
+        if (colpart) apply_staged_colsum<C>(*this, acc, m0, n0, mw0, nw0, lane, wave, M, N, smem, colpart);
+        else apply_staged<C>(*this, acc, mw0, nw0, lane, wave, M, N, smem);
+    }
 };
 
 // Split-K partial: part[split][r*ld + c] = v (fp32). Reduced later in split order.

@@ -77,7 +77,7 @@ static hipError_t gemm_run(const GemmReq& r, const GemmPlan& p, void* ws, hipStr
             break;
         case EPI_DGELU:
             if constexpr ((KINDS & (1 << EPI_DGELU)) != 0)
-                return launch_plan<LA, LB>(r, p, EpiDGelu<bf16>{(bf16*)r.out, (const bf16*)r.aux, r.ldc}, st);
+                return launch_plan<LA, LB>(r, p, EpiDGelu<bf16>{(bf16*)r.out, (const bf16*)r.aux, r.ldc, r.colpart}, st);
             break;
         case EPI_STORE_T:
             if constexpr ((KINDS & (1 << EPI_STORE_T)) != 0)

@@ -34,6 +34,9 @@ struct GemmReq {
     const float* stat_m; const float* stat_s; const float* dloss; int ld2;
     // fp8 GEMM: device pointers to the per-tensor descales of A and B
     const float* descale_a; const float* descale_b;
+    // EPI_DGELU (bf16): if set, column sums of the stored output, one row per BM-row tile
+    // ([ceil(M / plan.bm)][N] floats)
+    float* colpart;
 };
 
 struct GemmPlan {
@@ -73,12 +76,13 @@ hipError_t gemm_bf16_tn(const GemmReq& r, const GemmPlan& p, void* ws, hipStream
 // Attention (bf16, head width d)
 // dp.thr = 0: no dropout; otherwise attention dropout with dp.mask written by attn_fwd, read by attn_bwd.
 // attn_bwd's dSws holds the bf16 score gradients between its two passes: attn_bwd_ds_bytes(b, s, heads_t)
-// bytes (every 64 x 64 block of every head; a causal mask uses a little over half).
+// bytes (every 64 x 64 block of every head; a causal mask uses a little over half). colpart (may be
+// null): column sums of the stored dQKV per 64-token tile, [b * ceil(s/64)][3 h_t] floats.
 hipError_t attn_fwd(int b, int s, int h_t, int heads_t, int d, int causal, const void* QKV, void* O, float* lse,
                     const DropParams& dp, hipStream_t st);
 hipError_t attn_bwd(int b, int s, int h_t, int heads_t, int d, int causal, const void* QKV, const void* O,
-                    const float* lse, const void* dO, float* Dws, void* dSws, void* dQKV, const DropParams& dp,
-                    hipStream_t st);
+                    const float* lse, const void* dO, float* Dws, void* dSws, void* dQKV, float* colpart,
+                    const DropParams& dp, hipStream_t st);
 size_t attn_bwd_ds_bytes(int b, int s, int heads_t);
 
 // Fused logits GEMM of a vocabulary shard (Vt rows x N tokens, depth K), in two launches: 256x256
@@ -120,6 +124,8 @@ hipError_t layernorm_bwd(int dt, int rows, int h, const void* x, const void* g, 
                          void* dres_sum, void* dx_sum, int accumulate, float* ws, hipStream_t st);
 int colsum_row_blocks(int rows);
 hipError_t colsum(int dt, int rows, int n, const void* G, void* out, int accumulate, float* ws, hipStream_t st);
+// out (+)= sum over the nb rows of part [nb][n] (n % 4 == 0), in a fixed order; nb = 0 gives zeros
+hipError_t colsum_reduce(int dt, int nb, int n, const float* part, void* out, int accumulate, hipStream_t st);
 hipError_t sum_partials(int in_dt, int out_dt, size_t rows, int cols, int t, const void* const* parts,
                         const void* bias, const void* residual, void* out, const DropParams& drop, hipStream_t st);
 // y = D(x) over [rows, n] (n % 8 == 0, in place allowed) and out (+)= column sums of y (fp32

@@ -148,6 +148,13 @@ hipError_t colsum(int dt, int rows, int n, const void* G, void* out, int accumul
                    : reduce_rows<float>(parts, outs, nb, n, accumulate, st);
 }
 
+hipError_t colsum_reduce(int dt, int nb, int n, const float* part, void* out, int accumulate, hipStream_t st) {
+    const float* parts[RR_JOBS] = {part, nullptr, nullptr, nullptr};
+    void* outs[RR_JOBS] = {out, nullptr, nullptr, nullptr};
+    return dt == 1 ? reduce_rows<bf16>(parts, outs, nb, n, accumulate, st)
+                   : reduce_rows<float>(parts, outs, nb, n, accumulate, st);
+}
+
 hipError_t dropout_colsum(int dt, int rows, int n, const void* x, void* y, const DropParams& dp, void* out,
                           int accumulate, float* ws, hipStream_t st) {
     int rb = colsum_row_blocks(rows);

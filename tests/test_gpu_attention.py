@@ -93,6 +93,43 @@ def test_attn_deterministic():
         assert bool((a[k] == c[k]).all()), k
 
 
+def test_attn_accumulate_and_optional_bias_grad():
+    """accumulate = 1 adds the new dWqkv, dbqkv and dWo to the old ones (dXn is overwritten); with
+    dbqkv = NULL the kernels skip their column sums and every other output is bit-identical."""
+    b, s, h, heads, t, r = 2, 200, 384, 4, 2, 1
+    inp = tp_synth.attn_inputs(95, b, s, h, "bf16", bias_std=0.2, w_std=0.05)
+    T, ht, dt = b * s, h // t, tp.TP_BF16
+    Xn, G = dev(inp["Xn"], "bf16"), dev(inp["G"], "bf16")
+    Wqkv_r = dev(oracle.qkv_shard(inp["Wqkv"], heads, t, r), "bf16")
+    bqkv_r = dev(oracle.qkv_shard(inp["bqkv"], heads, t, r), "bf16")
+    Wo_r = dev(oracle.wo_shard(inp["Wo"], heads, t, r), "bf16")
+    QKV, O, Z = empty((T, 3 * ht), "bf16"), empty((T, ht), "bf16"), empty((T, h), "bf16")
+    lse = empty((b, heads // t, s), "f32")
+    tp.tp_attn_shard_fwd(b, s, h, heads, t, r, dt, 1, Xn, Wqkv_r, bqkv_r, Wo_r, QKV, O, lse, Z)
+    nb = tp.tp_attn_shard_bwd_workspace(b, s, h, heads, t, dt)
+
+    def bwd(dbqkv, acc, prev=None):
+        o = dict(dXn=empty((T, h), "bf16"), dWqkv=empty((h, 3 * ht), "bf16"), dWo=empty((ht, h), "bf16"))
+        if prev is not None:
+            o["dWqkv"].copy_(prev["dWqkv"]); o["dWo"].copy_(prev["dWo"])
+        tp.tp_attn_shard_bwd(b, s, h, heads, t, r, dt, 1, Xn, Wqkv_r, Wo_r, QKV, O, lse, G, o["dXn"], o["dWqkv"],
+                             dbqkv, o["dWo"], acc, ws(nb), nb)
+        o["dbqkv"] = dbqkv
+        return o
+
+    first = bwd(empty((3 * ht,), "bf16"), 0)
+    nob = bwd(None, 0)
+    for k in ("dXn", "dWqkv", "dWo"):
+        assert bool((first[k] == nob[k]).all()), k
+    db = first["dbqkv"].clone()
+    second = bwd(db, 1, prev=first)
+    for k in ("dWqkv", "dWo", "dbqkv"):
+        e = rel_l2(host(second[k]), 2 * host(first[k]))
+        say(f"[attn] accumulate {k}: {e:.2e}")
+        assert e < 1e-2, k
+    assert bool((second["dXn"] == first["dXn"]).all())
+
+
 def _sampled_full_size(w, ranks_to_run, seq, tol=TOL):
     """Full-size shard: the oracle is run on one sequence (every head of the rank) and on one head
     (every sequence), which fixes sampled rows of Z, O, lse, dXn and sampled columns of the weight
