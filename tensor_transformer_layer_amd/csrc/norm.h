@@ -195,16 +195,43 @@ __global__ __launch_bounds__(256) void add_ln_fwd_kernel(int rows, int h, int t,
 }
 
 // ---------------------------------------------------------------------------------------------
-// LayerNorm backward: a block of ceil(h/512)*64 threads spans a row, 8 columns per thread
-// (h <= 8192), and takes RPI rows per iteration, fetched together (x, dy and dres of RPI rows in
-// flight per block). Row sums are wave butterflies followed by a sum over the block's waves in
-// wave order through LDS (double-buffered: one barrier per iteration). Block b takes rows
-// b*RPI + j + k*(RPI*nblocks); NTMAX bounds the block size, which sets the register budget.
-// dx is written per row; each thread accumulates, for its 8 columns over the block's rows, the
-// column sums wanted (dgamma, dbeta, and the plain sums of dres and of dx) and writes them as row
-// b of part_* [nblocks][h] (NULL: not wanted); they are reduced afterwards.
+// LayerNorm backward: a group of nt = ceil(h/512)*64 threads spans a row, 8 columns per thread
+// (h <= 8192); a block holds G groups (blockDim = G*nt). Each group takes RPI rows per iteration;
+// with PF the next iteration's rows (x, dy, dres, mean, rstd) are loaded while the current ones
+// are reduced and written, so two iterations are in flight per group. Row sums are wave
+// butterflies followed by a sum over the group's waves in wave order through LDS (double-buffered:
+// one barrier per iteration). Group g of block b takes rows (b*G + g)*RPI + j + k*(RPI*G*nblocks);
+// NTMAX bounds the block size, which sets the register budget. dx is written per row; each thread
+// accumulates, for its 8 columns over its group's rows, the column sums wanted (dgamma, dbeta,
+// and the plain sums of dres and of dx); the G groups' sums are added in group order through LDS
+// and written as row b of part_* [nblocks][h] (NULL: not wanted); they are reduced afterwards.
 // ---------------------------------------------------------------------------------------------
-template <typename T, int NTMAX, int RPI>
+template <typename T, int RPI>
+struct LnBwdRows {
+    Raw8<T> x[RPI], dy[RPI], dr[RPI];
+    float mu[RPI], rs[RPI];
+    __device__ __forceinline__ void load(int r0, int rows, int h, int c, bool act, const T* __restrict__ xp,
+                                         const T* __restrict__ dyp, const T* __restrict__ dresp,
+                                         const float* __restrict__ mean, const float* __restrict__ rstd) {
+#pragma unroll
+        for (int j = 0; j < RPI; ++j) {
+            const int row = r0 + j;
+            const size_t ro = (size_t)row * h + c;
+            if (act && row < rows) {
+                x[j].load(xp + ro);
+                dy[j].load(dyp + ro);
+                if (dresp) dr[j].load(dresp + ro);
+                else dr[j].zero();
+            } else {
+                x[j].zero(); dy[j].zero(); dr[j].zero();
+            }
+            mu[j] = row < rows ? mean[row] : 0.f;
+            rs[j] = row < rows ? rstd[row] : 0.f;
+        }
+    }
+};
+
+template <typename T, int NTMAX, int RPI, int G, bool PF>
 __global__ __launch_bounds__(NTMAX) void ln_bwd_kernel(int rows, int h, const T* __restrict__ x,
                                                       const T* __restrict__ gamma, const float* __restrict__ mean,
                                                       const float* __restrict__ rstd, const T* __restrict__ dy,
@@ -212,7 +239,8 @@ __global__ __launch_bounds__(NTMAX) void ln_bwd_kernel(int rows, int h, const T*
                                                       float* __restrict__ part_g, float* __restrict__ part_b,
                                                       float* __restrict__ part_r, float* __restrict__ part_x) {
     __shared__ float red[2][16][2 * RPI];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int nt = blockDim.x / G, grp = threadIdx.x / nt, tid = threadIdx.x - grp * nt;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwg = nt >> 6, w0 = grp * nwg;
     const int c = tid * 8;
     const bool act = c < h;
     const float inv_h = 1.0f / (float)h;
@@ -222,32 +250,14 @@ __global__ __launch_bounds__(NTMAX) void ln_bwd_kernel(int rows, int h, const T*
     float pg[8], pb[8], pr[8], px[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) { pg[e] = 0.f; pb[e] = 0.f; pr[e] = 0.f; px[e] = 0.f; }
-    int it = 0;
-    for (int r0 = blockIdx.x * RPI; r0 < rows; r0 += RPI * gridDim.x, ++it) {
-        Raw8<T> xr[RPI], dr[RPI], rr[RPI];
-        float mu[RPI], rs[RPI];
-#pragma unroll
-        for (int j = 0; j < RPI; ++j) {
-            const int row = r0 + j;
-            const size_t ro = (size_t)row * h + c;
-            if (act && row < rows) {
-                xr[j].load(x + ro);
-                dr[j].load(dy + ro);
-                if (dres) rr[j].load(dres + ro);
-                else rr[j].zero();
-            } else {
-                xr[j].zero(); dr[j].zero(); rr[j].zero();
-            }
-            mu[j] = row < rows ? mean[row] : 0.f;
-            rs[j] = row < rows ? rstd[row] : 0.f;
-        }
+    auto process = [&](const LnBwdRows<T, RPI>& b, int r0, int it) {
         float s[2 * RPI];
 #pragma unroll
         for (int j = 0; j < RPI; ++j) {
             float s1 = 0.f, s2 = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float xh = (xr[j][e] - mu[j]) * rs[j], d = dr[j][e];
+                float xh = (b.x[j][e] - b.mu[j]) * b.rs[j], d = b.dy[j][e];
                 float g = d * gm[e];
                 s1 += g;
                 s2 += g * xh;
@@ -257,7 +267,21 @@ __global__ __launch_bounds__(NTMAX) void ln_bwd_kernel(int rows, int h, const T*
             s[2 * j] = s1;
             s[2 * j + 1] = s2;
         }
-        block_sum<2 * RPI>(s, red[it & 1], lane, wave, nw);
+        // sum over the group's waves (every thread of the block reaches the barrier)
+        float (*rd)[2 * RPI] = red[it & 1];
+#pragma unroll
+        for (int k = 0; k < 2 * RPI; ++k) s[k] = wave_sum(s[k]);
+        if (lane == 0) {
+#pragma unroll
+            for (int k = 0; k < 2 * RPI; ++k) rd[wave][k] = s[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 2 * RPI; ++k) {
+            float a = rd[w0][k];
+            for (int w = 1; w < nwg; ++w) a += rd[w0 + w][k];
+            s[k] = a;
+        }
 #pragma unroll
         for (int j = 0; j < RPI; ++j) {
             const int row = r0 + j;
@@ -266,21 +290,68 @@ __global__ __launch_bounds__(NTMAX) void ln_bwd_kernel(int rows, int h, const T*
                 float o[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    float xh = (xr[j][e] - mu[j]) * rs[j];
-                    o[e] = rs[j] * (dr[j][e] * gm[e] - s1 - xh * s2) + rr[j][e];
-                    pr[e] += rr[j][e];
+                    float xh = (b.x[j][e] - b.mu[j]) * b.rs[j];
+                    o[e] = b.rs[j] * (b.dy[j][e] * gm[e] - s1 - xh * s2) + b.dr[j][e];
+                    pr[e] += b.dr[j][e];
                     px[e] += o[e];
                 }
                 store8(dx + (size_t)row * h + c, o);
             }
         }
+    };
+    // The loop bounds depend on blockIdx only (uniform), so every thread of the block reaches the
+    // same barriers; a group's rows past the end are masked. PF: two register sets, alternating.
+    const int stride = RPI * G * (int)gridDim.x;
+    int base = (int)blockIdx.x * G * RPI, it = 0;
+    const int off = grp * RPI;
+    if constexpr (PF) {
+        LnBwdRows<T, RPI> A, B;
+        if (base < rows) A.load(base + off, rows, h, c, act, x, dy, dres, mean, rstd);
+        while (base < rows) {
+            const int b1 = base + stride;
+            if (b1 < rows) B.load(b1 + off, rows, h, c, act, x, dy, dres, mean, rstd);
+            process(A, base + off, it++);
+            if (b1 >= rows) break;
+            const int b2 = b1 + stride;
+            if (b2 < rows) A.load(b2 + off, rows, h, c, act, x, dy, dres, mean, rstd);
+            process(B, b1 + off, it++);
+            base = b2;
+        }
+    } else {
+        for (; base < rows; base += stride) {
+            LnBwdRows<T, RPI> A;
+            A.load(base + off, rows, h, c, act, x, dy, dres, mean, rstd);
+            process(A, base + off, it++);
+        }
     }
-    if (!act) return;
+    // the groups' column sums, added in group order: group g > 0 hands its 8 values per column to
+    // group 0 through LDS, one job at a time
     const size_t po = (size_t)blockIdx.x * h + c;
-    if (part_g) store8(part_g + po, pg);
-    if (part_b) store8(part_b + po, pb);
-    if (part_r) store8(part_r + po, pr);
-    if (part_x) store8(part_x + po, px);
+    auto finish = [&](float* __restrict__ out, float (&v)[8]) {
+        if (!out) return;   // uniform
+        if constexpr (G > 1) {
+            __shared__ f32x4 xg[2][512];   // one group's 8 values per thread
+            static_assert(NTMAX / G <= 512, "group exchange buffer too small");
+            for (int g = 1; g < G; ++g) {
+                __syncthreads();
+                if (grp == g) {
+                    xg[0][tid] = f32x4{v[0], v[1], v[2], v[3]};
+                    xg[1][tid] = f32x4{v[4], v[5], v[6], v[7]};
+                }
+                __syncthreads();
+                if (grp == 0) {
+                    const f32x4 lo = xg[0][tid], hi = xg[1][tid];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { v[e] += lo[e]; v[4 + e] += hi[e]; }
+                }
+            }
+        }
+        if (grp == 0 && act) store8(out + po, v);
+    };
+    finish(part_g, pg);
+    finish(part_b, pb);
+    finish(part_r, pr);
+    finish(part_x, px);
 }
 
 // out_j[c] (+)= sum_{b=0}^{nb-1} part_j[b][c] for job j = blockIdx.y (n % 4 == 0). Block = 16

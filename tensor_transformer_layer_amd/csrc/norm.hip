@@ -72,10 +72,11 @@ hipError_t sum_partials_layernorm(int dt, int rows, int h, int t, const void* co
 // threads of a LayerNorm backward block: 8 columns each, whole waves
 static int ln_threads(int h) { return (h + 511) / 512 * 64; }
 
-// Blocks of the LayerNorm backward: at least eight rows each, at most 512 (partial rows).
+// Blocks of the LayerNorm backward: at least 32 rows each (16 per row group), at most 256 (one per
+// CU; fewer blocks also mean fewer column-sum partial rows to write and reduce).
 int ln_bwd_blocks(int rows) {
-    int nb = (rows + 7) / 8;
-    return nb < 512 ? (nb > 0 ? nb : 1) : 512;
+    int nb = (rows + 31) / 32;
+    return nb < 256 ? (nb > 0 ? nb : 1) : 256;
 }
 
 // out_j (+)= column sums of part_j [nb][n] for the non-null outputs (nb may be 0: zeros)
@@ -102,14 +103,21 @@ static hipError_t ln_bwd_t(int rows, int h, const void* x, const void* g, const 
     float* parts[RR_JOBS];
     for (int j = 0; j < RR_JOBS; ++j) parts[j] = outs[j] ? ws + (size_t)j * ln_bwd_blocks(rows) * h : nullptr;
     if (rows > 0) {
-        // two rows per iteration (measured faster than one or four at h = 3072)
+        // Up to 384 threads per row: two row groups per block, one row per iteration and group with
+        // the next in flight (two rows per group spill at this block size). Against one group of
+        // two rows per iteration on 512 blocks, inside the layer step at T = 8192, h = 3072 (inputs
+        // not in the MALL), kernel + reduction: 60.8 -> 53.0 us with dres and four column sums,
+        // 49.9 -> 47.5 us with two: ~4.5 TB/s, near a plain copy's 5.05. Up to 512 threads: one
+        // group, two rows, prefetched. Wider (register budget 128 per lane): no prefetch.
         const int nt = ln_threads(h);
-        if (nt <= 512)
-            hipLaunchKernelGGL((ln_bwd_kernel<T, 512, 2>), dim3(nb), dim3(nt), 0, st, rows, h, (const T*)x, (const T*)g,
-                               mean, rstd, (const T*)dy, (const T*)dres, (T*)dx, parts[0], parts[1], parts[2], parts[3]);
-        else
-            hipLaunchKernelGGL((ln_bwd_kernel<T, 1024, 2>), dim3(nb), dim3(nt), 0, st, rows, h, (const T*)x, (const T*)g,
-                               mean, rstd, (const T*)dy, (const T*)dres, (T*)dx, parts[0], parts[1], parts[2], parts[3]);
+#define TP_LN_BWD(NTMAX, RPI, G, PF)                                                                          \
+    hipLaunchKernelGGL((ln_bwd_kernel<T, NTMAX, RPI, G, PF>), dim3(nb), dim3(G * nt), 0, st, rows, h, (const T*)x,  \
+                       (const T*)g, mean, rstd, (const T*)dy, (const T*)dres, (T*)dx, parts[0], parts[1], parts[2],   \
+                       parts[3])
+        if (nt <= 384) TP_LN_BWD(768, 1, 2, true);
+        else if (nt <= 512) TP_LN_BWD(512, 2, 1, true);
+        else TP_LN_BWD(1024, 2, 1, false);
+#undef TP_LN_BWD
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
