@@ -174,7 +174,10 @@ void attn_fwd_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int h
     bf16* Kb = smem;
     bf16* Vb = smem + 2 * ATT_B * D;
     const int head = blockIdx.x % heads_t, bi = blockIdx.x / heads_t, qt = gridDim.y - 1 - blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    // the wave index through readfirstlane: everything derived from it (row group, loop parity,
+    // masks) is known uniform, so those branches are scalar instead of per-lane selects
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5,
+              l32 = lane & 31;
     const int grp = wave & 1, kp = wave >> 1;
     const size_t tok0 = (size_t)bi * s;
     const bf16* Qp = QKV + tok0 * ld + head * D;
@@ -424,7 +427,10 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
     bf16* Gb = smem + ATT_B * D;
     bf16* KVs = smem + 2 * ATT_B * D;
     const int head = blockIdx.x % heads_t, bi = blockIdx.x / heads_t, kt = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    // the wave index through readfirstlane: everything derived from it (row group, loop parity,
+    // masks) is known uniform, so those branches are scalar instead of per-lane selects
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5,
+              l32 = lane & 31;
     const int grp = wave & 1, qh = wave >> 1;
     const size_t tok0 = (size_t)bi * s;
     const bf16* Qp = QKV + tok0 * ld + head * D;
@@ -498,12 +504,21 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
             }
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                int qi = qh * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                float pv = fast_exp2(fmaf(sacc[v], scale_log2, -lse_s[qi]));
-                if (need_mask) {
-                    int q = q0 + qi;
-                    if ((causal && mykey > q) || mykey >= s) pv = 0.f;
+                const int qi = qh * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                sacc[v] = fast_exp2(fmaf(sacc[v], scale_log2, -lse_s[qi]));
+            }
+            if (need_mask) {   // uniform: one skipped block on the tiles that need no mask
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int q = q0 + qh * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    const bool masked = (causal && mykey > q) || mykey >= s;
+                    sacc[v] = masked ? 0.f : sacc[v];
                 }
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int qi = qh * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                const float pv = sacc[v];
                 if constexpr (DROP) {
                     const bool kb = (mk_s[qi][grp] >> l32) & 1u;
                     sacc[v] = kb ? pv * dp.scale : 0.0f;
@@ -634,7 +649,10 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, in
     bf16* Kb = sm;                      // key tiles of parity 0 | 1
     bf16* Sb = sm + 2 * ATT_B * D;      // their dS blocks
     const int head = blockIdx.x % heads_t, bi = blockIdx.x / heads_t, qt = gridDim.y - 1 - blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    // the wave index through readfirstlane: everything derived from it (row group, loop parity,
+    // masks) is known uniform, so those branches are scalar instead of per-lane selects
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5,
+              l32 = lane & 31;
     const int grp = wave & 1, kp = wave >> 1;
     const size_t tok0 = (size_t)bi * s;
     const bf16* Kp = QKV + tok0 * ld + h_t + head * D;
