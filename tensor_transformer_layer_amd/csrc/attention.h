@@ -54,13 +54,27 @@ constexpr int ATT_NT = 256;      // 4 waves: two 32-row groups x two loop-tile p
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// LDS tiles are row-major [64][D] bf16 with the 16-byte chunk index XOR-swizzled by
-// (row >> 2) & 3. Two access patterns are conflict-free on it: a 128-bit read of 8 consecutive
-// columns by 16 consecutive rows (MFMA operand with K along the columns), and the transposing
-// 64-bit read of a 4-row x 16-column block per 16-lane group (MFMA operand with K along the rows).
+// LDS tiles are row-major [64][D] bf16 with the 16-byte chunk index XOR-swizzled by a function of
+// the row's low four bits, chosen per width so that three access patterns are free of bank
+// conflicts (64 banks of 4 bytes; 128-bit accesses served 16 lanes at a time, 64-bit ones 32): the
+// 128-bit read of 8 consecutive columns by 32 consecutive rows (MFMA operand with K along the
+// columns), the transposing 64-bit read of 4-row x 16-column blocks (MFMA operand with K along the
+// rows), and row-major 16-byte stores of whole rows. Width 96 (192-byte rows): bits 2, 3 of the
+// row. Widths 64 and 192: bits 1, 2 and 1^3. Width 128: bits 0, 1, 0^2 and 1^3. (Row strides
+// that are multiples of 256 bytes, or of 128, put rows r and r + 2 on the same banks; the extra
+// terms separate them.) The XOR stays inside an aligned group of 4, 8 or 16 chunks, so it never
+// leaves the row.
+template <int D>
+__device__ __forceinline__ int att_swz(int row) {
+    const int b0 = row & 1, b1 = (row >> 1) & 1, b2 = (row >> 2) & 1, b3 = (row >> 3) & 1;
+    if constexpr (D == 128) return b0 | (b1 << 1) | ((b0 ^ b2) << 2) | ((b1 ^ b3) << 3);
+    else if constexpr (D == 64 || D == 192) return b1 | (b2 << 1) | ((b1 ^ b3) << 2);
+    else return (row >> 2) & 3;
+}
 template <int D>
 __device__ __forceinline__ int att_off(int row, int col) {
-    return row * D + ((((col >> 3) ^ ((row >> 2) & 3)) << 3) | (col & 7));
+    static_assert(D == 64 || D == 96 || D == 128 || D == 192, "tile width without a swizzle");
+    return row * D + ((((col >> 3) ^ att_swz<D>(row)) << 3) | (col & 7));
 }
 
 // Register-staged copy of rows [r0, r0 + ROWS) x D of a strided bf16 matrix into consecutive LDS
@@ -671,12 +685,12 @@ void attn_bwd_dq_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, in
     // key tile reads zeros). Chunk c = ((g*2 + qh)*2 + kk)*64 + 32h + k of a block holds key 32g + k
     // and queries 32qh + 16kk + 4h + 0..3 and + 8 .. + 11 (the dK/dV kernel's accumulator order);
     // it goes to the [key][query] tile as two 8-byte pieces. Pass u = 4j + wave covers block u/8,
-    // key group (u/4)%2, keys 8(u%4) .. + 7; lane = key%8 + 8 (h + 2kk + 4qh), so a wave reads
-    // whole 128-byte lines and each LDS write puts two dwords on every bank.
+    // key group (u/4)%2, keys 8(u%4) .. + 7; lane = key%8 + 8 (h + 2qh + 4kk), so a wave reads
+    // whole 128-byte lines and the 8-byte LDS writes of each half-wave fall on distinct banks.
     u32x4 sr[4];
     auto ds_coords = [&](int j, int& blk, int& key, int& q0, int& c) {
         const int u = 4 * j + wave, g = (u >> 2) & 1, k = (u & 3) * 8 + (lane & 7), cb = lane >> 3;
-        const int hh = cb & 1, kk = (cb >> 1) & 1, qh = cb >> 2;
+        const int hh = cb & 1, qh = (cb >> 1) & 1, kk = cb >> 2;
         blk = u >> 3;
         key = g * 32 + k;
         q0 = qh * 32 + 16 * kk + 4 * hh;
