@@ -239,13 +239,14 @@ void attn_fwd_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int h
                                                                       frag_rows<D>(Qs, grp * 32, ks * 16, lane),
                                                                       st[sub], 0, 0, 0);
             }
-            if (need_mask) {
+            if (need_mask) {   // uniform: tiles with every key visible skip the block
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        int key = k0 + sub * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                        if ((causal && key > myq) || key >= s) st[sub][v] = -INFINITY;
+                        const int key = k0 + sub * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                        const bool masked = (causal && key > myq) || key >= s;
+                        st[sub][v] = masked ? -INFINITY : st[sub][v];
                     }
             }
             float mx = -INFINITY;
