@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libtpshard.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "gemm_plan.cpp", "gemm_nn.hip", "gemm_nt.hip", "gemm_tn.hip", "gemm_f32.hip",
+SOURCES = ["abi.cpp", "gemm_plan.cpp", "gemm_nn.hip", "gemm_nt.hip", "gemm_tn.hip", "gemm_pair.hip", "gemm_f32.hip",
            "gemm_fp8.hip", "fp8.hip", "embedding.hip", "attention.hip", "xent.hip", "norm.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

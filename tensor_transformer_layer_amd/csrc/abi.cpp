@@ -167,7 +167,15 @@ AttnWs attn_ws(int b, int s, int h, int heads_t, int h_t) {
     w.dO = al256((size_t)T * h_t * 2);
     w.D = al256((size_t)b * heads_t * s * sizeof(float));
     w.dQKV = al256((size_t)T * 3 * h_t * 2);
-    w.partWo = al256(wgrad_split_ws(TP_BF16, h_t, h, (int)T));
+    // dWo split partials: its own plan's, or those of the launch paired with the dO GEMM
+    size_t pw = wgrad_split_ws(TP_BF16, h_t, h, (int)T);
+    {
+        GemmReq r1 = req((int)T, h_t, h, nullptr, h, 0, nullptr, h, 0, EPI_STORE, nullptr, h_t);
+        GemmReq r2 = req(h_t, h, (int)T, nullptr, h_t, 1, nullptr, h, 1, EPI_STORE, nullptr, h);
+        int s2;
+        if (plan_gemm_pair(r1, r2, s2)) pw = std::max(pw, (size_t)s2 * h_t * h * sizeof(float));
+    }
+    w.partWo = al256(pw);
     w.partWqkv = al256(wgrad_split_ws(TP_BF16, h, 3 * h_t, (int)T));
     // dbqkv partials: one row per 64-token tile of each sequence (at least the column-sum pass's)
     w.col = al256(std::max(colsum_ws((int)T, 3 * h_t), (size_t)b * ((s + 63) / 64) * 3 * h_t * sizeof(float)));
@@ -360,13 +368,18 @@ tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dty
     void* partWqkv = base + w.dO + w.D + w.dQKV + w.partWo;
     float* colp = (float*)(base + w.dO + w.D + w.dQKV + w.partWo + w.partWqkv);
     void* dSw = base + w.dO + w.D + w.dQKV + w.partWo + w.partWqkv + w.col;
-    // dO = G Wo_r^T
+    // dO = G Wo_r^T and dWo_r = O_r^T G: independent, both thin (h/t columns or rows), so one
+    // paired launch when they fit one round of the CUs together
     GemmReq g = req(T, h_t, h, G, h, 0, Wo_r, h, 0, EPI_STORE, dO, h_t);
-    HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_bwd: dO GEMM");
-    // dWo_r = O_r^T G
-    g = req(h_t, h, T, O_r, h_t, 1, G, h, 1, EPI_STORE, dWo_r, h);
-    g.accumulate = accumulate;
-    HIP_TRY(run_gemm(dt, g, true, partWo, stream), "tp_attn_shard_bwd: dWo GEMM");
+    GemmReq gw = req(h_t, h, T, O_r, h_t, 1, G, h, 1, EPI_STORE, dWo_r, h);
+    gw.accumulate = accumulate;
+    int s2;
+    if (plan_gemm_pair(g, gw, s2)) {
+        HIP_TRY(gemm_bf16_pair(g, gw, s2, partWo, stream), "tp_attn_shard_bwd: dO + dWo GEMMs");
+    } else {
+        HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_attn_shard_bwd: dO GEMM");
+        HIP_TRY(run_gemm(dt, gw, true, partWo, stream), "tp_attn_shard_bwd: dWo GEMM");
+    }
     if (T > 0)
         HIP_TRY(attn_bwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, dO, Dv, dSw, dQKV, dbqkv_r ? colp : nullptr,
                          dp, stream),

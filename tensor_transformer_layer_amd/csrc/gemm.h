@@ -682,18 +682,17 @@ __device__ __forceinline__ void gemm_tiles_ms_tail(GemmState<C, LA, LB>& g, char
     }
 }
 
+// One work unit of the bf16 MFMA GEMM: unit bid of nblocks -> (output tile, K split), see map_unit.
 template <class C, int LA, int LB, class Epi>
-__global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restrict__ A, int lda,
-                                                             const bf16* __restrict__ B, int ldb,
-                                                             int M, int N, int K, int k_per_split,
-                                                             uint32_t a_bytes, uint32_t b_bytes, Epi epi) {
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+__device__ __forceinline__ void gemm_unit(const bf16* __restrict__ A, int lda, const bf16* __restrict__ B, int ldb,
+                                          int M, int N, int K, int k_per_split, uint32_t a_bytes, uint32_t b_bytes,
+                                          const Epi& epi, int bid, int nblocks, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WGN, wn = wave % C::WGN;
     const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
     int tm, tn;
     int split;
-    map_unit(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn, split);
+    map_unit(bid, nblocks, tiles_m, tiles_n, tm, tn, split);
     Epi ep = epi;
     ep.set_split(split);
 
@@ -749,6 +748,40 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restr
         __syncthreads();
     }
     ep.template apply<C>(acc, g.m0, g.n0, g.m0 + wm * C::WM, g.n0 + wn * C::WN, lane, M, N, smem);
+}
+
+template <class C, int LA, int LB, class Epi>
+__global__ __launch_bounds__(C::NT, 1) void gemm_bf16_kernel(const bf16* __restrict__ A, int lda,
+                                                             const bf16* __restrict__ B, int ldb,
+                                                             int M, int N, int K, int k_per_split,
+                                                             uint32_t a_bytes, uint32_t b_bytes, Epi epi) {
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    gemm_unit<C, LA, LB, Epi>(A, lda, B, ldb, M, N, K, k_per_split, a_bytes, b_bytes, epi, (int)blockIdx.x,
+                              (int)gridDim.x, smem);
+}
+
+// Operands and epilogue of one GEMM of a paired launch.
+template <class Epi> struct GemmArgs {
+    const bf16* A; int lda; const bf16* B; int ldb;
+    int M, N, K, k_per_split;
+    uint32_t a_bytes, b_bytes;
+    Epi epi;
+};
+
+// Two independent GEMMs with the same tile configuration in one launch: blocks [0, n1) are the
+// first GEMM's units, the rest the second's (each mapped as in its own launch). For two GEMMs
+// that each leave most of the chip idle, so that their units share the CUs instead of running
+// one after the other.
+template <class C, int LA1, int LB1, class E1, int LA2, int LB2, class E2>
+__global__ __launch_bounds__(C::NT, 1) void gemm_bf16_pair_kernel(GemmArgs<E1> p, GemmArgs<E2> q, int n1) {
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    const int bid = (int)blockIdx.x;
+    if (bid < n1)
+        gemm_unit<C, LA1, LB1, E1>(p.A, p.lda, p.B, p.ldb, p.M, p.N, p.K, p.k_per_split, p.a_bytes, p.b_bytes, p.epi,
+                                   bid, n1, smem);
+    else
+        gemm_unit<C, LA2, LB2, E2>(q.A, q.lda, q.B, q.ldb, q.M, q.N, q.K, q.k_per_split, q.a_bytes, q.b_bytes, q.epi,
+                                   bid - n1, (int)gridDim.x - n1, smem);
 }
 
 // ----------------------------------------------------------------------------------------------

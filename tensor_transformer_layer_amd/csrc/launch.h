@@ -55,6 +55,13 @@ size_t split_ws_bytes(const GemmPlan& p, int M, int N);
 // Launch one bf16 GEMM (+ split-K reduction if the plan has splits). ws must hold
 // split_ws_bytes(plan) bytes when plan.splits > 1.
 hipError_t gemm_bf16(const GemmReq& r, const GemmPlan& plan, void* ws, hipStream_t st);
+// Two independent GEMMs in one launch on 128x128 tiles: r1 with both operands K-contiguous and a
+// plain store, r2 with both MN-contiguous, split splits2 ways over K (fp32 partials in ws2,
+// split_ws_bytes bytes for that split count, reduced in split order after). plan_gemm_pair says
+// whether the pair fits one round of two workgroups per CU with comparable work per unit (and
+// gives splits2); otherwise the two run as ordinary GEMMs.
+bool plan_gemm_pair(const GemmReq& r1, const GemmReq& r2, int& splits2);
+hipError_t gemm_bf16_pair(const GemmReq& r1, const GemmReq& r2, int splits2, void* ws2, hipStream_t st);
 // Launch one fp32 SIMT GEMM.
 hipError_t gemm_f32(const GemmReq& r, hipStream_t st);
 
