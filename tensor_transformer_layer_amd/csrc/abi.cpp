@@ -287,16 +287,22 @@ tp_status tp_mlp_shard_bwd(int T, int h, int ffn, int t, int r, tp_dtype dt, con
     const bool fused_db1 = db1_r && dt == TP_BF16;
     if (fused_db1) g.colpart = colp;
     HIP_TRY(run_gemm(dt, g, false, nullptr, stream), "tp_mlp_shard_bwd: dU GEMM");
-    if (fused_db1) {
-        const int bm = plan_gemm_bf16(T, Ft, h, false).bm;
-        HIP_TRY(colsum_reduce(1, T > 0 ? (T + bm - 1) / bm : 0, Ft, colp, db1_r, accumulate, stream),
-                "tp_mlp_shard_bwd: db1");
-    } else if (db1_r) {
-        HIP_TRY(colsum(0, T, Ft, dU, db1_r, accumulate, colp, stream), "tp_mlp_shard_bwd: db1");
-    }
-    // dB_r = Y_r^T G
+    // dB_r = Y_r^T G; db1 = the sum of dU's per-tile column sums, added by the dB GEMM's split-K
+    // reduction launch when it has one, else by a launch of its own
     g = req(Ft, h, T, Y_r, Ft, 1, G, h, 1, EPI_STORE, dB_r, h);
     g.accumulate = accumulate;
+    bool db1_done = !db1_r;
+    if (fused_db1) {
+        const int bm = plan_gemm_bf16(T, Ft, h, false).bm, nb = T > 0 ? (T + bm - 1) / bm : 0;
+        if (T > 0 && plan_gemm_bf16(Ft, h, T, true).splits > 1) {
+            g.cs_part = colp; g.cs_out = db1_r; g.cs_nb = nb; g.cs_n = Ft; g.cs_accumulate = accumulate;
+            db1_done = true;
+        } else {
+            HIP_TRY(colsum_reduce(1, nb, Ft, colp, db1_r, accumulate, stream), "tp_mlp_shard_bwd: db1");
+            db1_done = true;
+        }
+    }
+    if (!db1_done) HIP_TRY(colsum(0, T, Ft, dU, db1_r, accumulate, colp, stream), "tp_mlp_shard_bwd: db1");
     HIP_TRY(run_gemm(dt, g, true, partB, stream), "tp_mlp_shard_bwd: dB GEMM");
     // dA_r = X^T dU
     g = req(h, Ft, T, X, h, 1, dU, Ft, 1, EPI_STORE, dA_r, Ft);
@@ -384,13 +390,18 @@ tp_status tp_attn_shard_bwd(int b, int s, int h, int heads, int t, int r, tp_dty
         HIP_TRY(attn_bwd(b, s, h_t, heads_t, d, causal, QKV_r, O_r, lse_r, dO, Dv, dSw, dQKV, dbqkv_r ? colp : nullptr,
                          dp, stream),
                 "tp_attn_shard_bwd: attention backward");
-    // dbqkv = column sums of dQKV, from the attention backward's per-tile sums
-    if (dbqkv_r)
-        HIP_TRY(colsum_reduce(1, T > 0 ? b * ((s + 63) / 64) : 0, 3 * h_t, colp, dbqkv_r, accumulate, stream),
-                "tp_attn_shard_bwd: dbqkv");
-    // dWqkv_r = Xn^T dQKV
+    // dWqkv_r = Xn^T dQKV; dbqkv = the sum of the attention backward's per-tile column sums of dQKV,
+    // added by the dWqkv GEMM's split-K reduction launch when it has one, else by a launch of its own
     g = req(h, 3 * h_t, T, Xn, h, 1, dQKV, 3 * h_t, 1, EPI_STORE, dWqkv_r, 3 * h_t);
     g.accumulate = accumulate;
+    if (dbqkv_r) {
+        const int nb = T > 0 ? b * ((s + 63) / 64) : 0;
+        if (T > 0 && plan_gemm_bf16(h, 3 * h_t, T, true).splits > 1) {
+            g.cs_part = colp; g.cs_out = dbqkv_r; g.cs_nb = nb; g.cs_n = 3 * h_t; g.cs_accumulate = accumulate;
+        } else {
+            HIP_TRY(colsum_reduce(1, nb, 3 * h_t, colp, dbqkv_r, accumulate, stream), "tp_attn_shard_bwd: dbqkv");
+        }
+    }
     HIP_TRY(run_gemm(dt, g, true, partWqkv, stream), "tp_attn_shard_bwd: dWqkv GEMM");
     // dXn_r = dQKV Wqkv_r^T
     g = req(T, h, 3 * h_t, dQKV, 3 * h_t, 0, Wqkv_r, 3 * h_t, 0, EPI_STORE, dXn_r, h);

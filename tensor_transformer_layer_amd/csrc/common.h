@@ -81,4 +81,42 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// out[c] (+)= sum_{b=0}^{nb-1} part[b][c] over the 16 columns of column block cb (n % 4 == 0), by a
+// block of 256 threads: 4 columns per thread x 64 row phases; phase p sums rows p, p+64, ... in
+// order, then the 64 phase sums are added in a fixed pairwise tree. Every thread of the block calls it.
+constexpr int RR_COLS = 16;
+template <typename T>
+__device__ __forceinline__ void rowsum_block(const float* __restrict__ part, T* __restrict__ out, int nb, int n,
+                                             int accumulate, int cb) {
+    __shared__ f32x4 red[64][4];
+    const int cg = threadIdx.x & 3, ph = threadIdx.x >> 2;
+    const int c = cb * RR_COLS + cg * 4;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    if (c < n) {
+#pragma unroll 8
+        for (int b = ph; b < nb; b += 64) a += *(const f32x4*)(part + (size_t)b * n + c);
+    }
+    red[ph][cg] = a;
+    __syncthreads();
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) {
+        if (ph < s) red[ph][cg] += red[ph + s][cg];
+        __syncthreads();
+    }
+    if (ph == 0 && c < n) {
+        f32x4 r = red[0][cg];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = r[e];
+            if (accumulate) v += to_f32(out[c + e]);
+            out[c + e] = from_f32<T>(v);
+        }
+    }
+}
+
+// A column-sum job (bf16 output) carried by another kernel's launch as extra blocks.
+struct ColSumJob {
+    const float* part; void* out; int nb, n, accumulate;
+};
+
 }  // namespace tp

@@ -844,10 +844,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }
 
 // Split-K reduction: out = epi(sum_{s=0}^{splits-1} part[s][r*N + c]) in split order, 8 columns
-// per thread (N % 8 == 0).
+// per thread (N % 8 == 0), in blocks [0, nsk). Blocks past nsk run a column-sum job carried by the
+// launch (rowsum_block over its column blocks), so that a small reduction whose inputs are ready
+// needs no launch of its own.
 template <class Epi>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
-                                                            size_t split_stride, int M, int N, Epi epi) {
+                                                            size_t split_stride, int M, int N, Epi epi, ColSumJob cj,
+                                                            int nsk) {
+    if ((int)blockIdx.x >= nsk) {
+        rowsum_block<bf16>(cj.part, (bf16*)cj.out, cj.nb, cj.n, cj.accumulate, (int)blockIdx.x - nsk);
+        return;
+    }
     const size_t idx = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (idx >= (size_t)M * N) return;
     const int r = (int)(idx / N), c = (int)(idx % N);

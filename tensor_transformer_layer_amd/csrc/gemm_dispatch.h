@@ -9,13 +9,18 @@ namespace tp {
 
 static inline int cdiv_h(long a, long b) { return (int)((a + b - 1) / b); }
 
-// out = sum of the split partials in ws, in split order, through the plain bf16 store epilogue
+// out = sum of the split partials in ws, in split order, through the plain bf16 store epilogue;
+// the request's column-sum job (r.cs_out set), if any, rides along as extra blocks
 static inline hipError_t launch_splitk_reduce(const GemmReq& r, const GemmPlan& p, const void* ws, hipStream_t st) {
     EpiStore<bf16> fin{(bf16*)r.out, r.ldc, (const bf16*)r.bias, r.accumulate};
     size_t n = (size_t)r.M * r.N;
     if (n == 0 || p.splits <= 1) return hipSuccess;
-    hipLaunchKernelGGL((splitk_reduce_kernel<EpiStore<bf16>>), dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, st,
-                       (const float*)ws, p.splits, n, r.M, r.N, fin);
+    const unsigned nsk = (unsigned)((n / 8 + 255) / 256);
+    ColSumJob cj{r.cs_part, r.cs_out, r.cs_nb, r.cs_n, r.cs_accumulate};
+    const unsigned ncs = r.cs_out ? (unsigned)((r.cs_n + RR_COLS - 1) / RR_COLS) : 0u;
+    if (r.cs_out && r.cs_n % 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((splitk_reduce_kernel<EpiStore<bf16>>), dim3(nsk + ncs), dim3(256), 0, st, (const float*)ws,
+                       p.splits, n, r.M, r.N, fin, cj, (int)nsk);
     return hipGetLastError();
 }
 

@@ -216,8 +216,9 @@ hipError_t gemm_fp8(const GemmReq& r, const GemmPlan& p, void* ws, hipStream_t s
         if (err != hipSuccess) return err;
         EpiStore<bf16> fin{(bf16*)r.out, r.ldc, (const bf16*)r.bias, r.accumulate};
         const size_t n = (size_t)r.M * r.N;
-        hipLaunchKernelGGL((splitk_reduce_kernel<EpiStore<bf16>>), dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0,
-                           st, (const float*)ws, p.splits, n, r.M, r.N, fin);
+        const unsigned nsk = (unsigned)((n / 8 + 255) / 256);
+        hipLaunchKernelGGL((splitk_reduce_kernel<EpiStore<bf16>>), dim3(nsk), dim3(256), 0, st, (const float*)ws,
+                           p.splits, n, r.M, r.N, fin, ColSumJob{nullptr, nullptr, 0, 0, 0}, (int)nsk);
         return hipGetLastError();
     }
     switch (r.epi) {

@@ -37,6 +37,10 @@ struct GemmReq {
     // EPI_DGELU (bf16): if set, column sums of the stored output, one row per BM-row tile
     // ([ceil(M / plan.bm)][N] floats)
     float* colpart;
+    // bf16 GEMMs with split-K: an unrelated column-sum job run by the split-K reduction's launch,
+    // cs_out (bf16 [cs_n]) (+)= sums over the cs_nb rows of cs_part [cs_nb][cs_n] (cs_n % 4 == 0).
+    // Only for plans with splits > 1 (without splits there is no reduction launch to carry it).
+    const float* cs_part; void* cs_out; int cs_nb, cs_n, cs_accumulate;
 };
 
 struct GemmPlan {

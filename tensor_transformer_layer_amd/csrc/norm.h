@@ -354,40 +354,13 @@ __global__ __launch_bounds__(NTMAX) void ln_bwd_kernel(int rows, int h, const T*
     finish(part_x, px);
 }
 
-// out_j[c] (+)= sum_{b=0}^{nb-1} part_j[b][c] for job j = blockIdx.y (n % 4 == 0). Block = 16
-// columns (4 per thread) x 64 row phases: phase p sums rows p, p+64, ... in order, then the 64
-// phase sums are added in a fixed pairwise tree.
-constexpr int RR_COLS = 16;
+// out_j[c] (+)= sum_{b=0}^{nb-1} part_j[b][c] for job j = blockIdx.y (n % 4 == 0): rowsum_block over
+// column block blockIdx.x.
 constexpr int RR_JOBS = 4;
 struct RowSumJobs { const float* part[RR_JOBS]; void* out[RR_JOBS]; };
 template <typename T>
 __global__ __launch_bounds__(256) void reduce_rows_kernel(RowSumJobs jobs, int nb, int n, int accumulate) {
-    __shared__ f32x4 red[64][4];
-    const float* __restrict__ part = jobs.part[blockIdx.y];
-    T* __restrict__ out = (T*)jobs.out[blockIdx.y];
-    const int cg = threadIdx.x & 3, ph = threadIdx.x >> 2;
-    const int c = blockIdx.x * RR_COLS + cg * 4;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    if (c < n) {
-#pragma unroll 8
-        for (int b = ph; b < nb; b += 64) a += *(const f32x4*)(part + (size_t)b * n + c);
-    }
-    red[ph][cg] = a;
-    __syncthreads();
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) {
-        if (ph < s) red[ph][cg] += red[ph + s][cg];
-        __syncthreads();
-    }
-    if (ph == 0 && c < n) {
-        f32x4 r = red[0][cg];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float v = r[e];
-            if (accumulate) v += to_f32(out[c + e]);
-            out[c + e] = from_f32<T>(v);
-        }
-    }
+    rowsum_block<T>(jobs.part[blockIdx.y], (T*)jobs.out[blockIdx.y], nb, n, accumulate, (int)blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------------------------
