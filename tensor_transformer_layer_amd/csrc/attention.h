@@ -79,8 +79,9 @@ __device__ __forceinline__ int att_off(int row, int col) {
 
 // Register-staged copy of rows [r0, r0 + ROWS) x D of a strided bf16 matrix into consecutive LDS
 // tiles (row r lands in tile r / 64; att_off is valid across them). Loads go through a buffer
-// resource covering the sequence's rows: rows >= valid are fetched at an offset past the end,
-// which reads 0, so there is no branch per load.
+// resource covering exactly the sequence's `valid` rows (att_rsrc): a row index clamped to `valid`
+// starts at or past the resource's end (the row stride is at least D), so rows >= valid read 0
+// with no compare or branch per load.
 template <int D, int ROWS = 2 * ATT_B>
 struct AttTileRegs {
     static constexpr int CPR = D / 8, N = ROWS * CPR / ATT_NT;
@@ -90,7 +91,7 @@ struct AttTileRegs {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int c = tid + i * ATT_NT, row = c / CPR, dc = c % CPR;
-            const int off = (r0 + row < valid) ? ((r0 + row) * ld + dc * 8) * 2 : 0x7fffffff;
+            const int off = (min(r0 + row, valid) * ld + dc * 8) * 2;
             v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
         }
     }
