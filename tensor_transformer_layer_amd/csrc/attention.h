@@ -112,17 +112,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t att_rsrc(const bf16* p, int ld
                                              0x00020000);
 }
 
-// Direct copy of rows [r0, r0 + 64) x D of a strided bf16 matrix into one LDS tile (rows >= valid
+// Copy of rows [r0, r0 + 64) x D of a strided bf16 matrix into one LDS tile (rows >= valid
 // read 0); used once per block for the block's own rows, which then serve as MFMA operands
 // straight from LDS instead of occupying registers.
 template <int D>
 __device__ __forceinline__ void load_tile(const bf16* __restrict__ src, int ld, int r0, int valid, bf16* tile, int tid) {
-    constexpr int CPR = D / 8;
-    for (int c = tid; c < ATT_B * CPR; c += ATT_NT) {
-        const int row = c / CPR, dc = c % CPR;
-        const u32x4 v = (r0 + row < valid) ? *(const u32x4*)(src + (size_t)(r0 + row) * ld + dc * 8) : u32x4{0, 0, 0, 0};
-        *(u32x4*)(tile + att_off<D>(row, dc * 8)) = v;
-    }
+    AttTileRegs<D, ATT_B> r;   // every load issued before the first store
+    r.load(att_rsrc<D>(src, ld, valid), ld, r0, valid, tid);
+    r.store(tile, tid);
 }
 
 // MFMA operand with the tile's rows as M and its columns as K: rows row0 + lane%32, columns
@@ -201,20 +198,22 @@ void attn_fwd_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, int h
     const int q0w = qt * ATT_B + grp * 32;
     const int myq = q0w + l32;
 
-    load_tile<D>(Qp, ld, qt * ATT_B, s, Qs, tid);
-    f32x16 o[D / 32];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
-    float m_i = -INFINITY, l_i = 0.f;
-
     const int kv_end = causal ? min(s, (qt + 1) * ATT_B) : s;
     const int ntiles = (kv_end + ATT_B - 1) / ATT_B;
     const int niter = (ntiles + 1) / 2;
     AttTileRegs<D> kr, vr;
     const auto krs = att_rsrc<D>(Kp, ld, s), vrs = att_rsrc<D>(Vp, ld, s);
+    // the first step's K/V loads and the block's Q tile are in flight together
     if (niter > 0) {
         kr.load(krs, ld, 0, s, tid);
         vr.load(vrs, ld, 0, s, tid);
+    }
+    load_tile<D>(Qp, ld, qt * ATT_B, s, Qs, tid);
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
+    float m_i = -INFINITY, l_i = 0.f;
+    if (niter > 0) {
         kr.store(Kb, tid);
         vr.store(Vb, tid);
     }
@@ -460,12 +459,6 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
 
     const bf16* Ks = KVs;
     const bf16* Vs = KVs + ATT_B * D;
-    load_tile<D>(Kp, ld, kt * ATT_B, s, KVs, tid);
-    load_tile<D>(Vp, ld, kt * ATT_B, s, KVs + ATT_B * D, tid);
-    f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) { dk[dt] = zero16(); dv[dt] = zero16(); }
-
     const int nqt = (s + ATT_B - 1) / ATT_B;
     const int qt0 = causal ? kt : 0;
     AttTileRegs<D, ATT_B> qr, gr;
@@ -496,7 +489,14 @@ void attn_bwd_dkdv_kernel(const bf16* __restrict__ QKV, int ld, int h_t, int s, 
             if (tid < 2 * ATT_B) mk_s[tid >> 1][tid & 1] = mk_r;
         }
     };
-    if (qt0 < nqt) { fetch(qt0 * ATT_B); stash(); }
+    // the first query tile's loads and the block's K/V tiles are in flight together
+    if (qt0 < nqt) fetch(qt0 * ATT_B);
+    load_tile<D>(Kp, ld, kt * ATT_B, s, KVs, tid);
+    load_tile<D>(Vp, ld, kt * ATT_B, s, KVs + ATT_B * D, tid);
+    f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) { dk[dt] = zero16(); dv[dt] = zero16(); }
+    if (qt0 < nqt) stash();
     __syncthreads();
     // this wave's two 1 KB chunks (kk = 0, 1) of dS block (kt, qt), in the accumulator's own order
     bf16* dsw = dSb + ((size_t)(bi * heads_t + head) * ds_pairs(nqt, causal) + ds_pair(kt, qt0, nqt, causal)) * (ATT_B * ATT_B) +
