@@ -251,7 +251,8 @@ __device__ __forceinline__ void apply_staged(const Op& op, f32x16 (&acc)[C::TM][
         for (int j = 0; j < C::TN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) slab[(8 * (v >> 2) + 4 * h + (v & 3)) * S::LD + j * 32 + l32] = acc[i][j][v];
-        __syncthreads();
+        // the slab is this wave's own and a wave's LDS accesses complete in order: no barrier
+        // between writing a strip, reading it back and writing the next
 #pragma unroll
         for (int q = 0; q < S::CHUNKS / 64; ++q) {
             const int c = q * 64 + lane, r = c / S::CPR, cc = c - r * S::CPR;
@@ -261,7 +262,6 @@ __device__ __forceinline__ void apply_staged(const Op& op, f32x16 (&acc)[C::TM][
             const int row = mw0 + i * 32 + r, col = nw0 + cc * 8;
             if (row < M && col < N) op.op8(row, col, v);
         }
-        __syncthreads();   // the strip is consumed before the next one overwrites it
     }
 }
 
