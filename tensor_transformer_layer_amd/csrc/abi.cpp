@@ -592,22 +592,38 @@ tp_status tp_vocab_xent_shard_bwd(int N, int h, int Vpad, int Vreal, int t, int 
     void* DT = (char*)ws + al256((size_t)Vt * ldd * 2);
     GemmReq g;
     if (N > 0) {
-        // 1. logits again (E_r X^T), their gradient in the epilogue, stored in both layouts
-        g = req(Vt, N, h, E_r, h, 0, X, h, 0, EPI_XENT_GRAD, D, ldd);
+        // 1. logits again (E_r X^T), their gradient in the epilogue, stored in both layouts; the
+        //    forward's tiling: whole rounds of 256x256 tiles, the remaining vocabulary rows on 64x64
+        const VocabPlan lp = plan_vocab(Vt, N, h);
+        g = req(lp.main_rows, N, h, E_r, h, 0, X, h, 0, EPI_XENT_GRAD, D, ldd);
         g.out2 = DT; g.ld2 = Vt;
         g.targets = targets; g.col0 = r * Vt; g.Vreal = Vreal; g.mask = mask_padding;
         g.stat_m = max_all; g.stat_s = sumexp_all; g.dloss = dloss;
-        HIP_TRY(gemm_bf16(g, plan_gemm_bf16(Vt, N, h, false), nullptr, stream),
-                "tp_vocab_xent_shard_bwd: logits gradient");
+        HIP_TRY(gemm_bf16(g, lp.main, nullptr, stream), "tp_vocab_xent_shard_bwd: logits gradient");
+        if (lp.main_rows < Vt) {
+            g.M = Vt - lp.main_rows;
+            g.A = (const char*)E_r + (size_t)lp.main_rows * h * 2;
+            g.out = (char*)D + (size_t)lp.main_rows * ldd * 2;
+            g.out2 = (char*)DT + (size_t)lp.main_rows * 2;
+            g.col0 = r * Vt + lp.main_rows;
+            HIP_TRY(gemm_bf16(g, lp.tail, nullptr, stream), "tp_vocab_xent_shard_bwd: logits gradient (last rows)");
+        }
         // 2. dX_r = dlogits E_r   (token-major dlogits, E_r read MN-contiguous)
         g = req(N, h, Vt, DT, Vt, 0, E_r, h, 1, EPI_STORE, dX_r, h);
         HIP_TRY(gemm_bf16(g, plan_gemm_bf16(N, h, Vt, false), nullptr, stream), "tp_vocab_xent_shard_bwd: dX GEMM");
     }
     // 3. dE_r (+)= dlogits^T X   (vocab-major dlogits, X read MN-contiguous; with no tokens the
     //    K = 0 product writes zeros, or leaves dE_r unchanged when accumulating)
-    g = req(Vt, h, N, D, ldd, 0, X, h, 1, EPI_STORE, dE_r, h);
+    const RowSplitPlan ep = plan_row_split(Vt, h, N, false);
+    g = req(ep.main_rows, h, N, D, ldd, 0, X, h, 1, EPI_STORE, dE_r, h);
     g.accumulate = accumulate;
-    HIP_TRY(gemm_bf16(g, plan_gemm_bf16(Vt, h, N, false), nullptr, stream), "tp_vocab_xent_shard_bwd: dE GEMM");
+    HIP_TRY(gemm_bf16(g, ep.main, nullptr, stream), "tp_vocab_xent_shard_bwd: dE GEMM");
+    if (ep.main_rows < Vt) {
+        g.M = Vt - ep.main_rows;
+        g.A = (const char*)D + (size_t)ep.main_rows * ldd * 2;
+        g.out = (char*)dE_r + (size_t)ep.main_rows * h * 2;
+        HIP_TRY(gemm_bf16(g, ep.tail, nullptr, stream), "tp_vocab_xent_shard_bwd: dE GEMM (last rows)");
+    }
     return ok();
 }
 

@@ -91,6 +91,26 @@ VocabPlan plan_vocab(int Vt, int N, int K) {
     return v;
 }
 
+RowSplitPlan plan_row_split(int M, int N, int K, bool both_kcontig) {
+    RowSplitPlan v;
+    v.main = plan_gemm_bf16(M, N, K, false);
+    v.main_rows = M;
+    v.tail = v.main;
+    const long tn = (N + v.main.bn - 1) / v.main.bn, tm = (M + v.main.bm - 1) / v.main.bm;
+    const long slots = (long)kCUs * (v.main.cfg == 1 ? 2 : 1);
+    const long rounds = tm * tn / slots;
+    if (v.main.splits != 1 || rounds == 0 || (tm * tn) % slots == 0 || (rounds * slots) % tn != 0) return v;
+    const long rows_main = rounds * slots / tn * v.main.bm;
+    if (rows_main >= M) return v;
+    // the remaining rows on small tiles: one round of them at two workgroups per CU
+    const GemmPlan tail = both_kcontig ? GemmPlan{3, 1, 64, 64} : GemmPlan{1, 1, 128, 128};
+    const long tail_tiles = ((M - rows_main + tail.bm - 1) / tail.bm) * ((N + tail.bn - 1) / tail.bn);
+    if (tail_tiles > 2L * kCUs) return v;
+    v.main_rows = (int)rows_main;
+    v.tail = tail;
+    return v;
+}
+
 size_t split_ws_bytes(const GemmPlan& p, int M, int N) {
     return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
 }

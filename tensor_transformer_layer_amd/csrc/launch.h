@@ -109,6 +109,16 @@ struct VocabPlan {
 };
 VocabPlan plan_vocab(int Vt, int N, int K);
 
+// A GEMM whose tiles leave a partly filled last round: rows [0, main_rows) in whole rounds of the
+// ordinary plan's tiles, rows [main_rows, M) in one round of small tiles (64x64 on four LDS stages
+// when both operands are K-contiguous, else 128x128), two launches in row order. main_rows = M
+// (one launch) when the ordinary plan fills whole rounds or the remainder does not fit one round.
+struct RowSplitPlan {
+    int main_rows;
+    GemmPlan main, tail;
+};
+RowSplitPlan plan_row_split(int M, int N, int K, bool both_kcontig);
+
 // Cross-entropy merge / combine
 hipError_t xent_merge(const void* part, int tiles_m, int N, int col0, float* mx, float* se, float* tg,
                       int32_t* am, hipStream_t st);
