@@ -57,6 +57,32 @@ def test_xent_bwd_small_ragged(mask):
     assert within(e, TOL)
 
 
+def test_xent_bwd_row_split_ragged():
+    """A shard large enough that both row splits of the backward engage, with ragged remainders:
+    N = 4096 tokens, h = 3072, Vreal = 10990 padded to 10992 for t = 2 (V_t = 5496), rank 1 (which
+    holds the padding rows) with the padding mask. The logits gradient runs 256x256 tiles over
+    vocabulary rows 0-4095 and 64x64 tiles over the last 1400 (56 rows in the last tile row); dE_r
+    runs one round of 256x192 tiles over rows 0-4095 and 128x128 tiles over the last 1400 (120 in
+    the last tile row). Every element of dX_r and dE_r against the oracle."""
+    N, h, Vreal, t, r = 4096, 3072, 10990, 2, 1
+    Vpad = oracle.pad_vocab(Vreal, t, multiple=8)
+    assert Vpad == 10992
+    Vt = Vpad // t
+    inp = tp_synth.xent_inputs(507, N, h, Vreal, Vpad, "bf16")
+    g = np.random.default_rng(508).uniform(0.5, 1.5, N) / N
+    M, S = oracle.xent_merged_stats(inp["X"], inp["E"], inp["targets"], Vreal, True)
+    dX, dE = run_bwd(inp, N, h, Vpad, Vreal, t, r, 1, M, S, g)
+    ref = oracle.xent_shard_grad(inp["X"], inp["E"][r * Vt:(r + 1) * Vt], inp["targets"], t, r, Vreal, True, M,
+                                 S, g)
+    e = {"dX_r": rel_l2(dX, ref["dX"]), "dE_r rows 0-4095": rel_l2(dE[:4096], ref["dE"][:4096]),
+         "dE_r rows 4096-5495": rel_l2(dE[4096:], ref["dE"][4096:])}
+    say("[xent-bwd] row split: " + " ".join(f"{k}={v!r}" for k, v in e.items()))
+    for k, v in e.items():
+        assert within(v, TOL), (k, v)
+    pad = np.arange(Vt) + r * Vt >= Vreal
+    assert pad.sum() == 2 and np.all(dE[pad] == 0.0)
+
+
 def test_xent_bwd_chain_from_forward():
     """The whole chain on the device: per-rank statistics (forward), the merge with its M and S,
     then the backward; against the oracle computed from the inputs alone."""
