@@ -785,60 +785,76 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_bf16_pair_kernel(GemmArgs<E1> p
 }
 
 // ----------------------------------------------------------------------------------------------
-// fp32 SIMT kernel: 64x64 tile, BK = 16, 256 threads, 4x4 outputs per thread.
+// fp32 SIMT kernel: TS x TS tile (64 or 32), BK = 16, 256 threads, (TS/16)^2 outputs per thread.
+// The next K step's operand elements are fetched into registers while the current one is
+// multiplied from LDS, so a step waits on global memory only once at the start.
 // ----------------------------------------------------------------------------------------------
-template <int LA, int LB, class Epi>
+template <int TS, int LA, int LB, class Epi>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int lda,
                                                        const float* __restrict__ B, int ldb,
                                                        int M, int N, int K, int k_per_split, Epi epi) {
-    __shared__ float As[16][64 + 4];
-    __shared__ float Bs[16][64 + 4];
+    static_assert(TS == 64 || TS == 32, "tile size");
+    constexpr int R = TS / 16;   // outputs per thread per dimension, and elements per operand per step
+    __shared__ float As[16][TS + 4];
+    __shared__ float Bs[16][TS + 4];
     const int tid = threadIdx.x;
-    const int tiles_n = (N + 63) / 64;
-    const int m0 = (blockIdx.x / tiles_n) * 64, n0 = (blockIdx.x % tiles_n) * 64;
+    const int tiles_n = (N + TS - 1) / TS;
+    const int m0 = (blockIdx.x / tiles_n) * TS, n0 = (blockIdx.x % tiles_n) * TS;
     const int kbeg = blockIdx.y * k_per_split, kend = min(K, kbeg + k_per_split);
     Epi ep = epi;
     ep.set_split(blockIdx.y);
     const int ty = tid / 16, tx = tid % 16;
-    float acc[4][4] = {};
-    for (int k0 = kbeg; k0 < kend; k0 += 16) {
-        // 64 x 16 elements of each operand, 4 per thread
+    // element i of this thread's share of a TS x 16 operand slab: (mn, k)
+    auto coord = [&](int layout, int i, int& mn, int& k) {
+        const int e = tid + i * 256;
+        if (layout == KCONTIG) { mn = e / 16; k = e % 16; } else { k = e / TS; mn = e % TS; }
+    };
+    float ra[R], rb[R];
+    auto fetch = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int e = tid + i * 256;
+        for (int i = 0; i < R; ++i) {
             int mn, k;
-            if (LA == KCONTIG) { mn = e / 16; k = e % 16; } else { k = e / 64; mn = e % 64; }
-            int gm = m0 + mn, gk = k0 + k;
-            float va = 0.f;
-            if (gm < M && gk < kend) va = (LA == KCONTIG) ? A[(size_t)gm * lda + gk] : A[(size_t)gk * lda + gm];
-            As[k][mn] = va;
-            if (LB == KCONTIG) { mn = e / 16; k = e % 16; } else { k = e / 64; mn = e % 64; }
-            int gn = n0 + mn;
-            gk = k0 + k;
-            float vb = 0.f;
-            if (gn < N && gk < kend) vb = (LB == KCONTIG) ? B[(size_t)gn * ldb + gk] : B[(size_t)gk * ldb + gn];
-            Bs[k][mn] = vb;
+            coord(LA, i, mn, k);
+            const int gm = m0 + mn, gk = k0 + k;
+            ra[i] = (gm < M && gk < kend) ? ((LA == KCONTIG) ? A[(size_t)gm * lda + gk] : A[(size_t)gk * lda + gm]) : 0.f;
+            coord(LB, i, mn, k);
+            const int gn = n0 + mn, gkb = k0 + k;
+            rb[i] = (gn < N && gkb < kend) ? ((LB == KCONTIG) ? B[(size_t)gn * ldb + gkb] : B[(size_t)gkb * ldb + gn])
+                                           : 0.f;
+        }
+    };
+    float acc[R][R] = {};
+    if (kbeg < kend) fetch(kbeg);
+    for (int k0 = kbeg; k0 < kend; k0 += 16) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            int mn, k;
+            coord(LA, i, mn, k);
+            As[k][mn] = ra[i];
+            coord(LB, i, mn, k);
+            Bs[k][mn] = rb[i];
         }
         __syncthreads();
+        if (k0 + 16 < kend) fetch(k0 + 16);
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-            float a[4], b[4];
+            float a[R], b[R];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = As[k][ty * 4 + i];
+            for (int i = 0; i < R; ++i) a[i] = As[k][ty * R + i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = Bs[k][tx * 4 + j];
+            for (int j = 0; j < R; ++j) b[j] = Bs[k][tx * R + j];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < R; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < R; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int r = m0 + ty * 4 + i, c = n0 + tx * 4 + j;
+        for (int j = 0; j < R; ++j) {
+            int r = m0 + ty * R + i, c = n0 + tx * R + j;
             if (r < M && c < N) ep(r, c, acc[i][j]);
         }
 }

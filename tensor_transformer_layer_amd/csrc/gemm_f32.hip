@@ -4,12 +4,20 @@
 
 namespace tp {
 
+// 64x64 tiles, or 32x32 when 64x64 would give fewer than 128 workgroups (the small fp32 shapes are
+// bound by the latency of their K loop, so more and shorter-running workgroups pay)
 template <int LA, int LB, class Epi>
 static hipError_t f32_launch(const GemmReq& r, const Epi& e, hipStream_t st) {
-    int tiles = ((r.M + 63) / 64) * ((r.N + 63) / 64);
-    if (tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_f32_kernel<LA, LB, Epi>), dim3(tiles, 1), dim3(256), 0, st, (const float*)r.A, r.lda,
-                       (const float*)r.B, r.ldb, r.M, r.N, r.K, r.K, e);
+    const int tiles64 = ((r.M + 63) / 64) * ((r.N + 63) / 64);
+    if (tiles64 == 0) return hipSuccess;
+    if (tiles64 >= 128) {
+        hipLaunchKernelGGL((gemm_f32_kernel<64, LA, LB, Epi>), dim3(tiles64, 1), dim3(256), 0, st, (const float*)r.A,
+                           r.lda, (const float*)r.B, r.ldb, r.M, r.N, r.K, r.K, e);
+    } else {
+        const int tiles32 = ((r.M + 31) / 32) * ((r.N + 31) / 32);
+        hipLaunchKernelGGL((gemm_f32_kernel<32, LA, LB, Epi>), dim3(tiles32, 1), dim3(256), 0, st, (const float*)r.A,
+                           r.lda, (const float*)r.B, r.ldb, r.M, r.N, r.K, r.K, e);
+    }
     return hipGetLastError();
 }
 
