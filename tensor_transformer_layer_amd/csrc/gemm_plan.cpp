@@ -31,6 +31,9 @@ static const TunedPlan kTuned[] = {
     {3072, 1536, 8192, 1, 0, 3},   // dA
     {384, 3072, 8192, 1, 1, 6},    // dWo
     {3072, 1152, 8192, 1, 0, 4},   // dWqkv (240 units of 256x256)
+    // the 1.2B attention block (t = 2) and the 2.5B layer (t = 4)
+    {1536, 2304, 8192, 1, 0, 4},   // 1.2B dWqkv: 216 units of 256x256 (the model picks 432 of 128x128)
+    {1920, 1920, 8192, 1, 0, 4},   // 2.5B dB, dA: 256 units of 256x256 (the model picks 450 of 128x128)
 };
 
 // Time model over the three tile shapes and split counts: rounds of resident tiles x per-tile
