@@ -16,8 +16,9 @@ static const int kPerCU[kNCfg] = {1, 2, 1};
 static const int kCUs = 256;
 
 // Plans measured on MI355X for the GEMMs of the 8.3B-shape layer shard (t = 8) and its
-// vocabulary shard: the fastest of the three tile shapes and split counts 1..6 per shape
-// (layout-independent here). Other shapes use the time model below.
+// vocabulary shard (the fastest of the three tile shapes and split counts 1..6 per shape), and for
+// the weight gradients of the 1.2B attention block and the 2.5B layer where the model's pick was
+// slower (layout-independent here). Other shapes use the time model below.
 struct TunedPlan { int M, N, K, split_ok, cfg, splits; };
 static const TunedPlan kTuned[] = {
     {8192, 1536, 3072, 0, 2, 1},   // MLP GEMM1 fwd, dU
