@@ -795,50 +795,49 @@ def bench_fp8(args, tp, torch):
             return codes_t[ref[:-2]], desc[ref[:-2]]
         return codes[ref], desc[ref]
 
-    ev = {}
-
-    def timed(key, record, fn):
-        if record:
-            a = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-        fn()
-        if record:
-            b_ = torch.cuda.Event(enable_timing=True)
-            b_.record(stream)
-            ev.setdefault(key, []).append((a, b_))
-
-    def step(record):
+    def quantize_all():
         for name, rows, cols, std in FP8_TENSORS:
-            timed("quantize", record, lambda: tp.tp_fp8_quantize(
-                rows, cols, tp.TP_BF16, src[name], cols, codes[name], cols, codes_t[name], rows, None, desc[name],
-                qws, qws.numel()))
-        for name, M, N, K, a, b_, e in FP8_GEMMS:
-            (ca, da), (cb, db) = operand(a), operand(b_)
-            epi = {"store": tp.TP_EPI_STORE, "bias": tp.TP_EPI_STORE, "bias_gelu": tp.TP_EPI_BIAS_GELU,
-                   "dgelu": tp.TP_EPI_DGELU}[e]
-            timed(name, record, lambda: tp.tp_gemm_fp8(
-                M, N, K, ca, K, da, cb, K, db, epi, outs[name], out2 if e == "bias_gelu" else None, N,
-                bias.get(name), U if e == "dgelu" else None, 0, gws, gws.numel()))
+            tp.tp_fp8_quantize(rows, cols, tp.TP_BF16, src[name], cols, codes[name], cols, codes_t[name], rows, None,
+                               desc[name], qws, qws.numel())
+
+    def gemm_call(name, M, N, K, a, b_, e):
+        (ca, da), (cb, db) = operand(a), operand(b_)
+        epi = {"store": tp.TP_EPI_STORE, "bias": tp.TP_EPI_STORE, "bias_gelu": tp.TP_EPI_BIAS_GELU,
+               "dgelu": tp.TP_EPI_DGELU}[e]
+        return lambda: tp.tp_gemm_fp8(M, N, K, ca, K, da, cb, K, db, epi, outs[name],
+                                      out2 if e == "bias_gelu" else None, N, bias.get(name),
+                                      U if e == "dgelu" else None, 0, gws, gws.numel())
+
+    gemms = [(g[0], gemm_call(*g)) for g in FP8_GEMMS]
+
+    def step():
+        quantize_all()
+        for _, fn in gemms:
+            fn()
+
+    def back_to_back(fn, n):
+        """Mean time of fn over n calls back to back between one pair of HIP events (per-call events
+        would let the host's launch rate, not the GPU, set the pace of the short kernels)."""
+        fn()
+        torch.cuda.synchronize()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b_) / n
 
     if args.copy_probe:
         copy_probe(torch, dev)
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
-    # the step time without per-call events (48 event records per step would make the host, not
-    # the GPU, set the pace of the short quantisation kernels), then a second pass with them for
-    # the per-GEMM and quantisation breakdown
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step(False)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    per = {k: float(np.mean([a.elapsed_time(b_) for a, b_ in v])) * (len(v) / args.steps) for k, v in ev.items()}
+    # the step, then each GEMM and the twelve quantisations on their own for the breakdown
+    ms = back_to_back(step, args.steps)
+    per = {"quantize": back_to_back(quantize_all, args.steps)}
+    for name, fn in gemms:
+        per[name] = back_to_back(fn, args.steps)
     gemm_fl = {n: 2.0 * M * N * K for n, M, N, K, a, b_, e in FP8_GEMMS}
     total_fl = sum(gemm_fl.values())
     value = total_fl / (ms * 1e-3) / 1e12
